@@ -1,0 +1,14 @@
+"""fp64 CPU oracle (test infrastructure only; see oracle/attention.py).
+
+Only the test suite, ``__graft_entry__.smoke()`` and bench.py's cpu_baseline leg
+may import this package.  The HIP product path never does.
+"""
+
+from .attention import (  # noqa: F401
+    attention_forward,
+    attention_probs,
+    decode,
+    kv_cache_write,
+    kv_head_of,
+    visibility,
+)

@@ -1,0 +1,194 @@
+"""fp64 CPU oracle for fused attention forward, KV-cache decode and the cache write.
+
+TEST INFRASTRUCTURE ONLY.  This module is the checker, not the product: only the
+test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call it.  It shares no code, constant or helper with
+the HIP library and never imports it; the library never imports this.
+
+Sources (three web pages on one subject; cited by title and section):
+
+* [P1] "Skill: Write a Triton Attention Kernel" (ahel.ai catalog).
+* [P2] "FlashAttention Kernel Optimization" (the flash-attention-kernel skill page).
+* [P3] "Triton-FlashAttention" (project README: GQA/MQA prefill + KV-cache decode).
+
+What is computed.  The tiled, online-softmax kernel of [P1] "Required reasoning
+process" reaches, up to rounding order, the plain definition: [P1] "Correctness
+requirements" (first bullet) requires O_i / l_i to equal the true softmax-weighted
+sum of V, and [P2] "Online Softmax" describes the running-max rescale as a way to
+avoid a second pass, not as a different function.  So this oracle is that plain
+definition, written out in float64 with numpy (BLAS matmul as the only library
+step), in the obvious two-pass form:
+
+    S[i, j]  = scale * sum_d Q[b, h, i, d] * K[b, kvh, j, d]
+    vis(i,j) = (j < N_kv) and (not causal or j <= i)          top-left causal
+    m_i      = max over visible j of S[i, j]
+    P[i, j]  = exp(S[i, j] - m_i) / sum over visible j' of exp(S[i, j'] - m_i)
+    O[b,h,i] = sum_j P[i, j] * V[b, kvh, j, :]
+    lse[b,h,i] = m_i + ln(sum over visible j of exp(S[i, j] - m_i))
+    kvh      = h // (H_q // H_kv)                              GQA / MQA
+
+Readings taken where the pages leave a step open (each also listed in the design doc):
+
+* Causal mask is top-left aligned, kv position <= q position ([P1] step 5c; [P2]
+  "Common Pitfalls": the comparison is >=, not >).
+* ``scale`` multiplies the fp32 dot product; the oracle widens the exact float32
+  scale to float64 ([P1] "Inputs" item 4 and "Kernel design rules").
+* lse uses the natural log of the sum of exp of *scaled* scores ([P1] step 8).
+* A row with no visible key (unreachable with N_kv >= 1 and top-left causal)
+  gets O = 0 and lse = -inf by convention.
+* Decode is one query per (batch, head) over the first ``cache_len`` cache
+  slots, every slot visible, no causal loop ([P3] decode phase).
+* GQA maps q head h to kv head h // group, i.e. repeat_interleave expansion of
+  K/V, not tiling ([P1] step 1; [P3] GQA phase).
+
+Pins: tests/test_oracle_pins.py checks this module against closed forms,
+hand-derived fixtures (tests/golden/), invariants and an mpmath brute force.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "visibility",
+    "attention_probs",
+    "attention_forward",
+    "decode",
+    "kv_cache_write",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening to float64 (fp16, bf16-as-fp32 and fp32 all embed exactly)."""
+    a = np.asarray(x)
+    return a if a.dtype == np.float64 else a.astype(np.float64)
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """KV head read by q head ``h``: h // (Hq // Hkv).
+
+    [P1] "Required reasoning process" step 1 and "Kernel design rules" (GQA);
+    [P3] GQA/MQA design bullet: MHA is Hkv == Hq, MQA is Hkv == 1, one mapping.
+    """
+    return h // (Hq // Hkv)
+
+
+def visibility(q_pos: np.ndarray, Nkv: int, causal: bool) -> np.ndarray:
+    """Boolean (len(q_pos), Nkv): may query at position i attend to key j?
+
+    Keys exist only for j < Nkv ([P1] "Correctness requirements", KV boundary
+    bullet); with ``causal`` a key is visible when j <= i ([P1] step 5c).
+    """
+    j = np.arange(Nkv)
+    vis = np.ones((q_pos.shape[0], Nkv), dtype=bool)
+    if causal:
+        vis &= j[None, :] <= q_pos[:, None]
+    return vis
+
+
+def _scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * Q K^T in float64 ([P1] step 5b)."""
+    return np.float64(scale) * (q_rows @ k.T)
+
+
+def _masked_softmax(S: np.ndarray, vis: np.ndarray):
+    """Row-wise softmax over visible entries; returns (P, lse).
+
+    Two-pass, max-subtracted.  The mask is applied to S before the row max
+    ([P1] "Correctness requirements", causal bullet).
+    """
+    Sm = np.where(vis, S, -np.inf)
+    m = Sm.max(axis=1) if Sm.shape[1] else np.full(Sm.shape[0], -np.inf)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    E = np.where(vis, np.exp(Sm - m_safe[:, None]), 0.0)
+    l = E.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        P = np.where(empty[:, None], 0.0, E / np.where(empty, 1.0, l)[:, None])
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    return P, lse
+
+
+def attention_probs(q, k, scale: float, causal: bool) -> np.ndarray:
+    """Full softmax matrix P (B, Hq, Nq, Nkv) for small shapes (pin P1 uses it)."""
+    q = _f64(q)
+    k = _f64(k)
+    B, Hq, Nq, _ = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, Nq, Nkv))
+    vis = visibility(np.arange(Nq), Nkv, causal)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = kv_head_of(h, Hq, Hkv)
+            out[b, h], _ = _masked_softmax(_scores(q[b, h], k[b, kvh], scale), vis)
+    return out
+
+
+def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int = 512):
+    """O1: prefill attention by the plain definition.
+
+    q: (B, Hq, Nq, D); k, v: (B, Hkv, Nkv, D), any float dtype (widened exactly).
+    rows: optional 1-D array of query positions to evaluate (sampling at large
+    sizes); default all Nq positions.  Evaluated in row chunks so that the score
+    block stays small; chunking does not change any value.
+
+    Returns (O, lse): O (B, Hq, R, D) float64 and lse (B, Hq, R) float64 where R
+    is the number of evaluated rows ([P1] steps 6 and 8).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nkv, Dk = k.shape
+    if Bk != B or Dk != D or v.shape != k.shape or Hq % Hkv != 0:
+        raise ValueError("shape mismatch")
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    O = np.zeros((B, Hq, R, D))
+    lse = np.zeros((B, Hq, R))
+    for b in range(B):
+        for h in range(Hq):
+            kvh = kv_head_of(h, Hq, Hkv)
+            kb, vb = k[b, kvh], v[b, kvh]
+            for r0 in range(0, R, chunk):
+                sel = rows[r0:r0 + chunk]
+                S = _scores(q[b, h, sel], kb, scale)
+                P, ls = _masked_softmax(S, visibility(sel, Nkv, causal))
+                O[b, h, r0:r0 + chunk] = P @ vb
+                lse[b, h, r0:r0 + chunk] = ls
+    return O, lse
+
+
+def decode(q, k_cache, v_cache, cache_len: int, scale: float):
+    """O2: one query token per (batch, q head) over cache slots [0, cache_len).
+
+    [P3] decode phase: every cached position is valid, so there is no causal
+    mask; GQA indexing is the same as prefill.  q: (B, Hq, D); caches
+    (B, Hkv, S_max, D).  Returns O (B, Hq, D) and lse (B, Hq), float64.
+    """
+    q = _f64(q)
+    if not (1 <= cache_len <= np.asarray(k_cache).shape[2]):
+        raise ValueError("cache_len out of range")
+    kc = _f64(np.asarray(k_cache)[:, :, :cache_len])
+    vc = _f64(np.asarray(v_cache)[:, :, :cache_len])
+    O, lse = attention_forward(q[:, :, None, :], kc, vc, scale, causal=False)
+    return O[:, :, 0, :], lse[:, :, 0]
+
+
+def kv_cache_write(k_cache, v_cache, k_new, v_new, pos: int):
+    """O3: copies of the caches with slots [pos, pos + T) replaced by the new rows.
+
+    [P3] decode phase: a preallocated cache written by a separate helper.
+    Works on any dtype (including raw uint16 views of fp16/bf16); every other
+    element is left bit-for-bit unchanged.  Caches (B, Hkv, S_max, D); new rows
+    (B, Hkv, T, D).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    T = np.asarray(k_new).shape[2]
+    if pos < 0 or pos + T > kc.shape[2]:
+        raise ValueError("write outside the cache")
+    kc[:, :, pos:pos + T] = k_new
+    vc[:, :, pos:pos + T] = v_new
+    return kc, vc

@@ -1,0 +1,307 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle (looked up at call
+time through ``oracle.attention``, so a test can plant a mistake in it) breaks a
+fact fixed by the mathematics or by the pages' conventions:
+
+* hand-derived closed forms (tests/golden/closed_forms.json);
+* closed forms for structured inputs (equal scores -> mean of V, one key -> V[0],
+  causal row 0 -> V[0]);
+* invariants (rows of P sum to 1, shift and permutation invariance, linearity in
+  V, GQA == repeat_interleave-expanded MHA, causal prefill row i == decode over
+  i + 1 cached keys);
+* an mpmath brute force written independently (explicit loops, no max
+  subtraction, exact-rounded dot products, 40 significant digits).
+
+The module has no test_ prefix: tests/test_oracle_pins.py runs every pin against
+the real oracle and tests/test_oracle_mutations.py runs them against oracles
+with planted bugs to show each bug is caught.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+
+import oracle.attention as OA
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+# ---------------------------------------------------------------- helpers
+
+def _decode_value(x):
+    if isinstance(x, dict):
+        (key, arg), = x.items()
+        if key == "ln":
+            return math.log(arg)
+        if key == "one_minus_ln_over_1000":
+            return 1.0 - math.log(arg) / 1000.0
+        if key == "plus_1000_ln":
+            return 1000.0 + math.log(arg)
+        raise KeyError(key)
+    if isinstance(x, list):
+        return [_decode_value(e) for e in x]
+    return float(x)
+
+
+def _arr(x):
+    return np.array(_decode_value(x), dtype=np.float64)
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _fp16_exact(rng, *shape, std=1.0):
+    """Random values that are exactly representable in fp16 (as the kernels see them)."""
+    return (rng.standard_normal(shape) * std).astype(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------- pins
+
+def pin_golden_prefill():
+    for case in _golden()["prefill"]:
+        q, k, v = _arr(case["q"]), _arr(case["k"]), _arr(case["v"])
+        O, lse = OA.attention_forward(q, k, v, case["scale"], case["causal"])
+        np.testing.assert_allclose(O, _arr(case["o"]), rtol=0, atol=case["tol"], err_msg=case["name"])
+        np.testing.assert_allclose(lse, _arr(case["lse"]), rtol=0, atol=case["tol"], err_msg=case["name"])
+
+
+def pin_golden_decode():
+    for case in _golden()["decode"]:
+        O, lse = OA.decode(_arr(case["q"]), _arr(case["k_cache"]), _arr(case["v_cache"]),
+                           case["cache_len"], case["scale"])
+        np.testing.assert_allclose(O, _arr(case["o"]), rtol=0, atol=case["tol"], err_msg=case["name"])
+        np.testing.assert_allclose(lse, _arr(case["lse"]), rtol=0, atol=case["tol"], err_msg=case["name"])
+
+
+def pin_golden_cache_write():
+    for case in _golden()["cache_write"]:
+        kc, vc = OA.kv_cache_write(_arr(case["k_cache"]), _arr(case["v_cache"]),
+                                   _arr(case["k_new"]), _arr(case["v_new"]), case["pos"])
+        np.testing.assert_array_equal(kc, _arr(case["k_out"]), err_msg=case["name"])
+        np.testing.assert_array_equal(vc, _arr(case["v_out"]), err_msg=case["name"])
+
+
+def pin_rows_sum_to_one():
+    """P1: every row of P sums to 1 over visible keys and is 0 on masked keys."""
+    rng = np.random.default_rng(1)
+    for causal in (False, True):
+        q, k = _rand(rng, 2, 4, 13, 8), _rand(rng, 2, 2, 13, 8)
+        P = OA.attention_probs(q, k, 0.37, causal)
+        np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+        assert (P >= 0).all()
+        if causal:
+            i, j = np.indices((13, 13))
+            assert (P[..., j > i] == 0).all()
+            assert (P[..., j <= i] > 0).all()
+
+
+def pin_causal_row0_is_v0():
+    """P2: with top-left causal masking row 0 sees key 0 only: O = V[0] exactly."""
+    rng = np.random.default_rng(2)
+    q, k, v = _fp16_exact(rng, 2, 4, 9, 16), _fp16_exact(rng, 2, 2, 9, 16), _fp16_exact(rng, 2, 2, 9, 16)
+    scale = 0.25
+    O, lse = OA.attention_forward(q, k, v, scale, True)
+    for h in range(4):
+        kvh = h // 2
+        np.testing.assert_array_equal(O[:, h, 0], v[:, kvh, 0])
+        s00 = scale * np.einsum("bd,bd->b", q[:, h, 0], k[:, kvh, 0])
+        np.testing.assert_allclose(lse[:, h, 0], s00, rtol=0, atol=1e-12)
+
+
+def pin_equal_scores_give_mean():
+    """P3: all scores equal (Q = 0, or scale = 0) -> O is the mean of visible V, lse = ln(count)."""
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, N, D = 1, 4, 2, 11, 8
+    k, v = _rand(rng, B, Hkv, N, D), _rand(rng, B, Hkv, N, D)
+    for (q, scale) in ((np.zeros((B, Hq, N, D)), 0.5), (_rand(rng, B, Hq, N, D), 0.0)):
+        for causal in (False, True):
+            O, lse = OA.attention_forward(q, k, v, scale, causal)
+            for h in range(Hq):
+                kvh = h // (Hq // Hkv)
+                for i in range(N):
+                    n = i + 1 if causal else N
+                    np.testing.assert_allclose(O[0, h, i], v[0, kvh, :n].mean(0), rtol=0, atol=1e-13)
+                    np.testing.assert_allclose(lse[0, h, i], math.log(n), rtol=0, atol=1e-13)
+
+
+def pin_single_key():
+    """P4: N_kv = 1 -> every row returns V[0] and lse = its one score."""
+    rng = np.random.default_rng(4)
+    q, k, v = _rand(rng, 2, 4, 5, 8), _rand(rng, 2, 1, 1, 8), _rand(rng, 2, 1, 1, 8)
+    O, lse = OA.attention_forward(q, k, v, 0.3, False)
+    np.testing.assert_array_equal(O, np.broadcast_to(v[:, :, :1], O.shape))
+    np.testing.assert_allclose(lse, 0.3 * np.einsum("bhnd,bd->bhn", q, k[:, 0, 0]), rtol=0, atol=1e-12)
+    Od, lsed = OA.decode(q[:, :, 0], k, v, 1, 0.3)
+    np.testing.assert_array_equal(Od, np.broadcast_to(v[:, 0, 0][:, None], Od.shape))
+
+
+def pin_gqa_equals_expanded_mha():
+    """P5: GQA/MQA equals MHA on K/V expanded with repeat_interleave over heads."""
+    rng = np.random.default_rng(5)
+    for Hkv in (1, 2, 4):
+        q, k, v = _rand(rng, 2, 8, 7, 8), _rand(rng, 2, Hkv, 9, 8), _rand(rng, 2, Hkv, 9, 8)
+        g = 8 // Hkv
+        ke, ve = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+        for causal in (False, True):
+            O, lse = OA.attention_forward(q, k, v, 0.4, causal)
+            Oe, lsee = OA.attention_forward(q, ke, ve, 0.4, causal)
+            np.testing.assert_array_equal(O, Oe)
+            np.testing.assert_array_equal(lse, lsee)
+
+
+def _brute(q, k, v, scale, causal):
+    """Independent evaluation: explicit loops, exp without max subtraction at 40 digits."""
+    mpmath.mp.dps = 40
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    O = np.zeros((B, Hq, Nq, D))
+    lse = np.zeros((B, Hq, Nq))
+    sc = mpmath.mpf(float(scale))
+    for b in range(B):
+        for h in range(Hq):
+            kvh = (h * Hkv) // Hq
+            for i in range(Nq):
+                keys = [j for j in range(Nkv) if (not causal) or j <= i]
+                w = []
+                for j in keys:
+                    dot = mpmath.mpf(math.fsum(float(q[b, h, i, d]) * float(k[b, kvh, j, d]) for d in range(D)))
+                    w.append(mpmath.exp(sc * dot))
+                tot = mpmath.fsum(w)
+                for d in range(D):
+                    O[b, h, i, d] = float(mpmath.fsum(wj * mpmath.mpf(float(v[b, kvh, j, d])) for wj, j in zip(w, keys)) / tot)
+                lse[b, h, i] = float(mpmath.log(tot))
+    return O, lse
+
+
+def pin_brute_force_tiny():
+    """P6: agreement with the brute force on tiny shapes (odd N, g in {1,2,4})."""
+    rng = np.random.default_rng(6)
+    shapes = [(1, 1, 1, 1, 1, 1), (1, 2, 2, 5, 5, 3), (2, 4, 2, 7, 7, 4), (1, 4, 1, 9, 9, 8), (1, 4, 4, 3, 6, 2)]
+    for (B, Hq, Hkv, Nq, Nkv, D) in shapes:
+        q, k, v = _rand(rng, B, Hq, Nq, D), _rand(rng, B, Hkv, Nkv, D), _rand(rng, B, Hkv, Nkv, D)
+        for causal in (False, True):
+            if causal and Nq > Nkv:
+                continue
+            O, lse = OA.attention_forward(q, k, v, 0.7, causal)
+            Ob, lseb = _brute(q, k, v, 0.7, causal)
+            np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse, lseb, rtol=1e-12, atol=1e-12)
+
+
+def pin_shift_invariance():
+    """P7: adding one vector u to every key leaves O unchanged and shifts lse by scale*q.u."""
+    rng = np.random.default_rng(7)
+    q, k, v = _rand(rng, 1, 2, 6, 8), _rand(rng, 1, 1, 6, 8), _rand(rng, 1, 1, 6, 8)
+    u = _rand(rng, 8) * 3.0
+    for causal in (False, True):
+        O, lse = OA.attention_forward(q, k, v, 0.5, causal)
+        O2, lse2 = OA.attention_forward(q, k + u, v, 0.5, causal)
+        np.testing.assert_allclose(O2, O, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse2, lse + 0.5 * (q @ u), rtol=0, atol=1e-11)
+
+
+def pin_permutation_invariance():
+    """P8: without a causal mask, permuting key/value positions together changes nothing."""
+    rng = np.random.default_rng(8)
+    q, k, v = _rand(rng, 1, 2, 5, 8), _rand(rng, 1, 2, 10, 8), _rand(rng, 1, 2, 10, 8)
+    perm = rng.permutation(10)
+    O, lse = OA.attention_forward(q, k, v, 0.6, False)
+    O2, lse2 = OA.attention_forward(q, k[:, :, perm], v[:, :, perm], 0.6, False)
+    np.testing.assert_allclose(O2, O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
+
+
+def pin_linear_in_v():
+    """P9: O(a V1 + b V2) = a O(V1) + b O(V2)."""
+    rng = np.random.default_rng(9)
+    q, k = _rand(rng, 1, 2, 6, 8), _rand(rng, 1, 1, 6, 8)
+    v1, v2 = _rand(rng, 1, 1, 6, 8), _rand(rng, 1, 1, 6, 8)
+    for causal in (False, True):
+        O1, _ = OA.attention_forward(q, k, v1, 0.5, causal)
+        O2, _ = OA.attention_forward(q, k, v2, 0.5, causal)
+        O12, _ = OA.attention_forward(q, k, 2.0 * v1 - 3.0 * v2, 0.5, causal)
+        np.testing.assert_allclose(O12, 2.0 * O1 - 3.0 * O2, rtol=0, atol=1e-12)
+
+
+def pin_causal_row_equals_decode():
+    """P10: causal prefill row i equals decode of query i over i + 1 cached keys."""
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, N, D = 1, 4, 2, 12, 8
+    q, k, v = _rand(rng, B, Hq, N, D), _rand(rng, B, Hkv, N, D), _rand(rng, B, Hkv, N, D)
+    O, lse = OA.attention_forward(q, k, v, 0.45, True)
+    for i in range(N):
+        Od, lsed = OA.decode(q[:, :, i], k, v, i + 1, 0.45)
+        np.testing.assert_allclose(Od, O[:, :, i], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lsed, lse[:, :, i], rtol=0, atol=1e-13)
+
+
+def pin_row_sampling_matches_full():
+    """Evaluating a subset of rows gives the same values as the full evaluation."""
+    rng = np.random.default_rng(11)
+    q, k, v = _rand(rng, 1, 2, 40, 8), _rand(rng, 1, 1, 40, 8), _rand(rng, 1, 1, 40, 8)
+    rows = np.array([0, 3, 17, 39])
+    for causal in (False, True):
+        O, lse = OA.attention_forward(q, k, v, 0.5, causal, chunk=7)
+        Os, lses = OA.attention_forward(q, k, v, 0.5, causal, rows=rows)
+        np.testing.assert_array_equal(Os, O[:, :, rows])
+        np.testing.assert_array_equal(lses, lse[:, :, rows])
+
+
+def pin_cache_write_touches_only_its_slots():
+    rng = np.random.default_rng(12)
+    kc = rng.integers(0, 2**16, (2, 3, 10, 4), dtype=np.uint16)
+    vc = rng.integers(0, 2**16, (2, 3, 10, 4), dtype=np.uint16)
+    kn = rng.integers(0, 2**16, (2, 3, 3, 4), dtype=np.uint16)
+    vn = rng.integers(0, 2**16, (2, 3, 3, 4), dtype=np.uint16)
+    k2, v2 = OA.kv_cache_write(kc, vc, kn, vn, 6)
+    np.testing.assert_array_equal(k2[:, :, 6:9], kn)
+    np.testing.assert_array_equal(v2[:, :, 6:9], vn)
+    np.testing.assert_array_equal(np.delete(k2, [6, 7, 8], axis=2), np.delete(kc, [6, 7, 8], axis=2))
+    np.testing.assert_array_equal(np.delete(v2, [6, 7, 8], axis=2), np.delete(vc, [6, 7, 8], axis=2))
+
+
+ALL_PINS = [
+    pin_golden_prefill,
+    pin_golden_decode,
+    pin_golden_cache_write,
+    pin_rows_sum_to_one,
+    pin_causal_row0_is_v0,
+    pin_equal_scores_give_mean,
+    pin_single_key,
+    pin_gqa_equals_expanded_mha,
+    pin_brute_force_tiny,
+    pin_shift_invariance,
+    pin_permutation_invariance,
+    pin_linear_in_v,
+    pin_causal_row_equals_decode,
+    pin_row_sampling_matches_full,
+    pin_cache_write_touches_only_its_slots,
+]
+
+
+def pin_brute_force_tiny_config():
+    """P6 on the full tiny prefill workload (B=1, Hq=2, Hkv=1, N=65, D=64, fp16, causal)."""
+    from workloads import TINY, prefill_inputs
+    q, k, v = (t.float().numpy().astype(np.float64) for t in prefill_inputs(TINY))
+    rows = np.array([0, 1, 31, 32, 63, 64])
+    O, lse = OA.attention_forward(q, k, v, TINY.softmax_scale, True, rows=rows)
+    # brute force of selected rows: evaluate row-by-row with the causal prefix made explicit
+    for idx, i in enumerate(rows):
+        Oi, lsei = _brute(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1], TINY.softmax_scale, False)
+        np.testing.assert_allclose(O[:, :, idx], Oi[:, :, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, :, idx], lsei[:, :, 0], rtol=1e-12, atol=1e-12)
+
+
+ALL_PINS.append(pin_brute_force_tiny_config)

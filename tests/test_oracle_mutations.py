@@ -1,0 +1,118 @@
+"""Planted mistakes in the oracle must each trip at least one pin.
+
+Every mutation below is a plausible bug (a flipped comparison, a wrong head
+mapping, a dropped term, an off-by-one).  Each is planted in the oracle module
+on the CPU with monkeypatch; the test asserts that running the full pin set
+against the mutated oracle fails.  This shows the pins constrain every part of
+the oracle rather than only re-deriving it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.attention as OA
+from oracle_pins import ALL_PINS
+
+_orig_vis = OA.visibility
+_orig_soft = OA._masked_softmax
+_orig_scores = OA._scores
+_orig_decode = OA.decode
+_orig_write = OA.kv_cache_write
+
+
+def _vis_strict(q_pos, Nkv, causal):
+    j = np.arange(Nkv)
+    vis = np.ones((q_pos.shape[0], Nkv), dtype=bool)
+    if causal:
+        vis &= j[None, :] < q_pos[:, None]
+    return vis
+
+
+def _vis_no_causal(q_pos, Nkv, causal):
+    return _orig_vis(q_pos, Nkv, False)
+
+
+def _vis_off_by_one(q_pos, Nkv, causal):
+    return _orig_vis(q_pos + 1, Nkv, causal)
+
+
+def _kv_head_tiled(h, Hq, Hkv):
+    return h % Hkv
+
+
+def _scores_unscaled(q_rows, k, scale):
+    return _orig_scores(q_rows, k, 1.0)
+
+
+def _scores_scaled_twice(q_rows, k, scale):
+    return _orig_scores(q_rows, k, scale * scale)
+
+
+def _soft_lse_is_max(S, vis):
+    P, lse = _orig_soft(S, vis)
+    Sm = np.where(vis, S, -np.inf)
+    return P, Sm.max(axis=1)
+
+
+def _soft_unnormalised(S, vis):
+    Sm = np.where(vis, S, -np.inf)
+    m = Sm.max(axis=1)
+    E = np.where(vis, np.exp(Sm - m[:, None]), 0.0)
+    return E, m + np.log(E.sum(1))
+
+
+def _soft_base2(S, vis):
+    return _orig_soft(S * np.log2(np.e) * np.log(2.0) ** 2, vis)
+
+
+def _soft_mask_ignored_in_sum(S, vis):
+    Sm = np.where(vis, S, -np.inf)
+    m = Sm.max(axis=1)
+    E = np.exp(S - m[:, None])  # masked keys leak into the sum
+    l = E.sum(1)
+    return np.where(vis, E, 0.0) / l[:, None], m + np.log(l)
+
+
+def _decode_reads_one_more(q, k_cache, v_cache, cache_len, scale):
+    n = min(cache_len + 1, np.asarray(k_cache).shape[2])
+    return _orig_decode(q, k_cache, v_cache, n, scale)
+
+
+def _write_shifted(k_cache, v_cache, k_new, v_new, pos):
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    T = np.asarray(k_new).shape[2]
+    p = min(pos + 1, kc.shape[2] - T)
+    kc[:, :, p:p + T] = k_new
+    vc[:, :, p:p + T] = v_new
+    return kc, vc
+
+
+MUTATIONS = {
+    "causal_strict_lt": ("visibility", _vis_strict),
+    "causal_ignored": ("visibility", _vis_no_causal),
+    "causal_off_by_one": ("visibility", _vis_off_by_one),
+    "gqa_tiled_heads": ("kv_head_of", _kv_head_tiled),
+    "scale_dropped": ("_scores", _scores_unscaled),
+    "scale_twice": ("_scores", _scores_scaled_twice),
+    "lse_missing_log_l": ("_masked_softmax", _soft_lse_is_max),
+    "p_not_normalised": ("_masked_softmax", _soft_unnormalised),
+    "exp_wrong_base": ("_masked_softmax", _soft_base2),
+    "masked_keys_in_sum": ("_masked_softmax", _soft_mask_ignored_in_sum),
+    "decode_reads_past_cache_len": ("decode", _decode_reads_one_more),
+    "cache_write_off_by_one": ("kv_cache_write", _write_shifted),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(OA, attr, fn)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception:  # assertion or a crash both mean the mutation is visible
+            caught.append(pin.__name__)
+            break
+    assert caught, f"mutation {name} passed every pin"
