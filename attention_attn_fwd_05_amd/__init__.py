@@ -1,0 +1,41 @@
+"""Fused attention forward + KV-cache decode for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libattn.so`` (C ABI in include/attn.h).  Every
+step of the computation runs in the library's HIP kernels; this module only
+marshals torch tensors into pointers, element strides and the current HIP
+stream.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+
+Entry points (same names as the C ABI):
+
+* ``attn_fwd(q, k, v, *, causal, scale=None, return_lse=False, out=None)``
+* ``attn_decode(q, k_cache, v_cache, cache_len, *, scale=None, workspace=None,
+  num_splits=0, return_lse=False, out=None)``
+* ``attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)`` /
+  ``decode_workspace(...)`` (a zero-filled uint8 tensor of that size)
+* ``kv_cache_write(k_cache, v_cache, k_new, v_new, pos)``
+"""
+
+from ._binding import (  # noqa: F401
+    AttnError,
+    Status,
+    attn_decode,
+    attn_decode_workspace_bytes,
+    attn_fwd,
+    decode_workspace,
+    kv_cache_write,
+    lib_path,
+    load_library,
+)
+
+__all__ = [
+    "AttnError",
+    "Status",
+    "attn_fwd",
+    "attn_decode",
+    "attn_decode_workspace_bytes",
+    "decode_workspace",
+    "kv_cache_write",
+    "lib_path",
+    "load_library",
+]

@@ -1,0 +1,195 @@
+"""ctypes marshalling for libattn.so.  No computation happens here."""
+
+from __future__ import annotations
+
+import ctypes
+import enum
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    ERR_NULL = 1
+    ERR_SHAPE = 2
+    ERR_UNSUPPORTED = 3
+    ERR_WORKSPACE = 4
+    ERR_HIP = 5
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = Status(status)
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64), ("d", ctypes.c_int64)]
+
+
+_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, "libattn.so")
+
+
+def load_library():
+    """Load libattn.so once; raise if it is missing (there is no fallback path)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python __graft_entry__.py build)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, Strides
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32,
+                                vp, ctypes.c_size_t, vp]
+    lib.attn_decode.restype = i32
+    lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, i32, vp]
+    lib.kv_cache_write.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        lib = load_library()
+        raise AttnError(status, fn, lib.attn_status_string(status).decode())
+
+
+def _strides4(t: torch.Tensor) -> Strides:
+    s = t.stride()
+    return Strides(s[0], s[1], s[2], s[3])
+
+
+def _strides3(t: torch.Tensor) -> Strides:
+    s = t.stride()
+    return Strides(s[0], s[1], 0, s[2])
+
+
+def _dtype_code(*ts: torch.Tensor) -> int:
+    dt = ts[0].dtype
+    if dt not in _DTYPES or any(t.dtype != dt for t in ts):
+        raise TypeError("q/k/v (and out) must share one dtype, float16 or bfloat16")
+    return _DTYPES[dt]
+
+
+def _on_gpu(*ts: torch.Tensor):
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool, scale: float | None = None,
+             return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Fused attention forward.  q (B,Hq,Nq,D), k/v (B,Hkv,Nkv,D), any strides with stride(-1) == 1.
+
+    Returns ``out`` (B,Hq,Nq,D), or ``(out, lse)`` with lse fp32 (B,Hq,Nq) when ``return_lse``.
+    """
+    lib = load_library()
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, Nq)")
+    _on_gpu(q, k, v, out, *([lse] if lse is not None else []))
+    code = _dtype_code(q, k, v, out)
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v and out")
+    s = _default_scale(D) if scale is None else float(scale)
+    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None,
+                      B, Hq, Hkv, Nq, Nkv, D, _strides4(q), _strides4(k), _strides4(v), _strides4(out),
+                      s, 1 if causal else 0, code, _stream(q))
+    _check(st, "attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, S_max: int, D: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D))
+
+
+def decode_workspace(B: int, Hq: int, Hkv: int, S_max: int, D: int, device) -> torch.Tensor:
+    """A zero-filled workspace for attn_decode (reusable across calls on one stream)."""
+    n = attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)
+    if n == 0:
+        raise ValueError("invalid decode sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: int, *,
+                scale: float | None = None, workspace: torch.Tensor | None = None, num_splits: int = 0,
+                return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Decode one token per (batch, q head) over cache slots [0, cache_len).
+
+    q (B,Hq,D); caches (B,Hkv,S_max,D).  ``workspace`` must come from
+    ``decode_workspace`` (or be zero-filled before its first use); if omitted a
+    fresh one is allocated for this call.
+    """
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq)")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, S_max, D, q.device)
+    _on_gpu(q, k_cache, v_cache, out, workspace, *([lse] if lse is not None else []))
+    code = _dtype_code(q, k_cache, v_cache, out)
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, caches and out")
+    s = _default_scale(D) if scale is None else float(scale)
+    st = lib.attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                         lse.data_ptr() if lse is not None else None,
+                         B, Hq, Hkv, S_max, int(cache_len), D,
+                         _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out),
+                         s, code, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         _stream(q))
+    _check(st, "attn_decode")
+    return (out, lse) if return_lse else out
+
+
+def kv_cache_write(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   pos: int) -> None:
+    """Write k_new/v_new (B,Hkv,T,D) into cache slots [pos, pos+T) of (B,Hkv,S_max,D) caches."""
+    lib = load_library()
+    _on_gpu(k_cache, v_cache, k_new, v_new)
+    code = _dtype_code(k_cache, v_cache, k_new, v_new)
+    B, Hkv, S_max, D = k_cache.shape
+    T = k_new.shape[2]
+    if v_cache.shape != k_cache.shape or k_new.shape != v_new.shape or k_new.shape[:2] != (B, Hkv) \
+            or k_new.shape[3] != D:
+        raise ValueError("shape mismatch between caches and new rows")
+    st = lib.kv_cache_write(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                            B, Hkv, S_max, D, int(pos), T,
+                            _strides4(k_cache), _strides4(v_cache), _strides4(k_new), _strides4(v_new),
+                            code, _stream(k_cache))
+    _check(st, "kv_cache_write")

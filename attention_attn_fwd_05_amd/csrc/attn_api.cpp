@@ -1,0 +1,205 @@
+// C ABI of libattn.so (declared in include/attn.h): argument validation,
+// kernel selection and launch geometry.  Everything here runs on the host;
+// every check happens before the first HIP call, so an invalid call enqueues
+// nothing and touches no memory.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kPrefillRows = 128;  // query rows per prefill workgroup
+constexpr int kDecodeTile = 128;   // cache rows per decode tile
+constexpr int kDecodeMaxHeads = 16;
+constexpr int kTargetWorkgroups = 256;  // one decode workgroup per CU fills MI355X
+constexpr size_t kTicketAlign = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// head-dim stride 1; other strides non-negative multiples of 8 elements (16 bytes)
+inline bool strides_ok(const attn_strides& s) {
+  return s.d == 1 && s.b >= 0 && s.h >= 0 && s.n >= 0 && s.b % 8 == 0 && s.h % 8 == 0 && s.n % 8 == 0;
+}
+
+inline bool dtype_ok(attn_dtype t) { return t == ATTN_F16 || t == ATTN_BF16; }
+
+inline uint32_t q_sign_mask(float scale) { return std::signbit(scale) ? 0x80008000u : 0u; }
+
+struct DecodeGeometry {
+  int hgroups, heads_per_wg, max_splits;
+  size_t ticket_bytes, part_bytes;
+};
+
+DecodeGeometry decode_geometry(int B, int Hq, int Hkv, int S_max, int D) {
+  DecodeGeometry g{};
+  const int group = Hq / Hkv;
+  g.hgroups = (group + kDecodeMaxHeads - 1) / kDecodeMaxHeads;
+  g.heads_per_wg = (group + g.hgroups - 1) / g.hgroups;
+  g.max_splits = (S_max + kDecodeTile - 1) / kDecodeTile;
+  const size_t slots = (size_t)B * Hkv * g.hgroups;
+  g.ticket_bytes = ((slots * sizeof(uint32_t) + kTicketAlign - 1) / kTicketAlign) * kTicketAlign;
+  g.part_bytes = slots * (size_t)g.max_splits * g.heads_per_wg * (size_t)(D + 2) * sizeof(float);
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (size <= 0, Hq % Hkv != 0, or position/length out of range)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (head dim, dtype, stride, alignment or scale)";
+    case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                     float scale, int causal, attn_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
+  const int64_t nqb = ((int64_t)Nq + kPrefillRows - 1) / kPrefillRows;
+  const int64_t nblocks = nqb * Hq * B;
+  if (nblocks > INT_MAX) return ATTN_ERR_SHAPE;
+
+  attn::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.sqb = sq.b; a.sqh = sq.h; a.sqn = sq.n;
+  a.skb = sk.b; a.skh = sk.h; a.skn = sk.n;
+  a.svb = sv.b; a.svh = sv.h; a.svn = sv.n;
+  a.sob = so.b; a.soh = so.h; a.son = so.n;
+  a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.group = Hq / Hkv;
+  a.nqb = (int)nqb;
+  a.nblocks = (int)nblocks;
+  // XCD-aware remap: blocks are dispatched round-robin over 8 XCDs; remapping
+  // gives each XCD a contiguous run of (kv head, query block) work.  Only used
+  // when every XCD then gets whole kv-head units, or (non-causal, equal-length
+  // blocks) an equal slice of one unit.
+  const int64_t per_xcd = nblocks / 8;
+  const int64_t per_unit = (int64_t)a.group * nqb;
+  a.remap = (nblocks % 8 == 0) && per_xcd > 0 &&
+            ((per_xcd % per_unit == 0) || (!causal && per_unit % per_xcd == 0));
+  a.c = std::fabs(scale) * kLog2e;
+  a.qsign = q_sign_mask(scale);
+
+  const hipError_t e = attn::launch_prefill(a, D, dtype == ATTN_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
+  const DecodeGeometry g = decode_geometry(B, Hq, Hkv, S_max, D);
+  return g.ticket_bytes + g.part_bytes;
+}
+
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+                        attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
+                        float scale, attn_dtype dtype, int num_splits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || cache_len < 1 || cache_len > S_max || num_splits < 0) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  // q and o are (B, H, D): their n stride is unused and not checked
+  attn_strides sq3 = sq, so3 = so;
+  sq3.n = 0;
+  so3.n = 0;
+  if (!strides_ok(sq3) || !strides_ok(skc) || !strides_ok(svc) || !strides_ok(so3)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
+  const DecodeGeometry g = decode_geometry(B, Hq, Hkv, S_max, D);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < g.ticket_bytes + g.part_bytes)
+    return ATTN_ERR_WORKSPACE;
+  if ((int64_t)B * Hkv > 65535 || g.hgroups > 65535) return ATTN_ERR_SHAPE;  // grid y/z limits
+
+  const int units = B * Hkv;
+  const int tiles = (cache_len + kDecodeTile - 1) / kDecodeTile;
+  int want;
+  if (num_splits > 0) {
+    want = num_splits;
+  } else {
+    const int wgs_per_split = units * g.hgroups;
+    want = (kTargetWorkgroups + wgs_per_split - 1) / wgs_per_split;
+  }
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  const int tiles_per_split = (tiles + want - 1) / want;
+  const int nsplit = (tiles + tiles_per_split - 1) / tiles_per_split;
+
+  attn::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.sqb = sq.b; a.sqh = sq.h;
+  a.skb = skc.b; a.skh = skc.h; a.skn = skc.n;
+  a.svb = svc.b; a.svh = svc.h; a.svn = svc.n;
+  a.sob = so.b; a.soh = so.h;
+  a.Hq = Hq; a.Hkv = Hkv; a.group = Hq / Hkv; a.cache_len = cache_len;
+  a.heads_per_wg = g.heads_per_wg;
+  a.hgroups = g.hgroups;
+  a.nsplit = nsplit;
+  a.rows_per_split = tiles_per_split * kDecodeTile;
+  a.c = std::fabs(scale) * kLog2e;
+  a.qsign = q_sign_mask(scale);
+  a.tickets = static_cast<uint32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ticket_bytes);
+
+  const hipError_t e = attn::launch_decode(a, B, D, dtype == ATTN_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status kv_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           int B, int Hkv, int S_max, int D, int pos, int T,
+                           attn_strides skc, attn_strides svc, attn_strides skn, attn_strides svn,
+                           attn_dtype dtype, void* stream) {
+  if (!k_cache || !v_cache || !k_new || !v_new) return ATTN_ERR_NULL;
+  if (B <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || T <= 0) return ATTN_ERR_SHAPE;
+  if (pos < 0 || (int64_t)pos + T > S_max) return ATTN_ERR_SHAPE;
+  if (D % 8 != 0 || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  if (!strides_ok(skc) || !strides_ok(svc) || !strides_ok(skn) || !strides_ok(svn)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return ATTN_ERR_UNSUPPORTED;
+
+  attn::CacheWriteArgs a{};
+  a.kc = static_cast<uint16_t*>(k_cache);
+  a.vc = static_cast<uint16_t*>(v_cache);
+  a.kn = static_cast<const uint16_t*>(k_new);
+  a.vn = static_cast<const uint16_t*>(v_new);
+  a.skcb = skc.b; a.skch = skc.h; a.skcn = skc.n;
+  a.svcb = svc.b; a.svch = svc.h; a.svcn = svc.n;
+  a.sknb = skn.b; a.sknh = skn.h; a.sknn = skn.n;
+  a.svnb = svn.b; a.svnh = svn.h; a.svnn = svn.n;
+  a.Hkv = Hkv; a.pos = pos; a.T = T; a.D = D;
+  a.rows = (int64_t)B * Hkv * T;
+  const hipError_t e = attn::launch_cache_write(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

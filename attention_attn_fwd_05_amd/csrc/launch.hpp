@@ -1,0 +1,69 @@
+// Host-visible argument blocks and launchers of the attention kernels.  The C
+// ABI layer (attn_api.cpp) validates arguments and fills these; each launcher
+// enqueues its kernels on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;  // nullable, contiguous (B, Hq, Nq)
+  int64_t sqb, sqh, sqn;
+  int64_t skb, skh, skn;
+  int64_t svb, svh, svn;
+  int64_t sob, soh, son;
+  int Hq, Hkv, Nq, Nkv, group;
+  int nqb;      // number of 128-row query blocks
+  int nblocks;  // grid size
+  int remap;    // 1: XCD-aware block remap is valid for this grid
+  float c;      // |scale| * log2(e)
+  uint32_t qsign;  // 0x80008000 when scale < 0: flip Q's sign bits (exact)
+};
+
+hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, hipStream_t stream);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;  // nullable, contiguous (B, Hq)
+  int64_t sqb, sqh;
+  int64_t skb, skh, skn;
+  int64_t svb, svh, svn;
+  int64_t sob, soh;
+  int Hq, Hkv, group, cache_len;
+  int heads_per_wg;  // q heads handled by one workgroup (<= 16)
+  int hgroups;       // head groups per kv head
+  int nsplit;        // chunks along the cache
+  int rows_per_split;  // multiple of the 128-row tile
+  float c;
+  uint32_t qsign;
+  float* part;        // workspace: partial (m, l, o[D]) per (unit, head group, split, head)
+  uint32_t* tickets;  // workspace: one arrival counter per (unit, head group)
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool bf16, hipStream_t stream);
+
+struct CacheWriteArgs {
+  uint16_t* kc;
+  uint16_t* vc;
+  const uint16_t* kn;
+  const uint16_t* vn;
+  int64_t skcb, skch, skcn;
+  int64_t svcb, svch, svcn;
+  int64_t sknb, sknh, sknn;
+  int64_t svnb, svnh, svnn;
+  int Hkv, pos, T, D;
+  int64_t rows;  // B * Hkv * T
+};
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+
+}  // namespace attn

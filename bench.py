@@ -1,0 +1,238 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  1. attn_fwd: causal prefill, B=2, Hq=32, Hkv=8, N=8192, D=128, fp16;
+  2. kv_cache_write of one token into an 8192-slot cache;
+  3. attn_decode over cache_len=8192 (B=2, Hq=32, Hkv=8, D=128, fp16).
+W untimed warm-up steps, then K timed steps between two device synchronisations.
+Each launch is also bracketed by HIP events on the stream it runs on (the
+current torch stream, which the binding launches on); kernel throughput is
+algorithmic work per launch / mean event duration.
+
+`value` is the prefill throughput in TFLOP/s with algorithmic FLOPs counted as
+4 * D per visible (query, key) pair (causal: N(N+1)/2 pairs per head).  Decode
+is reported as GB/s of algorithmic bytes (K and V rows read once + q in + o
+out); its caches rotate over enough copies (>= 512 MiB) that the 256 MiB
+Infinity Cache cannot hold them between uses.
+
+Flags: --only prefill|decode|copy runs just that launch (for rocprofv3 runs),
+--no-cpu skips the oracle baseline.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--causal", type=int, default=1)
+    return p.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle, as it stands, on whole (batch, head) slices of the same workload until
+    the time budget is used; reported as algorithmic TFLOP/s (same unit as `value`)."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    q, k, v = W.prefill_inputs(case)
+    g = case.Hq // case.Hkv
+    pairs = case.visible_pairs_per_head()
+    done = 0
+    t0 = time.perf_counter()
+    order = [(b, h) for b in range(case.B) for h in range(case.Hq)]
+    for (b, h) in order:
+        kvh = h // g
+        qs = q[b:b + 1, h:h + 1].float().numpy().astype(np.float64)
+        ks = k[b:b + 1, kvh:kvh + 1].float().numpy().astype(np.float64)
+        vs = v[b:b + 1, kvh:kvh + 1].float().numpy().astype(np.float64)
+        oracle.attention_forward(qs, ks, vs, case.softmax_scale, case.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4 * case.D * pairs * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {case.B * case.Hq} (batch, head) slices of {case.name}, all {case.Nq} query rows "
+                      f"each, fp64 numpy (full masked score matrix), {dt:.1f} s",
+            "cpu_model": cpu_model(), "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(head-parallel sharding across GPUs is described in DESIGN.md but not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_attn_fwd_05_amd as A
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    A.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    pcase = W.serving(8192, bool(args.causal))
+    dcase = W.decode_case(8192)
+
+    # ---- resident inputs
+    q, k, v = (t.to(dev) for t in W.prefill_inputs(pcase))
+    o = torch.empty_like(q)
+    lse = torch.empty(pcase.B, pcase.Hq, pcase.Nq, dtype=torch.float32, device=dev)
+    qd, kc0, vc0 = W.decode_inputs(dcase)
+    cache_bytes = 2 * kc0.numel() * kc0.element_size()
+    rot = max(2, math.ceil(512 * 2 ** 20 / cache_bytes) + 1)
+    kcs = [kc0.to(dev) for _ in range(rot)]
+    vcs = [vc0.to(dev) for _ in range(rot)]
+    qd = qd.to(dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty(dcase.B, dcase.Hq, dtype=torch.float32, device=dev)
+    ws = A.decode_workspace(dcase.B, dcase.Hq, dcase.Hkv, dcase.S_max, dcase.D, dev)
+    knew = kc0[:, :, :1].clone().to(dev)
+    vnew = vc0[:, :, :1].clone().to(dev)
+
+    copy_src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+
+    do_p = args.only in ("all", "prefill")
+    do_d = args.only in ("all", "decode")
+    do_c = args.only == "copy"
+
+    def step(i, ev=None):
+        if do_p:
+            if ev: ev[0].record(stream)
+            A.attn_fwd(q, k, v, causal=pcase.causal, scale=pcase.softmax_scale, out=o, lse=lse, return_lse=True)
+            if ev: ev[1].record(stream)
+        if do_d:
+            j = i % rot
+            if ev: ev[2].record(stream)
+            A.kv_cache_write(kcs[j], vcs[j], knew, vnew, dcase.cache_len - 1)
+            if ev: ev[3].record(stream)
+            A.attn_decode(qd, kcs[j], vcs[j], dcase.cache_len, scale=dcase.softmax_scale, workspace=ws,
+                          out=od, lse=lsed, return_lse=True)
+            if ev: ev[4].record(stream)
+        if do_c:
+            if ev: ev[0].record(stream)
+            copy_dst.copy_(copy_src)
+            if ev: ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    res = {}
+    if do_p:
+        pt = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]  # ms
+        p_mean = statistics.fmean(pt)
+        flops = pcase.flops()
+        res["prefill"] = {"ms_mean": p_mean, "ms_median": statistics.median(pt), "ms_std": statistics.pstdev(pt),
+                          "tflops": flops / (p_mean * 1e-3) / 1e12, "flops_per_launch": flops,
+                          "flops_per_launch_no_causal_factor": 4 * pcase.B * pcase.Hq * pcase.Nq * pcase.Nkv * pcase.D}
+    if do_d:
+        dt_ = [evs[i][3].elapsed_time(evs[i][4]) for i in range(args.steps)]
+        wt = [evs[i][2].elapsed_time(evs[i][3]) for i in range(args.steps)]
+        d_mean = statistics.fmean(dt_)
+        nbytes = dcase.kv_bytes()
+        res["decode"] = {"ms_mean": d_mean, "ms_median": statistics.median(dt_), "ms_std": statistics.pstdev(dt_),
+                         "gbs": nbytes / (d_mean * 1e-3) / 1e9, "bytes_per_launch": nbytes,
+                         "cache_copies_rotated": rot, "kv_cache_write_ms_mean": statistics.fmean(wt)}
+    if do_c:
+        ct = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+        nb = copy_src.numel()
+        res["copy"] = {"bytes_read": nb, "bytes_written": nb, "ms_mean": statistics.fmean(ct),
+                       "gbs": 2 * nb / (statistics.fmean(ct) * 1e-3) / 1e9}
+
+    out = {
+        "metric": "causal prefill fwd TFLOPS (fp16) + decode KV-read GB/s, % of MI355X peak",
+        "value": round(res["prefill"]["tflops"], 2) if do_p else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded N(0,1) Q/K/V at the pages' shapes)",
+        "config": {"workload": f"{pcase.name} prefill + kv_cache_write(T=1) + {dcase.name} decode",
+                   "prefill": {"B": pcase.B, "Hq": pcase.Hq, "Hkv": pcase.Hkv, "Nq": pcase.Nq, "Nkv": pcase.Nkv,
+                               "D": pcase.D, "causal": pcase.causal},
+                   "decode": {"B": dcase.B, "Hq": dcase.Hq, "Hkv": dcase.Hkv, "S_max": dcase.S_max,
+                              "cache_len": dcase.cache_len, "D": dcase.D}},
+    }
+    if do_p:
+        t = res["prefill"]["tflops"]
+        out["roofline"] = {"bound": "mfma", "achieved": round(t, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(t / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                           "kernel": "prefill_fwd_kernel<128, f16, causal>"}
+    if do_d:
+        g = res["decode"]["gbs"]
+        out["decode"] = {"achieved": round(g, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "bound": "hbm",
+                         "frac": round(g / HBM_PEAK_GBS, 4), "us_mean": round(res["decode"]["ms_mean"] * 1e3, 2),
+                         "kernel": "decode_kernel<128, f16>", "traffic": None}
+    out["detail"] = res
+    if do_p and args.only == "all" and not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(pcase, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

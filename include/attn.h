@@ -1,0 +1,137 @@
+/*
+ * attn.h -- C ABI of libattn.so: fused attention forward (prefill), KV-cache
+ * decode and the KV-cache writer, hand-written HIP kernels for MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "Skill: Write a Triton Attention Kernel"
+ *   [P2] "FlashAttention Kernel Optimization" (flash-attention-kernel skill)
+ *   [P3] "Triton-FlashAttention" (project README)
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory and keeps no mutable global state.
+ *   - Strides are in ELEMENTS (not bytes), 64-bit, one per logical dimension,
+ *     so any (B,H,N,D) or (B,N,H,D) view is accepted ([P1] "Inputs" item 7 and
+ *     "Kernel design rules": all strides are arguments, no contiguity assumed).
+ *     The innermost (head-dim) stride must be 1, every other stride a multiple
+ *     of 8 elements, and every base pointer 16-byte aligned: the kernels move
+ *     rows in 16-byte vectors.  Violations return ATTN_ERR_UNSUPPORTED.
+ *   - Element types: IEEE fp16 or bf16 for Q/K/V/O; scores, softmax state and
+ *     accumulators are fp32 inside the kernels ([P1] "Kernel design rules").
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every
+ *     call is asynchronous on that stream; the caller synchronises.
+ *   - Every argument is validated on the host before anything is enqueued.  On
+ *     any error nothing is launched and no memory is touched ([P3] GQA phase:
+ *     unsupported cases must refuse rather than run silently).  Errors are
+ *     returned, never thrown.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  ATTN_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, cache_len or pos range  */
+  ATTN_ERR_UNSUPPORTED = 3, /* D not in {64,128}, unknown dtype, stride/alignment  */
+  ATTN_ERR_WORKSPACE = 4,   /* decode workspace missing or smaller than required   */
+  ATTN_ERR_HIP = 5          /* the HIP runtime reported an error at launch         */
+} attn_status;
+
+/* Element strides of a 4-D tensor viewed as (batch, head, position, head_dim). */
+typedef struct {
+  int64_t b, h, n, d;
+} attn_strides;
+
+/*
+ * attn_fwd -- O = softmax(scale * Q K^T + mask) V, one fused kernel.
+ *
+ * Defines: [P1] "Required reasoning process" steps 1-9 (tiling over KV blocks,
+ * online softmax with running max m and running sum l, alpha rescale, P.V
+ * accumulation, final 1/l, logsumexp, causal loop end); [P2] "Online Softmax",
+ * "Tiled Computation", "Causal Masking"; [P3] GQA design (kv_head = q_head /
+ * group).
+ *
+ *   q    (B, Hq,  Nq,  D) via sq      k, v (B, Hkv, Nkv, D) via sk, sv
+ *   o    (B, Hq,  Nq,  D) via so      written, same dtype as q
+ *   lse  nullable; if given, contiguous fp32 (B, Hq, Nq):
+ *        lse[b,h,i] = ln sum_{visible j} exp(scale * q_i . k_j)   ([P1] step 8)
+ *   Hq % Hkv == 0; q head h reads kv head h / (Hq / Hkv).
+ *   causal != 0: key j is visible to query i iff j <= i (top-left aligned,
+ *        [P1] step 5c); blocks wholly above the diagonal are never visited.
+ *   scale: multiplies the fp32 scores (any finite value, 0 and negative
+ *        included; the caller typically passes 1/sqrt(D)).
+ *   D in {64, 128}.  Nq, Nkv >= 1, any value (ragged tails are masked).
+ *   Rows of o beyond Nq and elements outside the described views are never
+ *   written; K/V rows at positions >= Nkv are never read.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                     float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode needs
+ * for a cache of S_max slots (covers every cache_len <= S_max and every split
+ * count the library may choose).  Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D);
+
+/*
+ * attn_decode -- one query token per (batch, q head) attending to cache slots
+ * [0, cache_len) of a preallocated KV cache ([P3] decode phase: separate decode
+ * kernel, cache_len is a runtime value, GQA indexing as in prefill, every
+ * cached position visible).  The cache is split along its length into chunks
+ * processed in parallel; each chunk's (max, sum, unnormalised output) partial
+ * is merged with the same rescale identity the online softmax uses ([P1] step
+ * 5f, [P2] "Online Softmax").
+ *
+ *   q        (B, Hq, D): element (b,h,d) at q[b*sq.b + h*sq.h + d]  (sq.n unused)
+ *   k_cache, v_cache (B, Hkv, S_max, D) via skc, svc
+ *   o        (B, Hq, D) via so (so.n unused);  lse nullable, contiguous fp32 (B, Hq)
+ *   1 <= cache_len <= S_max.  Slots >= cache_len are never read.
+ *   num_splits: 0 = library heuristic; k > 0 forces min(k, splits allowed by
+ *               S_max) chunks (used to test split invariance).
+ *   workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes,
+ *              16-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Every call
+ *              that completes leaves it valid for the next call (its counters
+ *              return to zero).  One workspace must not be shared by calls that
+ *              can run concurrently (different streams).
+ */
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+                        attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
+                        float scale, attn_dtype dtype, int num_splits,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kv_cache_write -- copy T new rows per (batch, kv head) into cache slots
+ * [pos, pos + T) of K and V ([P3] decode phase: the preallocated-cache write
+ * helper kept separate from the attention kernel).  A bit-exact copy; every
+ * other cache element is untouched.
+ *
+ *   k_cache, v_cache (B, Hkv, S_max, D) via skc, svc
+ *   k_new, v_new     (B, Hkv, T, D)     via skn, svn
+ *   0 <= pos, T >= 1, pos + T <= S_max; D a positive multiple of 8.
+ */
+attn_status kv_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           int B, int Hkv, int S_max, int D, int pos, int T,
+                           attn_strides skc, attn_strides svc, attn_strides skn, attn_strides svn,
+                           attn_dtype dtype, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,140 @@
+"""Host-only checks of the C ABI: symbols, workspace sizing, and that every
+invalid argument is rejected with its status code before anything is launched.
+
+These calls pass fake (never dereferenced) device addresses, so they are only
+run in a process without a GPU; each one is invalid in exactly one argument and
+must return before the first HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from attention_attn_fwd_05_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="fake-pointer validation tests run on a host without a GPU")
+
+S = bd.Strides
+OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bd.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "kv_cache_write",
+                          "attn_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.attn_status_string(code)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def c4(D, N, H):  # contiguous (B,H,N,D) strides
+    return S(H * N * D, N * D, D, 1)
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=1, Nq=65, Nkv=65, D=64,
+             sq=c4(64, 65, 2), sk=c4(64, 65, 1), sv=c4(64, 65, 1), so=c4(64, 65, 2),
+             scale=0.125, causal=1, dtype=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"],
+                        a["D"], a["sq"], a["sk"], a["sv"], a["so"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(B=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=-1), SHAPE), (dict(Nq=0), SHAPE), (dict(Nkv=0), SHAPE),
+    (dict(Hq=3, Hkv=2), SHAPE),
+    (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP),
+    (dict(dtype=2), UNSUP), (dict(scale=float("nan")), UNSUP), (dict(scale=float("inf")), UNSUP),
+    (dict(sq=S(8320, 4160, 64, 2)), UNSUP), (dict(sk=S(4160, 4160, 60, 1)), UNSUP),
+    (dict(so=S(-8, 4160, 64, 1)), UNSUP),
+    (dict(q=FAKE + 2), UNSUP), (dict(o=FAKE + 8), UNSUP), (dict(lse=FAKE + 2), UNSUP),
+    (dict(B=1 << 20, Nq=1 << 30, Hq=64, Hkv=1), SHAPE),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def dec(lib, **kw):
+    B, Hq, Hkv, Smax, D = 2, 32, 8, 8192, 128
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, B=B, Hq=Hq, Hkv=Hkv, S_max=Smax, cache_len=100, D=D,
+             sq=S(Hq * D, D, 0, 1), skc=c4(D, Smax, Hkv), svc=c4(D, Smax, Hkv), so=S(Hq * D, D, 0, 1),
+             scale=0.088, dtype=0, num_splits=0, ws=FAKE,
+             ws_bytes=lib.attn_decode_workspace_bytes(B, Hq, Hkv, Smax, D), stream=None)
+    a.update(kw)
+    return lib.attn_decode(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["S_max"],
+                           a["cache_len"], a["D"], a["sq"], a["skc"], a["svc"], a["so"], a["scale"], a["dtype"],
+                           a["num_splits"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(o=None), NULL),
+    (dict(cache_len=0), SHAPE), (dict(cache_len=8193), SHAPE), (dict(S_max=0), SHAPE),
+    (dict(Hq=30), SHAPE), (dict(num_splits=-1), SHAPE),
+    (dict(D=80), UNSUP), (dict(dtype=-1), UNSUP), (dict(scale=float("nan")), UNSUP),
+    (dict(skc=S(8192 * 128 * 8, 8192 * 128, 128, 2)), UNSUP), (dict(vc=FAKE + 4), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=1024), WS), (dict(ws=FAKE + 8), WS),
+])
+def test_decode_rejects(lib, kw, code):
+    assert dec(lib, **kw) == code
+
+
+def cw(lib, **kw):
+    B, Hkv, Smax, D, T = 2, 8, 64, 128, 3
+    a = dict(kc=FAKE, vc=FAKE, kn=FAKE, vn=FAKE, B=B, Hkv=Hkv, S_max=Smax, D=D, pos=10, T=T,
+             skc=c4(D, Smax, Hkv), svc=c4(D, Smax, Hkv), skn=c4(D, T, Hkv), svn=c4(D, T, Hkv), dtype=1, stream=None)
+    a.update(kw)
+    return lib.kv_cache_write(a["kc"], a["vc"], a["kn"], a["vn"], a["B"], a["Hkv"], a["S_max"], a["D"], a["pos"],
+                              a["T"], a["skc"], a["svc"], a["skn"], a["svn"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), NULL), (dict(vn=None), NULL),
+    (dict(pos=-1), SHAPE), (dict(pos=62), SHAPE), (dict(T=0), SHAPE), (dict(B=0), SHAPE),
+    (dict(D=12), UNSUP), (dict(dtype=5), UNSUP), (dict(skn=S(8, 8, 8, 8)), UNSUP), (dict(kn=FAKE + 2), UNSUP),
+])
+def test_cache_write_rejects(lib, kw, code):
+    assert cw(lib, **kw) == code
+
+
+def test_workspace_bytes(lib):
+    assert lib.attn_decode_workspace_bytes(0, 32, 8, 8192, 128) == 0
+    assert lib.attn_decode_workspace_bytes(2, 30, 8, 8192, 128) == 0
+    # 16 (batch, kv head) slots x 64 max splits x 4 heads x (128 + 2) floats, after a 256-byte ticket block
+    assert lib.attn_decode_workspace_bytes(2, 32, 8, 8192, 128) == 256 + 16 * 64 * 4 * 130 * 4
+    # 32 q heads per kv head -> 2 groups of 16
+    assert lib.attn_decode_workspace_bytes(1, 32, 1, 128, 64) == 256 + 2 * 1 * 16 * 66 * 4
+
+
+def test_binding_refuses_cpu_tensors():
+    q = torch.zeros(1, 2, 65, 64, dtype=torch.float16)
+    k = torch.zeros(1, 1, 65, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        bd.attn_fwd(q, k, k, causal=True)

@@ -1,0 +1,148 @@
+"""GPU parity of attn_decode and kv_cache_write against the fp64 oracle, plus
+the autoregressive-equivalence test (prefill vs per-token decode with
+interleaved cache writes)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_05_amd as A
+import oracle
+import workloads as W
+from gpu_util import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _np(t):
+    return t.float().numpy().astype(np.float64)
+
+
+def _poisoned(cache: torch.Tensor, cache_len: int) -> torch.Tensor:
+    c = cache.clone()
+    c[:, :, cache_len:] = float("nan")
+    return c
+
+
+def run_decode(case: W.DecodeCase, num_splits=0, ws=None, check=True):
+    q, kc, vc = W.decode_inputs(case)
+    _say(f"{case.name} splits={num_splits}")
+    kd, vd = _poisoned(kc, case.cache_len).to(DEV), _poisoned(vc, case.cache_len).to(DEV)
+    o, l = A.attn_decode(q.to(DEV), kd, vd, case.cache_len, scale=case.softmax_scale, workspace=ws,
+                         num_splits=num_splits, return_lse=True)
+    torch.cuda.synchronize()
+    if check:
+        Oref, Lref = oracle.decode(_np(q), _np(kc), _np(vc), case.cache_len, case.softmax_scale)
+        e = check_o(o, Oref, case.torch_dtype)
+        r = check_lse(l, Lref)
+        print(f"    max|dO| = {e:.3e}, worst lse err/bound = {r:.3f}", flush=True)
+    return o, l
+
+
+@pytest.mark.parametrize("L", W.DECODE_LENS)
+def test_decode_lengths(L):
+    run_decode(W.decode_case(L))
+
+
+@pytest.mark.parametrize("Hkv", [32, 16, 8, 4, 2, 1])
+def test_decode_gqa_ratio_sweep_aligned(Hkv):
+    run_decode(W.decode_case(1024, Hkv=Hkv, seed_offset=Hkv))
+
+
+@pytest.mark.parametrize("L", [1, 31, 33, 63, 65, 127, 257])
+def test_decode_nonaligned_mid_ratio(L):
+    run_decode(W.DecodeCase(f"dec_mid_L{L}", 2, 32, 4, 512, L, 128, "fp16", seed=500 + L))
+
+
+@pytest.mark.parametrize("L", [1, 300, 5000])
+def test_decode_bf16_and_d64(L):
+    run_decode(W.DecodeCase(f"dec_bf16_L{L}", 2, 32, 8, 8192, L, 128, "bf16", seed=600 + L))
+    run_decode(W.DecodeCase(f"dec_d64_L{L}", 3, 12, 4, 8192, L, 64, "fp16", seed=700 + L))
+
+
+def test_decode_split_invariance():
+    case = W.decode_case(8192)
+    ws = A.decode_workspace(case.B, case.Hq, case.Hkv, case.S_max, case.D, DEV)
+    base_o, base_l = run_decode(case, num_splits=1, ws=ws)
+    for s in (2, 3, 7, 64, 10 ** 6, 0):
+        o, l = run_decode(case, num_splits=s, ws=ws, check=(s == 0))
+        # one fp16 ulp of the larger of the two values (ulp(x) <= |x| * 2**-10), with a floor at tiny |x|
+        a, bb = o.float(), base_o.float()
+        bound = torch.maximum(a.abs(), bb.abs()).clamp(min=2.0 ** -14) * 2.0 ** -10
+        d = ((a - bb).abs() / bound).max().item()
+        assert d <= 1.0, (s, d)
+        dl = ((l - base_l).abs() / base_l.abs().clamp(min=1.0)).max().item()
+        assert dl <= 1e-5, (s, dl)
+
+
+def test_workspace_reuse_many_calls():
+    """The arrival counters return to zero: repeated calls on one workspace stay correct."""
+    ws = A.decode_workspace(2, 32, 8, 8192, 128, DEV)
+    for L in (8192, 4096, 129, 8192, 1000, 8192):
+        run_decode(W.decode_case(L, seed_offset=L % 7), ws=ws)
+    assert int(ws[:64].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_kv_cache_write_bitwise():
+    _say("kv_cache_write")
+    g = torch.Generator().manual_seed(8)
+    for dt in (torch.float16, torch.bfloat16):
+        kc = torch.randn(2, 8, 64, 128, generator=g).to(dt)
+        vc = torch.randn(2, 8, 64, 128, generator=g).to(dt)
+        for pos, T in ((0, 1), (17, 5), (63, 1), (0, 64)):
+            kn = torch.randn(2, 8, T, 128, generator=g).to(dt)
+            vn = torch.randn(2, 8, T, 128, generator=g).to(dt)
+            kd, vd = kc.to(DEV), vc.to(DEV)
+            A.kv_cache_write(kd, vd, kn.to(DEV), vn.to(DEV), pos)
+            torch.cuda.synchronize()
+            ek, ev = oracle.kv_cache_write(kc.view(torch.int16).numpy(), vc.view(torch.int16).numpy(),
+                                           kn.view(torch.int16).numpy(), vn.view(torch.int16).numpy(), pos)
+            assert np.array_equal(kd.cpu().view(torch.int16).numpy(), ek)
+            assert np.array_equal(vd.cpu().view(torch.int16).numpy(), ev)
+
+
+def test_kv_cache_write_strided_new_rows():
+    """New rows given as a (B, T, H, D) view are written like contiguous ones."""
+    _say("kv_cache_write strided")
+    g = torch.Generator().manual_seed(9)
+    kc = torch.zeros(2, 4, 32, 64, dtype=torch.float16, device=DEV)
+    vc = torch.zeros_like(kc)
+    kn = torch.randn(2, 3, 4, 64, generator=g).half().to(DEV).transpose(1, 2)  # (B, H, T, D) view
+    vn = torch.randn(2, 3, 4, 64, generator=g).half().to(DEV).transpose(1, 2)
+    A.kv_cache_write(kc, vc, kn, vn, 5)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, :, 5:8], kn) and torch.equal(vc[:, :, 5:8], vn)
+    assert (kc[:, :, :5] == 0).all() and (kc[:, :, 8:] == 0).all()
+
+
+@pytest.mark.parametrize("Hkv", [8, 1])
+def test_autoregressive_equivalence(Hkv):
+    """Causal prefill over 512 tokens equals 512 decode calls, each preceded by
+    the cache write of its own token.  Both sides are also checked against the
+    oracle at the fp16 tolerance."""
+    B, Hq, D, N, S_max = 2, 32, 128, W.AR_TOKENS, 1024
+    _say(f"ar-equivalence Hkv={Hkv}")
+    case = W.PrefillCase("ar", B, Hq, Hkv, N, N, D, "fp16", True, seed=900 + Hkv)
+    q, k, v = W.prefill_inputs(case)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_pre = A.attn_fwd(qd, kd, vd, causal=True)
+    kc = torch.full((B, Hkv, S_max, D), float("nan"), dtype=torch.float16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    ws = A.decode_workspace(B, Hq, Hkv, S_max, D, DEV)
+    o_dec = torch.empty_like(o_pre)
+    for t in range(N):
+        A.kv_cache_write(kc, vc, kd[:, :, t:t + 1], vd[:, :, t:t + 1], t)
+        A.attn_decode(qd[:, :, t], kc, vc, t + 1, workspace=ws, out=o_dec[:, :, t])
+    torch.cuda.synchronize()
+    Oref, _ = oracle.attention_forward(_np(q), _np(k), _np(v), case.softmax_scale, True)
+    check_o(o_pre, Oref, torch.float16, "prefill")
+    check_o(o_dec, Oref, torch.float16, "decode")
+    d = (o_pre.float() - o_dec.float()).abs().max().item()
+    assert d <= 2e-3, d

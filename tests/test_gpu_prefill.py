@@ -1,0 +1,189 @@
+"""GPU parity of attn_fwd against the fp64 oracle (runs on an MI355X).
+
+Every case prints its name before touching the GPU so a failure is attributable.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_05_amd as A
+import oracle
+import workloads as W
+from gpu_util import O_TOL, check_lse, check_o, sample_rows, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _np(t):
+    return t.float().numpy().astype(np.float64)
+
+
+def run_case(case: W.PrefillCase, rows=None, lse=True):
+    q, k, v = W.prefill_inputs(case)
+    _say(f"{case.name} seed={case.seed}")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, l = A.attn_fwd(qd, kd, vd, causal=case.causal, scale=case.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.attention_forward(_np(q), _np(k), _np(v), case.softmax_scale, case.causal, rows=rows)
+    og, lg = (o, l) if rows is None else (o[:, :, torch.as_tensor(rows)], l[:, :, torch.as_tensor(rows)])
+    assert torch.isfinite(o.float()).all(), "non-finite output somewhere in the full result"
+    e = check_o(og, Oref, case.torch_dtype)
+    r = check_lse(lg, Lref)
+    print(f"    max|dO| = {e:.3e} (tol {O_TOL[case.torch_dtype]}), worst lse err/bound = {r:.3f}", flush=True)
+    return o, l
+
+
+def test_tiny():
+    run_case(W.TINY)
+
+
+@pytest.mark.parametrize("case", W.gqa_sweep(), ids=lambda c: c.name)
+def test_gqa_sweep(case):
+    run_case(case)
+
+
+@pytest.mark.parametrize("n", [2048, 4096, 8192])
+@pytest.mark.parametrize("causal", [True, False])
+def test_serving_sampled(n, causal):
+    case = W.serving(n, causal)
+    rows = sample_rows(n, causal, np.random.default_rng(n + causal))
+    run_case(case, rows=rows)
+
+
+def test_cross_mqa_bf16_sampled():
+    rows = sample_rows(W.CROSS.Nq, False, np.random.default_rng(5))
+    run_case(W.CROSS, rows=rows)
+
+
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, Nq, Nkv, D, dtype, causal
+    (1, 1, 1, 1, 1, 64, "fp16", True),
+    (1, 1, 1, 1, 1, 128, "bf16", False),
+    (2, 4, 2, 1, 300, 128, "fp16", False),
+    (1, 4, 1, 100, 300, 64, "fp16", False),
+    (1, 2, 2, 300, 100, 128, "fp16", True),   # Nq > Nkv, top-left causal
+    (1, 2, 1, 100, 300, 128, "fp16", True),   # Nq < Nkv, top-left causal
+    (2, 8, 8, 257, 257, 128, "bf16", True),
+    (1, 6, 3, 129, 65, 64, "bf16", False),
+    (3, 4, 4, 191, 191, 64, "fp16", True),
+])
+def test_edge_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, D, dt, causal = shape
+    case = W.PrefillCase(f"edge_{B}x{Hq}x{Hkv}x{Nq}x{Nkv}x{D}_{dt}_{causal}", B, Hq, Hkv, Nq, Nkv, D, dt, causal,
+                         seed=1000 + Nq + Nkv + D)
+    run_case(case)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.5])
+def test_scale_values(scale):
+    case = W.PrefillCase(f"scale_{scale}", 1, 4, 2, 200, 200, 64, "fp16", True, scale=scale, seed=77)
+    run_case(case)
+
+
+def test_causal_row0_and_equal_scores():
+    """Row 0 under causal masking returns V[0] exactly; Q = 0 returns running means of V."""
+    _say("row0 / equal scores")
+    g = torch.Generator().manual_seed(3)
+    B, Hq, Hkv, N, D = 1, 4, 2, 300, 128
+    q = torch.randn(B, Hq, N, D, generator=g).half()
+    k = torch.randn(B, Hkv, N, D, generator=g).half()
+    v = torch.randn(B, Hkv, N, D, generator=g).half()
+    o = A.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True).cpu()
+    assert torch.equal(o[:, :, 0], v.repeat_interleave(2, dim=1)[:, :, 0])
+    z = torch.zeros_like(q)
+    o0, l0 = A.attn_fwd(z.to(DEV), k.to(DEV), v.to(DEV), causal=True, return_lse=True)
+    vv = _np(v).repeat(2, axis=1)
+    means = np.cumsum(vv, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    check_o(o0, means, torch.float16)
+    check_lse(l0, np.broadcast_to(np.log(np.arange(1, N + 1)), (B, Hq, N)))
+
+
+def test_gqa_equals_expanded_mha_bitwise():
+    _say("gqa vs expanded mha")
+    case = W.PrefillCase("gqa_expand", 2, 16, 2, 333, 333, 128, "fp16", True, seed=9)
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(case))
+    o1 = A.attn_fwd(q, k, v, causal=True)
+    o2 = A.attn_fwd(q, k.repeat_interleave(8, 1).contiguous(), v.repeat_interleave(8, 1).contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_bnhd_layout_matches_contiguous():
+    """Strided (B, N, H, D) views give the same result as contiguous (B, H, N, D)."""
+    _say("layout (B,N,H,D)")
+    case = W.PrefillCase("layout", 2, 8, 2, 250, 250, 128, "bf16", True, seed=11)
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(case))
+    ref = A.attn_fwd(q, k, v, causal=True)
+    qs = q.transpose(1, 2).contiguous().transpose(1, 2)
+    ks = k.transpose(1, 2).contiguous().transpose(1, 2)
+    vs = v.transpose(1, 2).contiguous().transpose(1, 2)
+    out = torch.empty(2, 250, 8, 128, dtype=q.dtype, device=DEV).transpose(1, 2)
+    got = A.attn_fwd(qs, ks, vs, causal=True, out=out)
+    torch.cuda.synchronize()
+    assert got.stride() == out.stride()
+    assert torch.equal(got, ref)
+
+
+def test_out_of_bounds_guards():
+    """K/V rows past Nkv are NaN (never read); O rows past Nq and guard bands stay untouched;
+    every element of the output view is written (NaN prefill must disappear)."""
+    _say("oob guards")
+    B, Hq, Hkv, Nq, Nkv, D = 2, 4, 2, 190, 130, 64
+    case = W.PrefillCase("oob", B, Hq, Hkv, Nq, Nkv, D, "fp16", False, seed=21)
+    q, k, v = W.prefill_inputs(case)
+    pad = 70
+    kb = torch.full((B, Hkv, Nkv + pad, D), float("nan"), dtype=torch.float16)
+    vb = torch.full((B, Hkv, Nkv + pad, D), float("nan"), dtype=torch.float16)
+    kb[:, :, :Nkv] = k
+    vb[:, :, :Nkv] = v
+    kd, vd = kb.to(DEV)[:, :, :Nkv], vb.to(DEV)[:, :, :Nkv]
+    ob = torch.full((B, Hq, Nq + pad, D), 7.0, dtype=torch.float16, device=DEV)
+    ob[:, :, :Nq] = float("nan")
+    guard = torch.full((3 * 4096,), -3.0, dtype=torch.float32, device=DEV)
+    lse = guard[4096:4096 + B * Hq * Nq].view(B, Hq, Nq)
+    o, l = A.attn_fwd(q.to(DEV), kd, vd, causal=False, out=ob[:, :, :Nq], lse=lse, return_lse=True)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.attention_forward(_np(q), _np(k), _np(v), case.softmax_scale, False)
+    check_o(o, Oref, torch.float16)
+    check_lse(l, Lref)
+    assert (ob[:, :, Nq:] == 7.0).all()
+    assert (guard[:4096] == -3.0).all() and (guard[4096 + B * Hq * Nq:] == -3.0).all()
+    for causal in (True,):
+        o2, l2 = A.attn_fwd(q.to(DEV)[:, :, :Nkv], kd, vd, causal=causal, return_lse=True)
+        Oref2, Lref2 = oracle.attention_forward(_np(q)[:, :, :Nkv], _np(k), _np(v), case.softmax_scale, causal)
+        check_o(o2, Oref2, torch.float16)
+        check_lse(l2, Lref2)
+
+
+def test_deterministic():
+    _say("determinism")
+    case = W.serving(2048, True)
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(case))
+    o1, l1 = A.attn_fwd(q, k, v, causal=True, return_lse=True)
+    o2, l2 = A.attn_fwd(q, k, v, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_whole_output_properties_8192():
+    """At the headline size every row is finite and bounded by max|V| (a convex combination)."""
+    _say("properties serve_n8192 causal")
+    case = W.serving(8192, True)
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(case))
+    o, l = A.attn_fwd(q, k, v, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(l).all()
+    vmax = v.float().abs().amax(dim=2).repeat_interleave(4, 1)  # per (b, h, d)
+    assert (o.float().abs() <= vmax[:, :, None, :] * (1 + 1e-3) + 1e-3).all()
+    # lse of row i is at least the (scaled) score of its diagonal key and at most that plus ln(i+1) + max gap
+    assert math.isfinite(float(l.max()))
