@@ -32,6 +32,19 @@ inline bool dtype_ok(attn_dtype t) { return t == ATTN_F16 || t == ATTN_BF16; }
 
 inline uint32_t q_sign_mask(float scale) { return std::signbit(scale) ? 0x80008000u : 0u; }
 
+// Scores are scaled by c = |scale| log2(e) after the sign is folded into Q.  A
+// zero scale becomes a tiny positive c: every visible score is then ~0 (to far
+// below fp32 resolution) while masked keys still map to -inf, not to NaN.
+inline float score_coef(float scale) {
+  const float c = std::fabs(scale) * kLog2e;
+  return c > 0.f ? c : 1e-30f;
+}
+
+// Per-lane buffer offsets inside a tile must fit in 31 bits.
+constexpr int64_t kMaxRowStride = int64_t(1) << 22;
+
+inline int64_t slice_bytes(int64_t rows, int64_t stride_n, int D) { return ((rows - 1) * stride_n + D) * 2; }
+
 struct DecodeGeometry {
   int hgroups, heads_per_wg, max_splits;
   size_t ticket_bytes, part_bytes;
@@ -77,6 +90,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
+  if (sq.n > kMaxRowStride || sk.n > kMaxRowStride || sv.n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
   const int64_t nqb = ((int64_t)Nq + kPrefillRows - 1) / kPrefillRows;
   const int64_t nblocks = nqb * Hq * B;
   if (nblocks > INT_MAX) return ATTN_ERR_SHAPE;
@@ -102,8 +116,11 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   const int64_t per_unit = (int64_t)a.group * nqb;
   a.remap = (nblocks % 8 == 0) && per_xcd > 0 &&
             ((per_xcd % per_unit == 0) || (!causal && per_unit % per_xcd == 0));
-  a.c = std::fabs(scale) * kLog2e;
+  a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
+  a.q_bytes = slice_bytes(Nq, sq.n, D);
+  a.k_bytes = slice_bytes(Nkv, sk.n, D);
+  a.v_bytes = slice_bytes(Nkv, sv.n, D);
 
   const hipError_t e = attn::launch_prefill(a, D, dtype == ATTN_BF16, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -166,7 +183,7 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.hgroups = g.hgroups;
   a.nsplit = nsplit;
   a.rows_per_split = tiles_per_split * kDecodeTile;
-  a.c = std::fabs(scale) * kLog2e;
+  a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
   a.tickets = static_cast<uint32_t*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ticket_bytes);

@@ -42,17 +42,49 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // Two fp32 values -> two 16-bit values (round to nearest even) in one dword,
-// `lo` in the low half.
+// `lo` in the low half (one v_cvt_pk_{f16,bf16}_f32 on gfx950).
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  if constexpr (BF16) {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-  } else {
-    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-  }
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+
+// acc + lo + hi of a packed pair of 16-bit values, in fp32 (v_dot2c_f32_{f16,bf16}).
+template <bool BF16>
+__device__ __forceinline__ float sum2(uint32_t pair, float acc) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), (bf16x2){(__bf16)1.0f, (__bf16)1.0f},
+                                           acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), (f16x2){(_Float16)1.0f, (_Float16)1.0f}, acc,
+                                  false);
+}
+
+// max / sum of x over lanes l and l ^ 32 (one ds_bpermute through the LDS crossbar).
+__device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+
+// Buffer resource over [base, base + bytes): 16-byte loads at byte offsets
+// >= bytes return zeros (hardware range check), so ragged tails need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Low (SEL = 0x05040100) or high (SEL = 0x07060302) 16-bit halves of two dwords:
+// result = {a.half, b.half} with a's half in the low 16 bits.
+template <uint32_t SEL>
+__device__ __forceinline__ uint32_t halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, SEL);
 }
 
 template <bool BF16>

@@ -22,8 +22,11 @@ struct FwdArgs {
   int nqb;      // number of 128-row query blocks
   int nblocks;  // grid size
   int remap;    // 1: XCD-aware block remap is valid for this grid
-  float c;      // |scale| * log2(e)
+  float c;      // |scale| * log2(e), or a tiny positive value when scale == 0
   uint32_t qsign;  // 0x80008000 when scale < 0: flip Q's sign bits (exact)
+  // bytes from a (batch, head) slice's first element to the end of its last
+  // valid row: buffer loads at or past this offset read zeros
+  int64_t q_bytes, k_bytes, v_bytes;
 };
 
 hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, hipStream_t stream);

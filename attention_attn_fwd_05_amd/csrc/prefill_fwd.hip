@@ -8,10 +8,12 @@
 //
 // gfx950 design (not the pages' Triton tiling):
 //   * one workgroup = 4 wave64s = 128 query rows of one q head; each wave owns
-//     32 rows for the whole KV loop.
+//     32 rows for the whole KV loop.  Two workgroups share a CU.
 //   * KV tiles of 64 rows are staged in LDS, double buffered: K row-major, V
 //     transposed (head-dim major) so both MFMA operands are single 16-byte LDS
-//     reads.  Global loads for tile t+1 are issued before tile t is computed.
+//     reads.  Global loads for tile t+1 are issued before tile t is computed;
+//     they are buffer loads whose hardware range check returns zeros past the
+//     last key, so ragged tails need no branches.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //     Q is the register-resident B operand and each lane ends up owning one
 //     query row's scores.  The K rows fed to the MFMA are permuted (bits 2 and
@@ -19,13 +21,18 @@
 //     are exactly the B operand layout of the P.V MFMA: no data movement
 //     between the two contractions.
 //   * online softmax in the log2 domain: t = s * scale * log2(e); the row max
-//     needs one cross-lane exchange (lanes l and l+32 share a row); P goes to
-//     16 bits with round-to-nearest-even right before the P.V MFMA; m, l and
-//     the O accumulator stay fp32.  O is rescaled by alpha only when some row
-//     of the wave changed its max (alpha == 1 otherwise: skipping is exact).
-//   * causal: the KV loop stops at the block's diagonal, subtiles wholly above
-//     a wave's diagonal are skipped, and the per-element compare runs only on
-//     tiles that straddle the diagonal or the KV tail.
+//     needs one cross-lane exchange (lanes l and l+32 share a row); the row
+//     sum l is accumulated from the fp32 P, which then goes to 16 bits (round
+//     to nearest even) right before the P.V MFMA; m, l and O stay fp32.
+//   * the reference max used for exp2 moves -- rescaling O and l by alpha --
+//     only when a row's max exceeds it by more than 2^8.  O and l are always
+//     relative to the same reference, so O / l is unchanged (the rescale of
+//     step 5f is an identity); P stays <= 256, well inside fp16/bf16 range.
+//   * causal: the KV loop stops at the block's diagonal; tiles below every
+//     row's diagonal take a path with no per-element compare, and on the last
+//     tiles each wave skips 32-key subtiles that lie wholly above its rows.
+#include <type_traits>
+
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
@@ -33,8 +40,9 @@ namespace attn {
 
 namespace {
 
-constexpr int kBM = 128;  // query rows per workgroup
-constexpr int kBN = 64;   // key rows per LDS tile
+constexpr int kBM = 128;             // query rows per workgroup
+constexpr int kBN = 64;              // key rows per LDS tile
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct PrefillLds {
@@ -44,6 +52,10 @@ struct PrefillLds {
   static constexpr int VSZ = D * VLD;    // elements per V^T stage
   static constexpr int STAGE = KSZ + VSZ;
 };
+
+__device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
+  return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
+}
 
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
@@ -77,186 +89,193 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
   const int q0 = qb * kBM;
   const int qrow = q0 + 32 * w + n;
 
-  // ---- Q fragment, register resident: B operand of S^T = K Q^T
+  // ---- Q fragment, register resident: B operand of S^T = K Q^T (rows >= Nq read as 0)
   u32x4 qf[KS];
   {
-    const uint16_t* qp = a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh + (int64_t)qrow * a.sqn;
-    const bool ok = qrow < a.Nq;
+    const int64_t qblk = (int64_t)q0 * a.sqn;
+    const auto rq = make_rsrc(a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh + qblk,
+                              clamp_bytes(a.q_bytes - 2 * qblk));
+    const int32_t qoff = (32 * w + n) * (int32_t)a.sqn * 2 + 16 * hh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 x = ok ? load16(qp + 16 * ks + 8 * hh) : u32x4{0, 0, 0, 0};
-      qf[ks] = x ^ a.qsign;
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = bload16(rq, qoff + 32 * ks) ^ a.qsign;
   }
 
-  const uint16_t* kp = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
-  const uint16_t* vp = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
+  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
+  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
   const int kv_end = CAUSAL ? min(a.Nkv, q0 + kBM) : a.Nkv;
   const int ntiles = (kv_end + kBN - 1) / kBN;
+  // tiles every row of this block sees in full (no mask): below the block's
+  // diagonal and before the key tail
+  const int n_full = CAUSAL ? min(q0, a.Nkv) / kBN : a.Nkv / kBN;
 
-  // ---- global -> register staging of one KV tile
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
+  // ---- per-thread staging geometry (constant over the loop)
+  int32_t koff[KCH];
+  int kw[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int id = tid + 256 * i;
+    const int row = id / (D / 8), col = id % (D / 8);
+    koff[i] = row * (int32_t)a.skn * 2 + 16 * col;
+    kw[i] = row * L::KLD + 8 * col;
+  }
+  const bool vthr = tid < VBLK;
   const int v_kvg = tid % (kBN / 4);  // 4-row group of this thread's V block
   const int v_dc = tid / (kBN / 4);   // 8-column chunk of this thread's V block
+  int32_t voff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) voff[r] = (4 * v_kvg + r) * (int32_t)a.svn * 2 + 16 * v_dc;
+  const int vw = 8 * v_dc * L::VLD + 4 * v_kvg;
+
+  u32x4 kreg[KCH];
+  u32x4 vreg[4];
   auto gload = [&](int t) {
-    const int kb = t * kBN;
+    const int64_t ko = (int64_t)t * kBN * a.skn;
+    const auto rk = make_rsrc(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id / (D / 8), col = id % (D / 8);
-      kreg[i] = (kb + row < a.Nkv) ? load16(kp + (int64_t)(kb + row) * a.skn + 8 * col) : u32x4{0, 0, 0, 0};
-    }
-    if (tid < VBLK) {
+    for (int i = 0; i < KCH; ++i) kreg[i] = bload16(rk, koff[i]);
+    if (vthr) {
+      const int64_t vo = (int64_t)t * kBN * a.svn;
+      const auto rv = make_rsrc(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = kb + 4 * v_kvg + r;
-        vreg[r] = (row < a.Nkv) ? load16(vp + (int64_t)row * a.svn + 8 * v_dc) : u32x4{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 4; ++r) vreg[r] = bload16(rv, voff[r]);
     }
   };
-  auto swrite = [&](int buf) {
-    uint16_t* Ks = smem + buf * L::STAGE;
+  auto swrite = [&](uint16_t* Ks) {
     uint16_t* Vs = Ks + L::KSZ;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id / (D / 8), col = id % (D / 8);
-      store16(Ks + row * L::KLD + 8 * col, kreg[i]);
-    }
-    if (tid < VBLK) {
-      // transpose the 4x8 block: V^T row d gets the 4 keys of this group
+    for (int i = 0; i < KCH; ++i) store16(Ks + kw[i], kreg[i]);
+    if (vthr) {
+      // transpose the 4x8 block: V^T row d receives the 4 keys of this group
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        const uint32_t x0 = (vreg[0][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x1 = (vreg[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x2 = (vreg[2][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x3 = (vreg[3][e >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2*>(Vs + (8 * v_dc + e) * L::VLD + 4 * v_kvg) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 lo{halves<0x05040100u>(vreg[0][j], vreg[1][j]), halves<0x05040100u>(vreg[2][j], vreg[3][j])};
+        const u32x2 hi{halves<0x07060302u>(vreg[0][j], vreg[1][j]), halves<0x07060302u>(vreg[2][j], vreg[3][j])};
+        *reinterpret_cast<u32x2*>(Vs + vw + (2 * j) * L::VLD) = lo;
+        *reinterpret_cast<u32x2*>(Vs + vw + (2 * j + 1) * L::VLD) = hi;
       }
     }
   };
 
-  // ---- online softmax state (fp32): running max m (log2 domain), this lane's
-  //      share of the running sum l, and the O^T accumulator
+  // ---- online softmax state (fp32): reference max m (log2 domain), this
+  //      lane's share of the running sum l, and the O^T accumulator
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   float m = -INFINITY;
   float l = 0.f;
-  const float c = a.c;
+  const float c = a.c;  // > 0
   // K row fed to MFMA row n: swap bits 2 and 3 so that score register e of a
   // lane holds key 16*(e/8) + 8*hh + e%8 of its 32-key subtile.
   const int sig = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
+  const int kr = sig * L::KLD + 8 * hh;
+  const int vr = n * L::VLD + 8 * hh;
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
 
-  auto compute = [&](int t, int buf) {
-    const int kb = t * kBN;
-    const bool act0 = kb < a.Nkv && (!CAUSAL || kb <= wq_hi);
-    if (!act0) return;  // the whole tile is above this wave's diagonal
-    const bool act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi);
-    const bool need_mask = (kb + kBN > a.Nkv) || (CAUSAL && kb + kBN - 1 > wq_lo);
-    const uint16_t* Ks = smem + buf * L::STAGE;
+  auto compute = [&](const uint16_t* Ks, int t, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const uint16_t* Vs = Ks + L::KSZ;
-
+    const int kb = t * kBN;
+    bool act1 = true;
+    if constexpr (MASKED) {
+      if (kb >= a.Nkv || (CAUSAL && kb > wq_hi)) return;  // whole tile above this wave's rows
+      act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi);
+    }
     // S^T = K Q^T for the two 32-key subtiles
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      s0 = mfma_32x32x16<BF16>(load16(Ks + sig * L::KLD + 16 * ks + 8 * hh), qf[ks], s0);
+    for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(load16(Ks + kr + 16 * ks), qf[ks], s0);
     if (act1) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s1 = mfma_32x32x16<BF16>(load16(Ks + (32 + sig) * L::KLD + 16 * ks + 8 * hh), qf[ks], s1);
+        s1 = mfma_32x32x16<BF16>(load16(Ks + 32 * L::KLD + kr + 16 * ks), qf[ks], s1);
     }
-
-    // row max of the scaled scores (mask first, then reduce)
-    float mx = -INFINITY;
-    if (!need_mask) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-      mx *= c;
-    } else {
+    if constexpr (MASKED) {
+      // mask before the row max: key index of register e is kb + 16*(e/8) + 8*hh + e%8
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kv0 = kb + 16 * (e >> 3) + 8 * hh + (e & 7);
         const int kv1 = kv0 + 32;
         const bool vis0 = kv0 < a.Nkv && (!CAUSAL || kv0 <= qrow);
         const bool vis1 = act1 && kv1 < a.Nkv && (!CAUSAL || kv1 <= qrow);
-        s0[e] = vis0 ? s0[e] * c : -INFINITY;
-        s1[e] = vis1 ? s1[e] * c : -INFINITY;
-        mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+        s0[e] = vis0 ? s0[e] : -INFINITY;
+        s1[e] = vis1 ? s1[e] : -INFINITY;
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // a row with nothing visible yet
-    const float alpha = fast_exp2(m - m_use);
-
-    // P = exp2(t - m), its row sum, and the 16-bit B operand of P.V
-    u32x4 pf[4];
-    float rs = 0.f;
-    if (!need_mask) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s0[e], c, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(s0[e + 1], c, -m_use));
-        const float p2 = fast_exp2(__builtin_fmaf(s1[e], c, -m_use));
-        const float p3 = fast_exp2(__builtin_fmaf(s1[e + 1], c, -m_use));
-        rs += (p0 + p1) + (p2 + p3);
-        pf[(e >> 3)][(e & 7) >> 1] = pack2<BF16>(p0, p1);
-        pf[2 + (e >> 3)][(e & 7) >> 1] = pack2<BF16>(p2, p3);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = fast_exp2(s0[e] - m_use);
-        const float p1 = fast_exp2(s0[e + 1] - m_use);
-        const float p2 = fast_exp2(s1[e] - m_use);
-        const float p3 = fast_exp2(s1[e + 1] - m_use);
-        rs += (p0 + p1) + (p2 + p3);
-        pf[(e >> 3)][(e & 7) >> 1] = pack2<BF16>(p0, p1);
-        pf[2 + (e >> 3)][(e & 7) >> 1] = pack2<BF16>(p2, p3);
-      }
-    }
-    l = l * alpha + rs;
-    m = m_new;
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    mx = max_xor32(mx) * c;  // this row's max in the log2 domain
 
-    // alpha rescale of the accumulator before adding this tile's P.V
-    if (__any(alpha != 1.f)) {
+    // move the reference max only when some row's max outgrew it by > 2^8
+    if (__any(mx > m + kRescaleLog2)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      l *= alpha;
+      m = m_new;
     }
+    const float m_use = (m == -INFINITY) ? 0.f : m;  // rows with nothing visible yet get P = 0
+
+    // P = exp2(s*c - m) in fp32, its fp32 row sum, then the 16-bit B operand of P.V
+    u32x4 pf[4];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(s0[e], c, -m_use));
+      const float p1 = fast_exp2(__builtin_fmaf(s0[e + 1], c, -m_use));
+      const float p2 = fast_exp2(__builtin_fmaf(s1[e], c, -m_use));
+      const float p3 = fast_exp2(__builtin_fmaf(s1[e + 1], c, -m_use));
+      rs0 += p0 + p1;
+      rs1 += p2 + p3;
+      pf[e >> 3][(e & 7) >> 1] = pack2<BF16>(p0, p1);
+      pf[2 + (e >> 3)][(e & 7) >> 1] = pack2<BF16>(p2, p3);
+    }
+    l += rs0 + rs1;
 
     // O^T += V^T P^T : A = V^T rows from LDS, B = P^T from registers
-    const int nk = act1 ? 4 : 2;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (kk < nk) {
+      if (kk < 2 || act1) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          oacc[dt] = mfma_32x32x16<BF16>(load16(Vs + (32 * dt + n) * L::VLD + 16 * kk + 8 * hh), pf[kk], oacc[dt]);
+          oacc[dt] = mfma_32x32x16<BF16>(load16(Vs + 32 * dt * L::VLD + vr + 16 * kk), pf[kk], oacc[dt]);
       }
     }
   };
+  using full_t = std::false_type;
+  using mask_t = std::true_type;
+  uint16_t* const S0 = smem;
+  uint16_t* const S1 = smem + L::STAGE;
 
-  // ---- KV loop, double-buffered LDS
+  // ---- KV loop, double-buffered LDS.  Full tiles in pairs (stage 0, stage 1),
+  //      then the remaining tiles (diagonal / key tail) on the masked path.
   if (ntiles > 0) {
     gload(0);
-    swrite(0);
+    swrite(S0);
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    gload(t + 1);
+    compute(S0, t, full_t{});
+    swrite(S1);
+    __syncthreads();
+    if (t + 2 < ntiles) gload(t + 2);
+    compute(S1, t + 1, full_t{});
+    if (t + 2 < ntiles) swrite(S0);
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
+    const bool odd = t & 1;
     if (t + 1 < ntiles) gload(t + 1);
-    compute(t, buf);
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+    compute(odd ? S1 : S0, t, mask_t{});
+    if (t + 1 < ntiles) swrite(odd ? S0 : S1);
     __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, cast, store; lse = (m + log2 l) ln 2
-  l += __shfl_xor(l, 32);
+  l = sum_xor32(l);
   if (qrow < a.Nq) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     uint16_t* op = a.o + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)qrow * a.son;

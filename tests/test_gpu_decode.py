@@ -73,9 +73,11 @@ def test_decode_split_invariance():
     base_o, base_l = run_decode(case, num_splits=1, ws=ws)
     for s in (2, 3, 7, 64, 10 ** 6, 0):
         o, l = run_decode(case, num_splits=s, ws=ws, check=(s == 0))
-        # one fp16 ulp of the larger of the two values (ulp(x) <= |x| * 2**-10), with a floor at tiny |x|
+        # one fp16 ulp of the larger value (ulp(x) <= |x| * 2**-10), plus an absolute 2**-16 for
+        # outputs near zero, where fp32 sums taken in a different split order legitimately differ
+        # by more than one ulp of the (cancelled) result
         a, bb = o.float(), base_o.float()
-        bound = torch.maximum(a.abs(), bb.abs()).clamp(min=2.0 ** -14) * 2.0 ** -10
+        bound = torch.maximum(a.abs(), bb.abs()) * 2.0 ** -10 + 2.0 ** -16
         d = ((a - bb).abs() / bound).max().item()
         assert d <= 1.0, (s, d)
         dl = ((l - base_l).abs() / base_l.abs().clamp(min=1.0)).max().item()
