@@ -12,7 +12,7 @@ Entry points (same names as the C ABI):
 * ``attn_decode(q, k_cache, v_cache, cache_len, *, scale=None, workspace=None,
   num_splits=0, return_lse=False, out=None)``
 * ``attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)`` /
-  ``decode_workspace(...)`` (a zero-filled uint8 tensor of that size)
+  ``decode_workspace(...)`` (a uint8 scratch tensor of that size)
 * ``kv_cache_write(k_cache, v_cache, k_new, v_new, pos)``
 """
 

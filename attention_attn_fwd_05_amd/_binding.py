@@ -135,11 +135,11 @@ def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, S_max: int, D: int) -
 
 
 def decode_workspace(B: int, Hq: int, Hkv: int, S_max: int, D: int, device) -> torch.Tensor:
-    """A zero-filled workspace for attn_decode (reusable across calls on one stream)."""
+    """Scratch for attn_decode (reusable across calls on one stream; needs no initialisation)."""
     n = attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)
     if n == 0:
         raise ValueError("invalid decode sizes")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: int, *,
@@ -147,9 +147,9 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, c
                 return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """Decode one token per (batch, q head) over cache slots [0, cache_len).
 
-    q (B,Hq,D); caches (B,Hkv,S_max,D).  ``workspace`` must come from
-    ``decode_workspace`` (or be zero-filled before its first use); if omitted a
-    fresh one is allocated for this call.
+    q (B,Hq,D); caches (B,Hkv,S_max,D).  ``workspace`` is scratch of at least
+    ``attn_decode_workspace_bytes`` bytes (see ``decode_workspace``); if omitted
+    a fresh one is allocated for this call.
     """
     lib = load_library()
     B, Hq, D = q.shape

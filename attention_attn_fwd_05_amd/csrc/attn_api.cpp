@@ -17,8 +17,12 @@ namespace {
 constexpr int kPrefillRows = 128;  // query rows per prefill workgroup
 constexpr int kDecodeTile = 128;   // cache rows per decode tile
 constexpr int kDecodeMaxHeads = 16;
-constexpr int kTargetWorkgroups = 256;  // one decode workgroup per CU fills MI355X
-constexpr size_t kTicketAlign = 256;
+constexpr int kDecodeMaxSplits = 64;     // partials one combine merges
+#ifndef ATTN_DECODE_TARGET_WGS
+#define ATTN_DECODE_TARGET_WGS 512
+#endif
+constexpr int kDecodeTargetWorkgroups = ATTN_DECODE_TARGET_WGS;  // decode workgroups that fill MI355X (2 per CU)
+constexpr int kDecodePartPad = 4;       // floats ahead of o[D] in a per-head partial
 constexpr float kLog2e = 1.4426950408889634f;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -47,7 +51,7 @@ inline int64_t slice_bytes(int64_t rows, int64_t stride_n, int D) { return ((row
 
 struct DecodeGeometry {
   int hgroups, heads_per_wg, max_splits;
-  size_t ticket_bytes, part_bytes;
+  size_t part_bytes;
 };
 
 DecodeGeometry decode_geometry(int B, int Hq, int Hkv, int S_max, int D) {
@@ -55,10 +59,10 @@ DecodeGeometry decode_geometry(int B, int Hq, int Hkv, int S_max, int D) {
   const int group = Hq / Hkv;
   g.hgroups = (group + kDecodeMaxHeads - 1) / kDecodeMaxHeads;
   g.heads_per_wg = (group + g.hgroups - 1) / g.hgroups;
-  g.max_splits = (S_max + kDecodeTile - 1) / kDecodeTile;
+  const int tiles = (S_max + kDecodeTile - 1) / kDecodeTile;
+  g.max_splits = tiles < kDecodeMaxSplits ? tiles : kDecodeMaxSplits;
   const size_t slots = (size_t)B * Hkv * g.hgroups;
-  g.ticket_bytes = ((slots * sizeof(uint32_t) + kTicketAlign - 1) / kTicketAlign) * kTicketAlign;
-  g.part_bytes = slots * (size_t)g.max_splits * g.heads_per_wg * (size_t)(D + 2) * sizeof(float);
+  g.part_bytes = slots * (size_t)g.max_splits * g.heads_per_wg * (size_t)(D + kDecodePartPad) * sizeof(float);
   return g;
 }
 
@@ -129,7 +133,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
   const DecodeGeometry g = decode_geometry(B, Hq, Hkv, S_max, D);
-  return g.ticket_bytes + g.part_bytes;
+  return g.part_bytes;
 }
 
 attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -150,19 +154,17 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
   const DecodeGeometry g = decode_geometry(B, Hq, Hkv, S_max, D);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < g.ticket_bytes + g.part_bytes)
+  if (!workspace || !aligned16(workspace) || workspace_bytes < g.part_bytes)
     return ATTN_ERR_WORKSPACE;
   if ((int64_t)B * Hkv > 65535 || g.hgroups > 65535) return ATTN_ERR_SHAPE;  // grid y/z limits
 
-  const int units = B * Hkv;
   const int tiles = (cache_len + kDecodeTile - 1) / kDecodeTile;
-  int want;
-  if (num_splits > 0) {
-    want = num_splits;
-  } else {
-    const int wgs_per_split = units * g.hgroups;
-    want = (kTargetWorkgroups + wgs_per_split - 1) / wgs_per_split;
-  }
+  // default: enough chunks for ~kDecodeTargetWorkgroups workgroups (two per CU,
+  // each with two 128-row tiles in flight), at most max_splits per (batch, kv
+  // head, head group)
+  const int slots = B * Hkv * g.hgroups;
+  int want = num_splits > 0 ? num_splits : (kDecodeTargetWorkgroups + slots - 1) / slots;
+  if (want > g.max_splits) want = g.max_splits;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   const int tiles_per_split = (tiles + want - 1) / want;
@@ -182,11 +184,11 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.heads_per_wg = g.heads_per_wg;
   a.hgroups = g.hgroups;
   a.nsplit = nsplit;
+  a.max_splits = g.max_splits;
   a.rows_per_split = tiles_per_split * kDecodeTile;
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
-  a.tickets = static_cast<uint32_t*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + g.ticket_bytes);
+  a.part = static_cast<float*>(workspace);
 
   const hipError_t e = attn::launch_decode(a, B, D, dtype == ATTN_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

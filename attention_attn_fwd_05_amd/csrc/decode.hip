@@ -12,17 +12,25 @@
 // one is split along the cache so that a 16-unit problem fills 256 CUs):
 //   * a workgroup = 4 wave64s handles one (batch, kv head), up to 16 of the q
 //     heads that share it (K/V are read from HBM once for the whole group), and
-//     one contiguous chunk ("split") of the cache.
-//   * 128-key tiles are staged in LDS (K row-major, V transposed), double
-//     buffered; each wave takes 32 keys of a tile.
+//     one contiguous chunk ("split") of the cache, normally a single 128-key
+//     tile, so that all of a workgroup's loads are in flight at once and up to
+//     four workgroups share a CU.
+//   * each wave takes 32 keys of a tile.  K goes straight from HBM into
+//     registers in MFMA operand layout (buffer loads; keys past the split end
+//     read as zero and are masked); V is staged through LDS transposed, the
+//     layout the P.V MFMA needs.
 //   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32; the q heads of the
 //     group are the 16 MFMA columns.  K rows are fed in a permuted order so the
 //     score registers are directly the B operand of the P.V MFMA.
-//   * each workgroup merges its 4 waves' (m, l, o) in LDS; with one split it
-//     writes the normalised output, otherwise it stores its partial and the
-//     last workgroup of the (batch, kv head, head group) to arrive -- counted
-//     with a device-scope atomic ticket -- merges all partials with the same
-//     max/rescale identity and resets the ticket to zero.
+//   * each workgroup merges its 4 waves' (m, l, o) in LDS.  With one split it
+//     writes the normalised output; otherwise it stores its partial
+//     (m, l, unnormalised o) and a second, small kernel merges the partials of
+//     every (batch, q head) with the same max/rescale identity, in parallel
+//     over head-dim columns and split groups.  The kernel boundary orders the
+//     two, so no workgroup waits on or signals another.  (A single kernel in
+//     which the last workgroup to finish merges measured slower on MI355X:
+//     device-coherent publication costs every workgroup a store drain and an
+//     atomic, more than the second launch costs.)
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
@@ -30,27 +38,36 @@ namespace attn {
 
 namespace {
 
-constexpr int kDT = 128;  // keys per LDS tile (32 per wave)
+constexpr int kDT = 128;        // keys per tile (32 per wave)
+#ifndef ATTN_DECODE_VSWZ
+#define ATTN_DECODE_VSWZ 1  // coalesced V loads + XOR-swizzled V^T in LDS
+#endif
+#ifndef ATTN_DECODE_WAVES_PER_SIMD
+#define ATTN_DECODE_WAVES_PER_SIMD 2  // workgroups per CU the register budget is sized for
+#endif
+constexpr int kMaxSplits = 64;  // partials merged by one combine (the host keeps nsplit <= this)
+constexpr int kPartPad = 4;     // per-head partial: m, l, 2 pad, o[D] -> 16-byte aligned o
 
-template <int D>
-struct DecodeLds {
-  static constexpr int KLD = D + 8;
-  static constexpr int VLD = kDT + 8;
-  static constexpr int KSZ = kDT * KLD;
-  static constexpr int VSZ = D * VLD;
-  static constexpr int STAGE = KSZ + VSZ;
-};
+__device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
+  return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
+}
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
-  using L = DecodeLds<D>;
-  constexpr int KS = D / 32;                  // k-steps of the score MFMA
-  constexpr int NDT = D / 16;                 // 16-wide head-dim tiles of O
-  constexpr int KCH = kDT * D / 8 / 256;      // 16-byte K chunks per thread per tile
-  constexpr int VBLK = (kDT / 4) * (D / 8);   // 4x8 V blocks per tile
-  constexpr int VPT = VBLK / 256;             // V blocks per thread
+__global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel(const DecodeArgs a) {
+  constexpr int KS = D / 32;                 // k-steps of the score MFMA
+  constexpr int NDT = D / 16;                // 16-wide head-dim tiles of O
+#if ATTN_DECODE_VSWZ
+  constexpr int VLD = kDT;                   // V^T row pitch (elements); 16-byte groups XOR-swizzled
+#else
+  constexpr int VLD = kDT + 8;               // V^T row pitch in LDS (elements)
+#endif
+  constexpr int VBLK = (kDT / 4) * (D / 8);  // 4x8 V blocks per tile
+  constexpr int VPT = VBLK / 256;            // V blocks per thread
   static_assert(VBLK % 256 == 0, "V blocks divide evenly");
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  constexpr int RED_FLOATS = 128 + 4 * 16 * D;  // wave merge: m[4][16], l[4][16], o[4][16][D]
+  constexpr int LDS_BYTES = (RED_FLOATS * 4 > D * VLD * 2) ? RED_FLOATS * 4 : D * VLD * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];  // V^T stage, then the merges
+  uint16_t* const vt = reinterpret_cast<uint16_t*>(lds);
 
   const int split = blockIdx.x;
   const int hgi = blockIdx.y;
@@ -68,7 +85,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   const int k0 = split * a.rows_per_split;
   const int k1 = min(a.cache_len, k0 + a.rows_per_split);
-  const int ntiles = (k1 - k0 + kDT - 1) / kDT;
 
   // q heads as the B operand (columns beyond nh are zero)
   u32x4 qf[KS];
@@ -77,58 +93,43 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     const bool ok = col < nh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 x = ok ? load16(qp + 32 * ks + 8 * rg) : u32x4{0, 0, 0, 0};
+      const u32x4 x = ok ? load16(qp + 32 * ks + 8 * rg) : u32x4{0, 0, 0, 0};
       qf[ks] = x ^ a.qsign;
     }
   }
 
-  const uint16_t* kp = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
-  const uint16_t* vp = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
-
-  u32x4 kreg[KCH];
-  u32x4 vreg[VPT][4];
-  auto gload = [&](int t) {
-    const int kb = k0 + t * kDT;
+  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
+  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
+  // MFMA row i of key group gi reads key 8*(i/4) + 4*gi + i%4 of the wave's 32,
+  // so that lane (col, rg) holds keys 8*rg .. 8*rg+7 in its score registers.
+  const int krow = 32 * w + 8 * (col >> 2) + (col & 3);
+  const int32_t koff = krow * (int32_t)a.skn * 2 + 16 * rg;
+  // V blocks of 4 keys x 8 columns.  With the swizzled layout, 16 consecutive
+  // lanes cover one 256-byte row per load and V^T group g of row d sits at
+  // 16-byte slot g ^ vswz(d), which keeps both the transposing writes and the
+  // MFMA operand reads free of LDS bank conflicts without padding.
+  int32_t voff[VPT][4];
+  int vkvg[VPT], vdc[VPT];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id / (D / 8), c8 = id % (D / 8);
-      kreg[i] = (kb + row < k1) ? load16(kp + (int64_t)(kb + row) * a.skn + 8 * c8) : u32x4{0, 0, 0, 0};
-    }
+  for (int j = 0; j < VPT; ++j) {
+    const int id = tid + 256 * j;
+#if ATTN_DECODE_VSWZ
+    vdc[j] = id % (D / 8);
+    vkvg[j] = id / (D / 8);
+#else
+    vkvg[j] = id % (kDT / 4);
+    vdc[j] = id / (kDT / 4);
+#endif
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int id = tid + 256 * j;
-      const int kvg = id % (kDT / 4), dc = id / (kDT / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = kb + 4 * kvg + r;
-        vreg[j][r] = (row < k1) ? load16(vp + (int64_t)row * a.svn + 8 * dc) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-    uint16_t* Ks = smem + buf * L::STAGE;
-    uint16_t* Vs = Ks + L::KSZ;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id / (D / 8), c8 = id % (D / 8);
-      store16(Ks + row * L::KLD + 8 * c8, kreg[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int id = tid + 256 * j;
-      const int kvg = id % (kDT / 4), dc = id / (kDT / 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        const uint32_t x0 = (vreg[j][0][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x1 = (vreg[j][1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x2 = (vreg[j][2][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x3 = (vreg[j][3][e >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2*>(Vs + (8 * dc + e) * L::VLD + 4 * kvg) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
-      }
-    }
+    for (int r = 0; r < 4; ++r) voff[j][r] = (4 * vkvg[j] + r) * (int32_t)a.svn * 2 + 16 * vdc[j];
+  }
+  auto vt_at = [&](int d, int key) {  // element offset of V^T[d][key], key a multiple of 4
+#if ATTN_DECODE_VSWZ
+    const int sw = (d ^ (d >> 3)) & 15;
+    return d * VLD + 8 * ((key >> 3) ^ sw) + (key & 7);
+#else
+    return d * VLD + key;
+#endif
   };
 
   f32x4 oacc[NDT];
@@ -137,76 +138,99 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   float m = -INFINITY;  // running max of this lane's head column (log2 domain)
   float l = 0.f;        // this lane's share of the running sum
   const float c = a.c;
-  // MFMA row i of key group gi reads key 8*(i/4) + 4*gi + i%4 of the wave's 32,
-  // so that lane (col, rg) holds keys 8*rg .. 8*rg+7 in its score registers.
-  const int krow0 = 32 * w + 8 * (col >> 2) + (col & 3);
 
-  auto compute = [&](int t, int buf) {
-    const int kb = k0 + t * kDT + 32 * w;  // first key of this wave
-    if (kb >= k1) return;
-    const uint16_t* Ks = smem + buf * L::STAGE;
-    const uint16_t* Vs = Ks + L::KSZ;
+  // one tile's loads: K straight into MFMA operand registers, V into registers
+  // for the transposed LDS write; keys >= k1 read as zero
+  struct Tile {
+    u32x4 kf[2][KS];
+    u32x4 v[VPT][4];
+  };
+  auto load_tile = [&](Tile& T, int kb) {
+    const int64_t ko = (int64_t)kb * a.skn, vo = (int64_t)kb * a.svn;
+    const int64_t rows = k1 - kb;  // keys of this split from kb on
+    const auto rk = make_rsrc(kbase + ko, clamp_bytes(((rows - 1) * a.skn + D) * 2));
+    const auto rv = make_rsrc(vbase + vo, clamp_bytes(((rows - 1) * a.svn + D) * 2));
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) T.kf[gi][ks] = bload16(rk, koff + gi * 4 * (int32_t)a.skn * 2 + 64 * ks);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) T.v[j][r] = bload16(rv, voff[j][r]);
+  };
+  auto compute_tile = [&](const Tile& T, int kb, bool first) {
+    if (!first) __syncthreads();  // the previous tile's V^T reads are done
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 lo{halves<0x05040100u>(T.v[j][0][q], T.v[j][1][q]), halves<0x05040100u>(T.v[j][2][q], T.v[j][3][q])};
+        const u32x2 hi{halves<0x07060302u>(T.v[j][0][q], T.v[j][1][q]), halves<0x07060302u>(T.v[j][2][q], T.v[j][3][q])};
+        *reinterpret_cast<u32x2*>(vt + vt_at(8 * vdc[j] + 2 * q, 4 * vkvg[j])) = lo;
+        *reinterpret_cast<u32x2*>(vt + vt_at(8 * vdc[j] + 2 * q + 1, 4 * vkvg[j])) = hi;
+      }
+    }
+    __syncthreads();
+    const int kw0 = kb + 32 * w;  // first key of this wave
+    if (kw0 >= k1) return;
     f32x4 s0 = f32x4{}, s1 = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s0 = mfma_16x16x32<BF16>(load16(Ks + krow0 * L::KLD + 32 * ks + 8 * rg), qf[ks], s0);
-      s1 = mfma_16x16x32<BF16>(load16(Ks + (krow0 + 4) * L::KLD + 32 * ks + 8 * rg), qf[ks], s1);
+      s0 = mfma_16x16x32<BF16>(T.kf[0][ks], qf[ks], s0);
+      s1 = mfma_16x16x32<BF16>(T.kf[1][ks], qf[ks], s1);
     }
-    // lane (col, rg): s0[e] is key kb + 8*rg + e, s1[e] is key kb + 8*rg + 4 + e
-    float mx = -INFINITY;
-    const bool full = kb + 32 <= k1;
+    // lane (col, rg): s0[e] is key kw0 + 8*rg + e, s1[e] is key kw0 + 8*rg + 4 + e
+    if (kw0 + 32 > k1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!full) {
-        const int key = kb + 8 * rg + e;
-        s0[e] = (key < k1) ? s0[e] * c : -INFINITY;
-        s1[e] = (key + 4 < k1) ? s1[e] * c : -INFINITY;
-      } else {
-        s0[e] *= c;
-        s1[e] *= c;
+      for (int e = 0; e < 4; ++e) {
+        const int key = kw0 + 8 * rg + e;
+        s0[e] = (key < k1) ? s0[e] : -INFINITY;
+        s1[e] = (key + 4 < k1) ? s1[e] : -INFINITY;
       }
-      mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
     }
+    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
     float p[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      p[e] = fast_exp2(s0[e] - m_use);
-      p[4 + e] = fast_exp2(s1[e] - m_use);
+      p[e] = fast_exp2(__builtin_fmaf(s0[e], c, -m_use));
+      p[4 + e] = fast_exp2(__builtin_fmaf(s1[e], c, -m_use));
     }
-    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    l = l * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
     m = m_new;
     const u32x4 pf{pack2<BF16>(p[0], p[1]), pack2<BF16>(p[2], p[3]), pack2<BF16>(p[4], p[5]),
                    pack2<BF16>(p[6], p[7])};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       oacc[dt] *= alpha;
-      oacc[dt] = mfma_16x16x32<BF16>(load16(Vs + (16 * dt + col) * L::VLD + 32 * w + 8 * rg), pf, oacc[dt]);
+      oacc[dt] = mfma_16x16x32<BF16>(load16(vt + vt_at(16 * dt + col, 32 * w + 8 * rg)), pf, oacc[dt]);
     }
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    swrite(0);
+  // tiles of this split, the next tile's loads always issued before the
+  // current tile is consumed (two tiles in flight per workgroup)
+  Tile ta, tb;
+  load_tile(ta, k0);
+  for (int kb = k0; kb < k1; kb += 2 * kDT) {
+    const bool has_b = kb + kDT < k1;
+    if (has_b) load_tile(tb, kb + kDT);
+    compute_tile(ta, kb, kb == k0);
+    if (!has_b) break;
+    if (kb + 2 * kDT < k1) load_tile(ta, kb + 2 * kDT);
+    compute_tile(tb, kb + kDT, false);
   }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    compute(t, buf);
-    if (t + 1 < ntiles) swrite(buf ^ 1);
-    __syncthreads();
-  }
+  __syncthreads();  // V^T reads done: the LDS is reused for the merges below
 
   // ---- merge the 4 waves in LDS: per wave m[16], l[16], o[16][D] (fp32)
-  float* red = reinterpret_cast<float*>(smem);
-  float* rm = red;                 // [4][16]
-  float* rl = red + 64;            // [4][16]
-  float* ro = red + 128;           // [4][16][D]
+  float* red = reinterpret_cast<float*>(lds);
+  float* rm = red;       // [4][16]
+  float* rl = red + 64;  // [4][16]
+  float* ro = red + 128; // [4][16][D]
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   if (rg == 0) {
@@ -219,8 +243,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     for (int e = 0; e < 4; ++e) ro[(w * 16 + col) * D + 16 * dt + 4 * rg + e] = oacc[dt][e];
   __syncthreads();
 
-  // thread -> (head hn, 8-wide slice of the head dim)
-  constexpr int SL = D / 16;  // elements per thread
+  // thread -> (head hn, SL-wide slice of the head dim)
+  constexpr int SL = D / 16;
   const int hn = tid >> 4;
   const int d0 = (tid & 15) * SL;
   float M = -INFINITY;
@@ -239,88 +263,111 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     for (int j = 0; j < SL; ++j) acc[j] += sc * ro[(ww * 16 + hn) * D + d0 + j];
   }
 
-  auto store_out = [&](float Mx, float Lx, const float* o) {
-    if (hn >= nh) return;
-    const float inv = (Lx > 0.f) ? 1.f / Lx : 0.f;
-    uint16_t* op = a.o + (int64_t)b * a.sob + (int64_t)(h0 + hn) * a.soh + d0;
-    if constexpr (SL == 8) {
-      u32x4 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = pack2<BF16>(o[2 * j] * inv, o[2 * j + 1] * inv);
-      store16(op, v);
-    } else {
-      static_assert(SL == 4, "D is 64 or 128");
-      *reinterpret_cast<u32x2*>(op) = u32x2{pack2<BF16>(o[0] * inv, o[1] * inv), pack2<BF16>(o[2] * inv, o[3] * inv)};
-    }
-    if (a.lse != nullptr && (tid & 15) == 0)
-      a.lse[(int64_t)b * a.Hq + h0 + hn] = (Lx > 0.f) ? (Mx + __log2f(Lx)) * kLn2 : -INFINITY;
+  auto store_lse = [&](int head, float Mx, float Lx) {
+    if (a.lse != nullptr) a.lse[(int64_t)b * a.Hq + h0 + head] = (Lx > 0.f) ? (Mx + __log2f(Lx)) * kLn2 : -INFINITY;
   };
 
   if (a.nsplit == 1) {
-    store_out(M, Ls, acc);
+    if (hn < nh) {
+      const float inv = (Ls > 0.f) ? 1.f / Ls : 0.f;
+      uint16_t* op = a.o + (int64_t)b * a.sob + (int64_t)(h0 + hn) * a.soh + d0;
+      if constexpr (SL == 8) {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = pack2<BF16>(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+        store16(op, v);
+      } else {
+        static_assert(SL == 4, "D is 64 or 128");
+        *reinterpret_cast<u32x2*>(op) = u32x2{pack2<BF16>(acc[0] * inv, acc[1] * inv), pack2<BF16>(acc[2] * inv, acc[3] * inv)};
+      }
+      if ((tid & 15) == 0) store_lse(hn, M, Ls);
+    }
     return;
   }
 
-  // ---- several splits: publish this split's partial, the last arrival merges
-  const int64_t slot = ((int64_t)unit * a.hgroups + hgi);
-  const int64_t pstride = (int64_t)a.heads_per_wg * (D + 2);
-  float* mypart = a.part + (slot * a.nsplit + split) * pstride;
+  // ---- several splits: publish this split's partial (m, l, o[D]); a second
+  //      kernel merges them (the kernel boundary orders the two)
+  constexpr int HP = D + kPartPad;  // floats per head in a partial
   if (hn < nh) {
-    float* pr = mypart + (int64_t)hn * (D + 2);
-    if ((tid & 15) == 0) {
-      pr[0] = M;
-      pr[1] = Ls;
-    }
+    const int64_t slot = (int64_t)unit * a.hgroups + hgi;
+    float* pr = a.part + ((slot * a.max_splits + split) * a.heads_per_wg + hn) * HP;
+    if ((tid & 15) == 0) *reinterpret_cast<f32x4*>(pr) = f32x4{M, Ls, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < SL; ++j) pr[2 + d0 + j] = acc[j];
+    for (int j = 0; j < SL; j += 4)
+      *reinterpret_cast<f32x4*>(pr + kPartPad + d0 + j) = f32x4{acc[j], acc[j + 1], acc[j + 2], acc[j + 3]};
   }
-  __threadfence();
+}
+
+// Merge the split partials of one (batch, q head): o = sum_s e^(m_s - M) o_s /
+// sum_s e^(m_s - M) l_s and lse = M + ln(sum_s e^(m_s - M) l_s) (log2 domain
+// inside).  Thread -> (4-wide column of o, group of splits strided by G); all
+// of a thread's partial loads are issued before the (m, l) reduction.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a) {
+  constexpr int HP = D + kPartPad;
+  constexpr int C4 = D / 4;    // 4-wide columns
+  constexpr int G = 256 / C4;  // split groups
+  constexpr int PER = (kMaxSplits + G - 1) / G;  // splits per thread at most
+  __shared__ float sm[kMaxSplits], sw[kMaxSplits], sl[kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float sacc[G * D];
+  const int hx = blockIdx.x;  // head within the group
+  const int hgi = blockIdx.y;
+  const int unit = blockIdx.z;
+  const int nh = min(a.heads_per_wg, a.group - hgi * a.heads_per_wg);
+  if (hx >= nh) return;  // whole workgroup: uniform
+  const int b = unit / a.Hkv;
+  const int kvh = unit - b * a.Hkv;
+  const int h = kvh * a.group + hgi * a.heads_per_wg + hx;
+  const int ns = a.nsplit;
+  const int64_t slot = (int64_t)unit * a.hgroups + hgi;
+  const float* base = a.part + (slot * a.max_splits * a.heads_per_wg + hx) * HP;
+  const int64_t sstride = (int64_t)a.heads_per_wg * HP;  // between splits
+  const int tid = threadIdx.x;
+  const int dq = tid % C4, sg = tid / C4;
+  f32x4 ov[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = sg + i * G;
+    ov[i] = (s < ns) ? *reinterpret_cast<const f32x4*>(base + s * sstride + kPartPad + 4 * dq) : f32x4{};
+  }
+  if (tid < ns) {
+    const f32x4 ml = *reinterpret_cast<const f32x4*>(base + tid * sstride);
+    sm[tid] = ml[0];
+    sl[tid] = ml[1];
+  }
   __syncthreads();
-  __shared__ int s_last;
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.tickets + slot, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (uint32_t)(a.nsplit - 1));
-  }
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, sm[s]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  if (tid < ns) sw[tid] = fast_exp2(sm[tid] - Mu);
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (hn < nh) {
-    const float* base = a.part + slot * a.nsplit * pstride + (int64_t)hn * (D + 2);
-    float Mg = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) Mg = fmaxf(Mg, base[s * pstride]);
-    const float Mgu = (Mg == -INFINITY) ? 0.f : Mg;
-    float Lg = 0.f;
-    float og[SL];
+  f32x4 o4 = f32x4{};
 #pragma unroll
-    for (int j = 0; j < SL; ++j) og[j] = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float* pr = base + s * pstride;
-      const float sc = fast_exp2(pr[0] - Mgu);
-      Lg += sc * pr[1];
-#pragma unroll
-      for (int j = 0; j < SL; ++j) og[j] += sc * pr[2 + d0 + j];
-    }
-    store_out(Mg, Lg, og);
+  for (int i = 0; i < PER; ++i) {
+    const int s = sg + i * G;
+    if (s < ns) o4 += sw[s] * ov[i];
   }
-  if (tid == 0) __hip_atomic_store(a.tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  *reinterpret_cast<f32x4*>(sacc + 4 * (sg * C4 + dq)) = o4;
+  __syncthreads();
+  if (tid < C4) {
+    f32x4 t = f32x4{};
+#pragma unroll
+    for (int g = 0; g < G; ++g) t += *reinterpret_cast<const f32x4*>(sacc + 4 * (g * C4 + tid));
+    float L = 0.f;
+    for (int s = 0; s < ns; ++s) L += sw[s] * sl[s];
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    uint16_t* op = a.o + (int64_t)b * a.sob + (int64_t)h * a.soh + 4 * tid;
+    *reinterpret_cast<u32x2*>(op) = u32x2{pack2<BF16>(t[0] * inv, t[1] * inv), pack2<BF16>(t[2] * inv, t[3] * inv)};
+    if (tid == 0 && a.lse != nullptr) a.lse[(int64_t)b * a.Hq + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  }
 }
 
 template <int D, bool BF16>
 hipError_t launch_t(const DecodeArgs& a, int B, hipStream_t stream) {
-  using L = DecodeLds<D>;
-  const size_t lds = 2 * L::STAGE * sizeof(uint16_t);
-  // allow more than the default dynamic LDS (gfx950 has 160 KiB per CU); set once per device
-  static bool attr_set[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!attr_set[dev]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set[dev] = true;
-  }
-  dim3 grid(a.nsplit, a.hgroups, B * a.Hkv);
-  hipLaunchKernelGGL((decode_kernel<D, BF16>), grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, BF16>), dim3(a.nsplit, a.hgroups, B * a.Hkv), dim3(256), 0, stream, a);
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16>), dim3(a.heads_per_wg, a.hgroups, B * a.Hkv), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

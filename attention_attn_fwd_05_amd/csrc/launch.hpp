@@ -44,12 +44,12 @@ struct DecodeArgs {
   int Hq, Hkv, group, cache_len;
   int heads_per_wg;  // q heads handled by one workgroup (<= 16)
   int hgroups;       // head groups per kv head
-  int nsplit;        // chunks along the cache
+  int nsplit;          // chunks along the cache (<= max_splits)
+  int max_splits;      // partial slots per (unit, head group) in the workspace (<= 64)
   int rows_per_split;  // multiple of the 128-row tile
   float c;
   uint32_t qsign;
-  float* part;        // workspace: partial (m, l, o[D]) per (unit, head group, split, head)
-  uint32_t* tickets;  // workspace: one arrival counter per (unit, head group)
+  float* part;  // workspace: partial (m, l, pad, pad, o[D]) per (unit, head group, split, head)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool bf16, hipStream_t stream);

@@ -81,7 +81,9 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 /*
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode needs
  * for a cache of S_max slots (covers every cache_len <= S_max and every split
- * count the library may choose).  Returns 0 for invalid sizes.
+ * count): U * min(64, ceil(S_max/128)) * ceil(G/ceil(G/16)) * (D + 4) * 4
+ * bytes, with G = Hq / Hkv and U = B * Hkv * ceil(G/16) (batch, kv head, head
+ * group) slots.  Returns 0 for invalid sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D);
 
@@ -91,20 +93,20 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D);
  * kernel, cache_len is a runtime value, GQA indexing as in prefill, every
  * cached position visible).  The cache is split along its length into chunks
  * processed in parallel; each chunk's (max, sum, unnormalised output) partial
- * is merged with the same rescale identity the online softmax uses ([P1] step
- * 5f, [P2] "Online Softmax").
+ * is merged by a second kernel with the same rescale identity the online
+ * softmax uses ([P1] step 5f, [P2] "Online Softmax").
  *
  *   q        (B, Hq, D): element (b,h,d) at q[b*sq.b + h*sq.h + d]  (sq.n unused)
  *   k_cache, v_cache (B, Hkv, S_max, D) via skc, svc
  *   o        (B, Hq, D) via so (so.n unused);  lse nullable, contiguous fp32 (B, Hq)
  *   1 <= cache_len <= S_max.  Slots >= cache_len are never read.
- *   num_splits: 0 = library heuristic; k > 0 forces min(k, splits allowed by
- *               S_max) chunks (used to test split invariance).
- *   workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes,
- *              16-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Every call
- *              that completes leaves it valid for the next call (its counters
- *              return to zero).  One workspace must not be shared by calls that
- *              can run concurrently (different streams).
+ *   num_splits: 0 = library heuristic; k > 0 asks for k chunks (clamped to
+ *               [1, 64] and to the number of 128-slot tiles) -- used to test
+ *               that the result does not depend on the split.
+ *   workspace: device scratch of at least attn_decode_workspace_bytes(...)
+ *              bytes, 16-byte aligned, contents irrelevant (no initialisation
+ *              needed).  Calls that may run concurrently (different streams)
+ *              need distinct workspaces.
  */
 attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                         int B, int Hq, int Hkv, int S_max, int cache_len, int D,

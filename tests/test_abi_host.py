@@ -127,10 +127,12 @@ def test_cache_write_rejects(lib, kw, code):
 def test_workspace_bytes(lib):
     assert lib.attn_decode_workspace_bytes(0, 32, 8, 8192, 128) == 0
     assert lib.attn_decode_workspace_bytes(2, 30, 8, 8192, 128) == 0
-    # 16 (batch, kv head) slots x 64 max splits x 4 heads x (128 + 2) floats, after a 256-byte ticket block
-    assert lib.attn_decode_workspace_bytes(2, 32, 8, 8192, 128) == 256 + 16 * 64 * 4 * 130 * 4
-    # 32 q heads per kv head -> 2 groups of 16
-    assert lib.attn_decode_workspace_bytes(1, 32, 1, 128, 64) == 256 + 2 * 1 * 16 * 66 * 4
+    # 16 (batch, kv head) slots x 64 max splits x 4 heads x (128 + 4) floats
+    assert lib.attn_decode_workspace_bytes(2, 32, 8, 8192, 128) == 16 * 64 * 4 * 132 * 4
+    # 32 q heads per kv head -> 2 groups of 16; a 128-slot cache has one split
+    assert lib.attn_decode_workspace_bytes(1, 32, 1, 128, 64) == 2 * 1 * 16 * 68 * 4
+    # long caches still merge at most 64 splits
+    assert lib.attn_decode_workspace_bytes(10, 8, 8, 1 << 20, 128) == 80 * 64 * 1 * 132 * 4
 
 
 def test_binding_refuses_cpu_tensors():

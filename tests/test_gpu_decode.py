@@ -85,11 +85,12 @@ def test_decode_split_invariance():
 
 
 def test_workspace_reuse_many_calls():
-    """The arrival counters return to zero: repeated calls on one workspace stay correct."""
+    """One workspace serves many calls with different lengths; stale contents (here NaN
+    bit patterns everywhere) are never read before being written."""
     ws = A.decode_workspace(2, 32, 8, 8192, 128, DEV)
+    ws.fill_(0xFF)
     for L in (8192, 4096, 129, 8192, 1000, 8192):
         run_decode(W.decode_case(L, seed_offset=L % 7), ws=ws)
-    assert int(ws[:64].view(torch.int32).abs().sum().item()) == 0
 
 
 def test_kv_cache_write_bitwise():
