@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
         s1[e] = (key + 4 < k1) ? s1[e] : -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    float mx = vmax(vmax(vmax(s0[0], s0[1]), vmax(s0[2], s0[3])), vmax(vmax(s1[0], s1[1]), vmax(s1[2], s1[3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
     const float m_new = fmaxf(m, mx);

@@ -73,8 +73,14 @@ __device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 3
 
 // Buffer resource over [base, base + bytes): 16-byte loads at byte offsets
 // >= bytes return zeros (hardware range check), so ragged tails need no branch.
+// `base` and `bytes` must be wave-uniform; readfirstlane makes that explicit to
+// the compiler, which then keeps the descriptor in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* const pu = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -96,6 +102,10 @@ __device__ __forceinline__ float to_f32(uint32_t bits16) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// NaN-propagating maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no
+// quieting of its inputs, which matters in a row max over many scores.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

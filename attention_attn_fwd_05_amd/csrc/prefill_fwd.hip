@@ -43,6 +43,12 @@ namespace {
 constexpr int kBM = 128;             // query rows per workgroup
 constexpr int kBN = 64;              // key rows per LDS tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
+#ifndef ATTN_PF_SETPRIO
+#define ATTN_PF_SETPRIO 0  // raise wave priority around MFMA clusters
+#endif
+#ifndef ATTN_PF_BATCH
+#define ATTN_PF_BATCH 0  // read an operand batch from LDS before its MFMAs
+#endif
 
 template <int D>
 struct PrefillLds {
@@ -126,30 +132,33 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
   for (int r = 0; r < 4; ++r) voff[r] = (4 * v_kvg + r) * (int32_t)a.svn * 2 + 16 * v_dc;
   const int vw = 8 * v_dc * L::VLD + 4 * v_kvg;
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  auto gload = [&](int t) {
+  // one KV tile in flight from HBM/L2 to LDS
+  struct Staged {
+    u32x4 k[KCH];
+    u32x4 v[4];
+  };
+  auto gload = [&](Staged& r, int t) {
     const int64_t ko = (int64_t)t * kBN * a.skn;
     const auto rk = make_rsrc(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) kreg[i] = bload16(rk, koff[i]);
+    for (int i = 0; i < KCH; ++i) r.k[i] = bload16(rk, koff[i]);
     if (vthr) {
       const int64_t vo = (int64_t)t * kBN * a.svn;
       const auto rv = make_rsrc(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[r] = bload16(rv, voff[r]);
+      for (int q = 0; q < 4; ++q) r.v[q] = bload16(rv, voff[q]);
     }
   };
-  auto swrite = [&](uint16_t* Ks) {
+  auto swrite = [&](const Staged& r, uint16_t* Ks) {
     uint16_t* Vs = Ks + L::KSZ;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) store16(Ks + kw[i], kreg[i]);
+    for (int i = 0; i < KCH; ++i) store16(Ks + kw[i], r.k[i]);
     if (vthr) {
       // transpose the 4x8 block: V^T row d receives the 4 keys of this group
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x2 lo{halves<0x05040100u>(vreg[0][j], vreg[1][j]), halves<0x05040100u>(vreg[2][j], vreg[3][j])};
-        const u32x2 hi{halves<0x07060302u>(vreg[0][j], vreg[1][j]), halves<0x07060302u>(vreg[2][j], vreg[3][j])};
+        const u32x2 lo{halves<0x05040100u>(r.v[0][j], r.v[1][j]), halves<0x05040100u>(r.v[2][j], r.v[3][j])};
+        const u32x2 hi{halves<0x07060302u>(r.v[0][j], r.v[1][j]), halves<0x07060302u>(r.v[2][j], r.v[3][j])};
         *reinterpret_cast<u32x2*>(Vs + vw + (2 * j) * L::VLD) = lo;
         *reinterpret_cast<u32x2*>(Vs + vw + (2 * j + 1) * L::VLD) = hi;
       }
@@ -182,6 +191,25 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
     }
     // S^T = K Q^T for the two 32-key subtiles
     f32x16 s0 = f32x16{}, s1 = f32x16{};
+#if ATTN_PF_SETPRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
+#if ATTN_PF_BATCH
+    {
+      u32x4 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = load16(Ks + kr + 16 * ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(kf[ks], qf[ks], s0);
+    }
+    if (act1) {
+      u32x4 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = load16(Ks + 32 * L::KLD + kr + 16 * ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(kf[ks], qf[ks], s1);
+    }
+#else
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(load16(Ks + kr + 16 * ks), qf[ks], s0);
     if (act1) {
@@ -189,6 +217,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
       for (int ks = 0; ks < KS; ++ks)
         s1 = mfma_32x32x16<BF16>(load16(Ks + 32 * L::KLD + kr + 16 * ks), qf[ks], s1);
     }
+#endif
+#if ATTN_PF_SETPRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
     if constexpr (MASKED) {
       // mask before the row max: key index of register e is kb + 16*(e/8) + 8*hh + e%8
 #pragma unroll
@@ -203,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    for (int e = 0; e < 16; ++e) mx = vmax(mx, vmax(s0[e], s1[e]));
     mx = max_xor32(mx) * c;  // this row's max in the log2 domain
 
     // move the reference max only when some row's max outgrew it by > 2^8
@@ -234,43 +266,59 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
     l += rs0 + rs1;
 
     // O^T += V^T P^T : A = V^T rows from LDS, B = P^T from registers
+#if ATTN_PF_SETPRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 2 || act1) {
+#if ATTN_PF_BATCH
+        u32x4 vf[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vf[dt] = load16(Vs + 32 * dt * L::VLD + vr + 16 * kk);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_32x32x16<BF16>(vf[dt], pf[kk], oacc[dt]);
+#else
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
           oacc[dt] = mfma_32x32x16<BF16>(load16(Vs + 32 * dt * L::VLD + vr + 16 * kk), pf[kk], oacc[dt]);
+#endif
       }
     }
+#if ATTN_PF_SETPRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
   };
   using full_t = std::false_type;
   using mask_t = std::true_type;
   uint16_t* const S0 = smem;
   uint16_t* const S1 = smem + L::STAGE;
 
-  // ---- KV loop, double-buffered LDS.  Full tiles in pairs (stage 0, stage 1),
-  //      then the remaining tiles (diagonal / key tail) on the masked path.
+  // ---- KV loop, double-buffered LDS: the global loads of tile t+1 are issued
+  //      before tile t is computed.  Full tiles go in pairs (stage 0, stage 1);
+  //      the remaining tiles (diagonal / key tail) take the masked path.
+  Staged rs;
   if (ntiles > 0) {
-    gload(0);
-    swrite(S0);
+    gload(rs, 0);
+    swrite(rs, S0);
   }
   __syncthreads();
   int t = 0;
   for (; t + 1 < n_full; t += 2) {
-    gload(t + 1);
+    gload(rs, t + 1);
     compute(S0, t, full_t{});
-    swrite(S1);
+    swrite(rs, S1);
     __syncthreads();
-    if (t + 2 < ntiles) gload(t + 2);
+    if (t + 2 < ntiles) gload(rs, t + 2);
     compute(S1, t + 1, full_t{});
-    if (t + 2 < ntiles) swrite(S0);
+    if (t + 2 < ntiles) swrite(rs, S0);
     __syncthreads();
   }
   for (; t < ntiles; ++t) {
     const bool odd = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < ntiles) gload(rs, t + 1);
     compute(odd ? S1 : S0, t, mask_t{});
-    if (t + 1 < ntiles) swrite(odd ? S0 : S1);
+    if (t + 1 < ntiles) swrite(rs, odd ? S0 : S1);
     __syncthreads();
   }
 
