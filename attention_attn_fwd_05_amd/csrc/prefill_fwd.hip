@@ -9,17 +9,19 @@
 // gfx950 design (not the pages' Triton tiling):
 //   * one workgroup = 4 wave64s = 128 query rows of one q head; each wave owns
 //     32 rows for the whole KV loop.  Two workgroups share a CU.
-//   * KV tiles of 64 rows are staged in LDS, double buffered: K row-major, V
-//     transposed (head-dim major) so both MFMA operands are single 16-byte LDS
-//     reads.  Global loads for tile t+1 are issued before tile t is computed;
-//     they are buffer loads whose hardware range check returns zeros past the
-//     last key, so ragged tails need no branches.
+//   * KV tiles of 64 rows go from HBM/L2 straight into LDS with buffer-to-LDS
+//     loads (no register staging), double buffered, row-major with an XOR
+//     swizzle of 16-byte slots that keeps every access pattern free of bank
+//     conflicts.  The loads of tile t+1 are issued before tile t is computed;
+//     the buffer range check writes zeros past the last key, so ragged tails
+//     need no branches.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //     Q is the register-resident B operand and each lane ends up owning one
-//     query row's scores.  The K rows fed to the MFMA are permuted (bits 2 and
-//     3 of the row index swapped) so that the fp32 score registers of a lane
-//     are exactly the B operand layout of the P.V MFMA: no data movement
-//     between the two contractions.
+//     query row's scores.  The P.V MFMA takes V^T as its A operand, assembled
+//     by ds_read_b64_tr_b16 (the gfx950 transposing LDS read) from the
+//     row-major tile; its key order matches the fp32 score registers, which
+//     therefore are directly the B operand: no shuffles between the two
+//     contractions.
 //   * online softmax in the log2 domain: t = s * scale * log2(e); the row max
 //     needs one cross-lane exchange (lanes l and l+32 share a row); the row
 //     sum l is accumulated from the fp32 P, which then goes to 16 bits (round
@@ -43,35 +45,63 @@ namespace {
 constexpr int kBM = 128;             // query rows per workgroup
 constexpr int kBN = 64;              // key rows per LDS tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
-#ifndef ATTN_PF_SETPRIO
-#define ATTN_PF_SETPRIO 0  // raise wave priority around MFMA clusters
-#endif
-#ifndef ATTN_PF_BATCH
-#define ATTN_PF_BATCH 0  // read an operand batch from LDS before its MFMAs
+#ifndef ATTN_PF_KBATCH
+#define ATTN_PF_KBATCH 0  // read all K fragments of a tile before its score MFMAs
 #endif
 
 template <int D>
 struct PrefillLds {
-  static constexpr int KLD = D + 8;      // K row pitch in LDS (elements): 16 B pad, conflict-free reads
-  static constexpr int VLD = kBN + 8;    // V^T row pitch in LDS (elements)
-  static constexpr int KSZ = kBN * KLD;  // elements per K stage
-  static constexpr int VSZ = D * VLD;    // elements per V^T stage
-  static constexpr int STAGE = KSZ + VSZ;
+  static constexpr int C = D / 8;        // 16-byte slots per K/V row
+  static constexpr int TILE = kBN * D;   // elements of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE; // K tile then V tile
 };
+
+// XOR swizzle of the 16-byte slots of K/V row `row` in LDS (slot = chunk ^
+// swz(row)).  It keeps three access patterns free of LDS bank conflicts with no
+// padding: the DMA writes (1 KiB contiguous per wave), the K operand reads
+// (16 lanes = 16 rows, same chunk) and the transposed V reads (16 lanes = 4 rows
+// x 4 head-dim quads).  It depends only on row % 16, so every 16-row block of a
+// tile shares it.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
+  } else {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+  }
+}
 
 __device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
   return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 4 x 16-bit from LDS, transposed across each group of 16 lanes: lane i of a
+// group receives element i % 4 of the 8-byte pieces addressed by lanes
+// 4r + i/4 (r = 0..3) of its group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// one 16-byte global load per lane straight into LDS: lane l's data lands at
+// lds + 16 l bytes; loads at or past the resource's range write zeros
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
   using L = PrefillLds<D>;
-  constexpr int KS = D / 16;                 // k-steps of the score MFMA
-  constexpr int DT = D / 32;                 // 32-wide head-dim tiles of O
-  constexpr int KCH = kBN * D / 8 / 256;     // 16-byte K chunks per thread per tile
-  constexpr int VBLK = (kBN / 4) * (D / 8);  // 4-row x 8-col V blocks per tile
-  static_assert(VBLK <= 256, "one V block per thread at most");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+  constexpr int KS = D / 16;        // k-steps of the score MFMA
+  constexpr int DT = D / 32;        // 32-wide head-dim tiles of O
+  constexpr int NB = L::C / 4;      // 1 KiB DMA blocks per wave per K (or V) tile
+  constexpr int RPB = 64 / L::C;    // rows per 1 KiB block
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * L::STAGE];
 
   // ---- which (batch, q head, query block) this workgroup owns
   const int bid = blockIdx.x;
@@ -114,56 +144,48 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
   // diagonal and before the key tail
   const int n_full = CAUSAL ? min(q0, a.Nkv) / kBN : a.Nkv / kBN;
 
-  // ---- per-thread staging geometry (constant over the loop)
-  int32_t koff[KCH];
-  int kw[KCH];
+  // ---- DMA geometry: wave w fills 1 KiB blocks NB*w .. NB*w+NB-1 of each
+  //      K and V tile; lane l of block bk writes row RPB*bk + l/C, slot l%C,
+  //      i.e. global chunk (l%C) ^ swz(row) of that row
+  int32_t dk[NB], dv[NB];
 #pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int id = tid + 256 * i;
-    const int row = id / (D / 8), col = id % (D / 8);
-    koff[i] = row * (int32_t)a.skn * 2 + 16 * col;
-    kw[i] = row * L::KLD + 8 * col;
+  for (int i = 0; i < NB; ++i) {
+    const int bk = NB * w + i;
+    const int row = RPB * bk + lane / L::C;
+    const int chunk = (lane % L::C) ^ swz<D>(row);
+    dk[i] = row * (int32_t)a.skn * 2 + 16 * chunk;
+    dv[i] = row * (int32_t)a.svn * 2 + 16 * chunk;
   }
-  const bool vthr = tid < VBLK;
-  const int v_kvg = tid % (kBN / 4);  // 4-row group of this thread's V block
-  const int v_dc = tid / (kBN / 4);   // 8-column chunk of this thread's V block
-  int32_t voff[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = (4 * v_kvg + r) * (int32_t)a.svn * 2 + 16 * v_dc;
-  const int vw = 8 * v_dc * L::VLD + 4 * v_kvg;
-
-  // one KV tile in flight from HBM/L2 to LDS
-  struct Staged {
-    u32x4 k[KCH];
-    u32x4 v[4];
-  };
-  auto gload = [&](Staged& r, int t) {
-    const int64_t ko = (int64_t)t * kBN * a.skn;
+  auto dma_tile = [&](int t, uint16_t* stage) {
+    const int64_t ko = (int64_t)t * kBN * a.skn, vo = (int64_t)t * kBN * a.svn;
     const auto rk = make_rsrc(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
+    const auto rv = make_rsrc(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) r.k[i] = bload16(rk, koff[i]);
-    if (vthr) {
-      const int64_t vo = (int64_t)t * kBN * a.svn;
-      const auto rv = make_rsrc(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
+    for (int i = 0; i < NB; ++i) dma16(rk, stage + 512 * (NB * w + i), dk[i]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) r.v[q] = bload16(rv, voff[q]);
-    }
+    for (int i = 0; i < NB; ++i) dma16(rv, stage + L::TILE + 512 * (NB * w + i), dv[i]);
   };
-  auto swrite = [&](const Staged& r, uint16_t* Ks) {
-    uint16_t* Vs = Ks + L::KSZ;
+
+  // ---- LDS operand addresses (elements, relative to a 32-row subtile / 16-key chunk)
+  // K operand of S^T: lane (n, hh) reads row n, chunk 2*ks + hh
+  int ka[KS];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) store16(Ks + kw[i], r.k[i]);
-    if (vthr) {
-      // transpose the 4x8 block: V^T row d receives the 4 keys of this group
+  for (int ks = 0; ks < KS; ++ks) ka[ks] = n * D + (((2 * ks + hh) ^ swz<D>(n)) << 3);
+  // V^T operand of P.V via transposed reads: lane (group g = lane/16, i = lane%16)
+  // addresses row 8u + 4*(g/2) + i/4 of the 16-key chunk, head dims
+  // 32*dt + 16*(g%2) + 4*(i%4) .. +3; read u = 0 / 1 give MFMA k-slots 0-3 / 4-7
+  int va[DT][2];
+  {
+    const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 lo{halves<0x05040100u>(r.v[0][j], r.v[1][j]), halves<0x05040100u>(r.v[2][j], r.v[3][j])};
-        const u32x2 hi{halves<0x07060302u>(r.v[0][j], r.v[1][j]), halves<0x07060302u>(r.v[2][j], r.v[3][j])};
-        *reinterpret_cast<u32x2*>(Vs + vw + (2 * j) * L::VLD) = lo;
-        *reinterpret_cast<u32x2*>(Vs + vw + (2 * j + 1) * L::VLD) = hi;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 8 * u + 4 * (g >> 1) + (i >> 2);
+        const int d = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+        va[dt][u] = row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7));
       }
-    }
-  };
+  }
 
   // ---- online softmax state (fp32): reference max m (log2 domain), this
   //      lane's share of the running sum l, and the O^T accumulator
@@ -173,59 +195,54 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
   float m = -INFINITY;
   float l = 0.f;
   const float c = a.c;  // > 0
-  // K row fed to MFMA row n: swap bits 2 and 3 so that score register e of a
-  // lane holds key 16*(e/8) + 8*hh + e%8 of its 32-key subtile.
-  const int sig = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
-  const int kr = sig * L::KLD + 8 * hh;
-  const int vr = n * L::VLD + 8 * hh;
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
 
   auto compute = [&](const uint16_t* Ks, int t, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const uint16_t* Vs = Ks + L::KSZ;
+    const uint16_t* Vs = Ks + L::TILE;
     const int kb = t * kBN;
     bool act1 = true;
     if constexpr (MASKED) {
       if (kb >= a.Nkv || (CAUSAL && kb > wq_hi)) return;  // whole tile above this wave's rows
       act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi);
     }
-    // S^T = K Q^T for the two 32-key subtiles
+    // S^T = K Q^T for the two 32-key subtiles; score register e of lane
+    // (n, hh) is key 8*(e/4) + 4*hh + e%4 of its subtile
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-#if ATTN_PF_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
-#if ATTN_PF_BATCH
-    {
-      u32x4 kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = load16(Ks + kr + 16 * ks);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(kf[ks], qf[ks], s0);
-    }
+#if ATTN_PF_KBATCH
     if (act1) {
-      u32x4 kf[KS];
+      // all K fragments of both subtiles first, then the two MFMA chains interleaved
+      u32x4 kf0[KS], kf1[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = load16(Ks + 32 * L::KLD + kr + 16 * ks);
+      for (int ks = 0; ks < KS; ++ks) {
+        kf0[ks] = load16(Ks + ka[ks]);
+        kf1[ks] = load16(Ks + 32 * D + ka[ks]);
+      }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(kf[ks], qf[ks], s1);
+      for (int ks = 0; ks < KS; ++ks) {
+        s0 = mfma_32x32x16<BF16>(kf0[ks], qf[ks], s0);
+        s1 = mfma_32x32x16<BF16>(kf1[ks], qf[ks], s1);
+      }
+    } else {
+      u32x4 kf0[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf0[ks] = load16(Ks + ka[ks]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(kf0[ks], qf[ks], s0);
     }
 #else
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(load16(Ks + kr + 16 * ks), qf[ks], s0);
+    for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(load16(Ks + ka[ks]), qf[ks], s0);
     if (act1) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s1 = mfma_32x32x16<BF16>(load16(Ks + 32 * L::KLD + kr + 16 * ks), qf[ks], s1);
+      for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(load16(Ks + 32 * D + ka[ks]), qf[ks], s1);
     }
 #endif
-#if ATTN_PF_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
     if constexpr (MASKED) {
-      // mask before the row max: key index of register e is kb + 16*(e/8) + 8*hh + e%8
+      // mask before the row max
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int kv0 = kb + 16 * (e >> 3) + 8 * hh + (e & 7);
+        const int kv0 = kb + 8 * (e >> 2) + 4 * hh + (e & 3);
         const int kv1 = kv0 + 32;
         const bool vis0 = kv0 < a.Nkv && (!CAUSAL || kv0 <= qrow);
         const bool vis1 = act1 && kv1 < a.Nkv && (!CAUSAL || kv1 <= qrow);
@@ -249,7 +266,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
     }
     const float m_use = (m == -INFINITY) ? 0.f : m;  // rows with nothing visible yet get P = 0
 
-    // P = exp2(s*c - m) in fp32, its fp32 row sum, then the 16-bit B operand of P.V
+    // P = exp2(s*c - m) in fp32, its fp32 row sum, then the 16-bit B operand of
+    // P.V: pf[kk] holds keys 16*kk + 8u + 4*hh + t in k-slot 4u + t
     u32x4 pf[4];
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -265,60 +283,49 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
     }
     l += rs0 + rs1;
 
-    // O^T += V^T P^T : A = V^T rows from LDS, B = P^T from registers
-#if ATTN_PF_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
+    // O^T += V^T P^T : A = V^T from transposed LDS reads, B = P^T from registers
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 2 || act1) {
-#if ATTN_PF_BATCH
-        u32x4 vf[DT];
+        const uint16_t* vc = Vs + 16 * kk * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vf[dt] = load16(Vs + 32 * dt * L::VLD + vr + 16 * kk);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma_32x32x16<BF16>(vf[dt], pf[kk], oacc[dt]);
-#else
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          oacc[dt] = mfma_32x32x16<BF16>(load16(Vs + 32 * dt * L::VLD + vr + 16 * kk), pf[kk], oacc[dt]);
-#endif
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x2 lo = lds_read_tr16(vc + va[dt][0]);
+          const u32x2 hi = lds_read_tr16(vc + va[dt][1]);
+          oacc[dt] = mfma_32x32x16<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kk], oacc[dt]);
+        }
       }
     }
-#if ATTN_PF_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
   };
   using full_t = std::false_type;
   using mask_t = std::true_type;
   uint16_t* const S0 = smem;
   uint16_t* const S1 = smem + L::STAGE;
 
-  // ---- KV loop, double-buffered LDS: the global loads of tile t+1 are issued
-  //      before tile t is computed.  Full tiles go in pairs (stage 0, stage 1);
-  //      the remaining tiles (diagonal / key tail) take the masked path.
-  Staged rs;
-  if (ntiles > 0) {
-    gload(rs, 0);
-    swrite(rs, S0);
-  }
+  // ---- KV loop, double-buffered LDS filled by DMA: the loads of tile t+1 are
+  //      issued before tile t is computed; each wave waits for its own loads,
+  //      then the barrier publishes the stage to the workgroup.  Full tiles go
+  //      in pairs (stage 0, stage 1); the rest (diagonal / key tail) take the
+  //      masked path.
+  if (ntiles > 0) dma_tile(0, S0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int t = 0;
   for (; t + 1 < n_full; t += 2) {
-    gload(rs, t + 1);
+    dma_tile(t + 1, S1);
     compute(S0, t, full_t{});
-    swrite(rs, S1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 2 < ntiles) gload(rs, t + 2);
+    if (t + 2 < ntiles) dma_tile(t + 2, S0);
     compute(S1, t + 1, full_t{});
-    if (t + 2 < ntiles) swrite(rs, S0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (; t < ntiles; ++t) {
     const bool odd = t & 1;
-    if (t + 1 < ntiles) gload(rs, t + 1);
+    if (t + 1 < ntiles) dma_tile(t + 1, odd ? S0 : S1);
     compute(odd ? S1 : S0, t, mask_t{});
-    if (t + 1 < ntiles) swrite(rs, odd ? S0 : S1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
