@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kPrefillRows = 128;  // query rows per prefill workgroup
+constexpr int kPrefillRows = 256;  // query rows per prefill workgroup
 constexpr int kDecodeTile = 128;   // cache rows per decode tile
 constexpr int kDecodeMaxHeads = 16;
 constexpr int kDecodeMaxSplits = 64;     // partials one combine merges

@@ -7,12 +7,12 @@
 // head sharing as in the "Triton-FlashAttention" README (GQA phase).
 //
 // gfx950 design (not the pages' Triton tiling):
-//   * one workgroup = 4 wave64s = 128 query rows of one q head; each wave owns
-//     32 rows for the whole KV loop.  Two workgroups share a CU.
+//   * one workgroup = 8 wave64s = 256 query rows of one q head; each wave owns
+//     32 rows for the whole KV loop (two waves per SIMD).
 //   * KV tiles of 64 rows go from HBM/L2 straight into LDS with buffer-to-LDS
-//     loads (no register staging), double buffered, row-major with an XOR
-//     swizzle of 16-byte slots that keeps every access pattern free of bank
-//     conflicts.  The loads of tile t+1 are issued before tile t is computed;
+//     loads (no register staging), through a 3-stage ring, row-major with an
+//     XOR swizzle of 16-byte slots that keeps every access pattern free of bank
+//     conflicts.  The loads of tile t+2 are issued before tile t is computed;
 //     the buffer range check writes zeros past the last key, so ragged tails
 //     need no branches.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
@@ -42,18 +42,25 @@ namespace attn {
 
 namespace {
 
-constexpr int kBM = 128;             // query rows per workgroup
+constexpr int kWaves = 8;            // waves per workgroup (32 query rows each)
+constexpr int kBM = 32 * kWaves;     // query rows per workgroup
+constexpr int kStages = 3;           // LDS ring depth (tiles in flight + 1)
 constexpr int kBN = 64;              // key rows per LDS tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 #ifndef ATTN_PF_KBATCH
 #define ATTN_PF_KBATCH 0  // read all K fragments of a tile before its score MFMAs
 #endif
 
+// LDS ring: the V tiles of all stages first, then the K tiles, so that every
+// V^T read is its wave's base address plus an immediate below 64 KiB
 template <int D>
 struct PrefillLds {
   static constexpr int C = D / 8;        // 16-byte slots per K/V row
   static constexpr int TILE = kBN * D;   // elements of one K (or V) tile
-  static constexpr int STAGE = 2 * TILE; // K tile then V tile
+  static constexpr int V0 = 0;           // V tile of stage s at V0 + s * TILE
+  static constexpr int K0 = kStages * TILE;
+  static constexpr int ELEMS = 2 * kStages * TILE;
+  static_assert(2 * (kStages * TILE) <= 65536, "V^T read offsets fit the 16-bit DS offset");
 };
 
 // XOR swizzle of the 16-byte slots of K/V row `row` in LDS (slot = chunk ^
@@ -76,16 +83,41 @@ __device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
   return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 // 4 x 16-bit from LDS, transposed across each group of 16 lanes: lane i of a
 // group receives element i % 4 of the 8-byte pieces addressed by lanes
-// 4r + i/4 (r = 0..3) of its group.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
-  return __builtin_bit_cast(u32x2, v);
+// 4r + i/4 (r = 0..3) of its group.  Issued as inline assembly: the compiler
+// treats its builtin as possibly reading data still in flight from the
+// buffer-to-LDS loads and waits for all of them before it, which would
+// serialise the ring; here the ring's own waits and barriers order it.  The
+// result is only valid after lds_wait() ties it.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// waits for every outstanding LDS read and marks the given registers as
+// produced by that wait, so their consumers cannot move above it
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d, u32x2& e, u32x2& f,
+                                         u32x2& g, u32x2& h) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+
+// workgroup barrier without a memory fence: the compiler's fence would wait for
+// every buffer-to-LDS load in flight, including the ones for tiles not needed
+// yet.  The ring orders LDS itself: a tile's loads are waited for (vmcnt)
+// before the barrier that publishes it, and every wave has consumed all of its
+// LDS reads of a stage before the barrier after which that stage is refilled.
+// The clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
 }
 
 // one 16-byte global load per lane straight into LDS: lane l's data lands at
@@ -95,13 +127,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, i
 }
 
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdArgs a) {
   using L = PrefillLds<D>;
   constexpr int KS = D / 16;        // k-steps of the score MFMA
   constexpr int DT = D / 32;        // 32-wide head-dim tiles of O
-  constexpr int NB = L::C / 4;      // 1 KiB DMA blocks per wave per K (or V) tile
+  constexpr int NB = L::C / kWaves; // 1 KiB DMA blocks per wave per K (or V) tile
+  static_assert(NB >= 1, "every wave loads at least one block");
   constexpr int RPB = 64 / L::C;    // rows per 1 KiB block
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * L::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
 
   // ---- which (batch, q head, query block) this workgroup owns
   const int bid = blockIdx.x;
@@ -119,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = tid >> 6;  // wave 0..kWaves-1
   const int n = lane & 31;   // this lane's query column within the wave
   const int hh = lane >> 5;  // which half of the wave
   const int q0 = qb * kBM;
@@ -156,14 +189,14 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
     dk[i] = row * (int32_t)a.skn * 2 + 16 * chunk;
     dv[i] = row * (int32_t)a.svn * 2 + 16 * chunk;
   }
-  auto dma_tile = [&](int t, uint16_t* stage) {
+  auto dma_tile = [&](int t, int stage) {
     const int64_t ko = (int64_t)t * kBN * a.skn, vo = (int64_t)t * kBN * a.svn;
     const auto rk = make_rsrc(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
     const auto rv = make_rsrc(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rk, stage + 512 * (NB * w + i), dk[i]);
+    for (int i = 0; i < NB; ++i) dma16(rk, smem + L::K0 + stage * L::TILE + 512 * (NB * w + i), dk[i]);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rv, stage + L::TILE + 512 * (NB * w + i), dv[i]);
+    for (int i = 0; i < NB; ++i) dma16(rv, smem + L::V0 + stage * L::TILE + 512 * (NB * w + i), dv[i]);
   };
 
   // ---- LDS operand addresses (elements, relative to a 32-row subtile / 16-key chunk)
@@ -174,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
   // V^T operand of P.V via transposed reads: lane (group g = lane/16, i = lane%16)
   // addresses row 8u + 4*(g/2) + i/4 of the 16-key chunk, head dims
   // 32*dt + 16*(g%2) + 4*(i%4) .. +3; read u = 0 / 1 give MFMA k-slots 0-3 / 4-7
-  int va[DT][2];
+  uint32_t va[DT][2];  // LDS byte addresses within stage 0's V tile
   {
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
@@ -183,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
       for (int u = 0; u < 2; ++u) {
         const int row = 8 * u + 4 * (g >> 1) + (i >> 2);
         const int d = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
-        va[dt][u] = row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7));
+        va[dt][u] = lds_addr(smem + L::V0 + row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7)));
       }
   }
 
@@ -197,9 +230,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
   const float c = a.c;  // > 0
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
 
-  auto compute = [&](const uint16_t* Ks, int t, auto masked_tag) {
+  auto compute = [&](auto stage_tag, int t, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const uint16_t* Vs = Ks + L::TILE;
+    constexpr int STG = decltype(stage_tag)::value;
+    const uint16_t* Ks = smem + L::K0 + STG * L::TILE;
     const int kb = t * kBN;
     bool act1 = true;
     if constexpr (MASKED) {
@@ -284,49 +318,81 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
     l += rs0 + rs1;
 
     // O^T += V^T P^T : A = V^T from transposed LDS reads, B = P^T from registers
+    auto pv = [&](auto kk_tag) {
+      constexpr int kk = decltype(kk_tag)::value;
+      constexpr int off = 2 * (STG * L::TILE + 16 * kk * D);  // bytes past the V ring base
+      u32x2 lo[DT], hi[DT];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 2 || act1) {
-        const uint16_t* vc = Vs + 16 * kk * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const u32x2 lo = lds_read_tr16(vc + va[dt][0]);
-          const u32x2 hi = lds_read_tr16(vc + va[dt][1]);
-          oacc[dt] = mfma_32x32x16<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kk], oacc[dt]);
-        }
+      for (int dt = 0; dt < DT; ++dt) {
+        lo[dt] = lds_read_tr16<off>(va[dt][0]);
+        hi[dt] = lds_read_tr16<off>(va[dt][1]);
       }
+      if constexpr (DT == 4)
+        lds_wait(lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
+      else
+        lds_wait(lo[0], hi[0], lo[1], hi[1]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[dt] = mfma_32x32x16<BF16>(u32x4{lo[dt][0], lo[dt][1], hi[dt][0], hi[dt][1]}, pf[kk], oacc[dt]);
+    };
+    pv(std::integral_constant<int, 0>{});
+    pv(std::integral_constant<int, 1>{});
+    if (act1) {
+      pv(std::integral_constant<int, 2>{});
+      pv(std::integral_constant<int, 3>{});
     }
   };
   using full_t = std::false_type;
   using mask_t = std::true_type;
-  uint16_t* const S0 = smem;
-  uint16_t* const S1 = smem + L::STAGE;
+  using st0 = std::integral_constant<int, 0>;
+  using st1 = std::integral_constant<int, 1>;
+  using st2 = std::integral_constant<int, 2>;
+  static_assert(kStages == 3, "the loop below cycles three stages");
 
-  // ---- KV loop, double-buffered LDS filled by DMA: the loads of tile t+1 are
-  //      issued before tile t is computed; each wave waits for its own loads,
-  //      then the barrier publishes the stage to the workgroup.  Full tiles go
-  //      in pairs (stage 0, stage 1); the rest (diagonal / key tail) take the
-  //      masked path.
-  if (ntiles > 0) dma_tile(0, S0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // ---- KV loop over a 3-stage LDS ring filled by DMA: the loads of tile t+2
+  //      are issued before tile t is computed, so every tile's loads have two
+  //      tile computations to land.  After computing tile t a wave waits until
+  //      only its tile-(t+2) loads are outstanding (tile t+1 is in LDS), and
+  //      the barrier publishes it to the workgroup.  Full tiles go in triples
+  //      (stages 0, 1, 2); the rest (diagonal / key tail) take the masked path.
+  constexpr int NDMA = 2 * NB;  // DMA instructions per wave per tile
+  // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, expcnt and
+  // lgkmcnt left at their maxima, i.e. unconstrained)
+  constexpr int kWaitAllButTile = 0x0F70 | NDMA;
+  constexpr int kWaitAll = 0x0F70;
+  static_assert(NDMA < 16, "vmcnt field");
+  auto step = [&](int tt, auto stage_tag, auto masked_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
+    const bool pre = tt + 2 < ntiles;
+    if (pre) dma_tile(tt + 2, (STG + 2) % 3);
+    compute(stage_tag, tt, masked_tag);
+    if (pre)
+      __builtin_amdgcn_s_waitcnt(kWaitAllButTile);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    barrier_nofence();
+  };
+  if (ntiles > 0) dma_tile(0, 0);
+  if (ntiles > 1) dma_tile(1, 1);
+  if (ntiles > 1)
+    __builtin_amdgcn_s_waitcnt(kWaitAllButTile);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+  barrier_nofence();
   int t = 0;
-  for (; t + 1 < n_full; t += 2) {
-    dma_tile(t + 1, S1);
-    compute(S0, t, full_t{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 2 < ntiles) dma_tile(t + 2, S0);
-    compute(S1, t + 1, full_t{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  for (; t + 2 < n_full; t += 3) {
+    step(t, st0{}, full_t{});
+    step(t + 1, st1{}, full_t{});
+    step(t + 2, st2{}, full_t{});
   }
   for (; t < ntiles; ++t) {
-    const bool odd = t & 1;
-    if (t + 1 < ntiles) dma_tile(t + 1, odd ? S0 : S1);
-    compute(odd ? S1 : S0, t, mask_t{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    const int r = t % 3;
+    if (r == 0)
+      step(t, st0{}, mask_t{});
+    else if (r == 1)
+      step(t, st1{}, mask_t{});
+    else
+      step(t, st2{}, mask_t{});
   }
 
   // ---- epilogue: O = O^T / l, cast, store; lse = (m + log2 l) ln 2
@@ -351,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(const FwdArgs a) {
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(a.nblocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(a.nblocks), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

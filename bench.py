@@ -18,6 +18,11 @@ is reported as GB/s of algorithmic bytes (K and V rows read once + q in + o
 out); its caches rotate over enough copies (>= 512 MiB) that the 256 MiB
 Infinity Cache cannot hold them between uses.
 
+roofline.traffic / decode.traffic are the HBM bytes per launch that rocprofv3's
+FETCH_SIZE and WRITE_SIZE counters measured (scaled by a plain copy's reading),
+taken from the committed summaries under profiles/; null once the kernel
+sources differ from the ones those counters were taken with.
+
 Flags: --only prefill|decode|copy runs just that launch (for rocprofv3 runs),
 --no-cpu skips the oracle baseline.  Prints one JSON line.
 """
@@ -39,6 +44,34 @@ if ROOT not in sys.path:
 
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+CSRC = os.path.join(ROOT, "attention_attn_fwd_05_amd", "csrc")
+PREFILL_SOURCES = ["prefill_fwd.hip", "kernel_common.hpp", "launch.hpp", "attn_api.cpp"]
+DECODE_SOURCES = ["decode.hip", "kernel_common.hpp", "launch.hpp", "attn_api.cpp"]
+
+
+def measured_traffic(summary: str, sources: list[str]):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    The summary records the calibrated FETCH_SIZE + WRITE_SIZE bytes and the
+    sha256 of the kernel sources it was taken with; a kernel changed since then
+    has no measured traffic.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        key, sep, val = line.strip().partition(" = ")
+        if sep:
+            fields[key] = val
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -244,14 +277,16 @@ def main():
     if do_p:
         t = res["prefill"]["tflops"]
         out["roofline"] = {"bound": "mfma", "achieved": round(t, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(t / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                           "frac": round(t / MFMA_PEAK_TFLOPS, 4),
+                           "traffic": measured_traffic("prefill_fwd_n8192_d128_causal_fp16.md", PREFILL_SOURCES),
                            "kernel": "prefill_fwd_kernel<128, f16, causal>"}
     if do_d:
         g = res["decode"]["gbs"]
         out["decode"] = {"achieved": round(g, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "bound": "hbm",
                          "frac": round(g / HBM_PEAK_GBS, 4), "us_per_call": round(dec_ss * 1e3, 2),
                          "timing": "back-to-back calls over rotating caches (split kernel + combine kernel)",
-                         "kernel": "decode_kernel<128, f16> + decode_combine_kernel<128, f16>", "traffic": None}
+                         "kernel": "decode_kernel<128, f16> + decode_combine_kernel<128, f16>",
+                         "traffic": measured_traffic("decode_L8192_hkv8_d128_fp16.md", DECODE_SOURCES)}
     out["detail"] = res
     if do_p and args.only == "all" and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(pcase, args.cpu_seconds)
