@@ -64,18 +64,26 @@ struct PrefillLds {
 };
 
 // XOR swizzle of the 16-byte slots of K/V row `row` in LDS (slot = chunk ^
-// swz(row)).  It keeps three access patterns free of LDS bank conflicts with no
-// padding: the DMA writes (1 KiB contiguous per wave), the K operand reads
-// (16 lanes = 16 rows, same chunk) and the transposed V reads (16 lanes = 4 rows
-// x 4 head-dim quads).  It depends only on row % 16, so every 16-row block of a
-// tile shares it.
+// swz(row)).  With 256 bytes of banks served per LDS cycle it keeps three
+// access patterns free of bank conflicts with no padding:
+//   * the DMA writes: 1 KiB contiguous per wave;
+//   * the K operand reads (16 bytes a lane, 16 lanes a cycle): 16 rows at one
+//     chunk, so swz must take distinct values on any 16 rows sharing their
+//     256-byte bank phase;
+//   * the transposed V reads (8 bytes a lane, 32 lanes a cycle): 4 consecutive
+//     rows (from a multiple of 4) x 4 consecutive chunks (from a multiple of
+//     4), so the rows that share a bank phase must land in different groups of
+//     4 slots.
+// D = 128 (256-byte rows): bits 2-3 of swz are row % 4, bits 0-1 are row/4 % 4.
+// D = 64 (128-byte rows, two per bank phase; rows of one parity share it): with
+// x = row/2 % 8, bit 2 of swz is x % 2 and bits 0-1 are x/2 % 4.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (D == 128) {
-    return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
+    return ((row & 3) << 2) | ((row >> 2) & 3);
   } else {
     const int x = (row >> 1) & 7;
-    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+    return ((x & 1) << 2) | (x >> 1);
   }
 }
 
