@@ -47,8 +47,20 @@ constexpr int kBM = 32 * kWaves;     // query rows per workgroup
 constexpr int kStages = 3;           // LDS ring depth (tiles in flight + 1)
 constexpr int kBN = 64;              // key rows per LDS tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
-#ifndef ATTN_PF_KBATCH
-#define ATTN_PF_KBATCH 0  // read all K fragments of a tile before its score MFMAs
+#ifndef ATTN_PF_SCHED
+#define ATTN_PF_SCHED 1   // apply the instruction order hints below
+#endif
+#ifndef ATTN_PF_KLEAD
+#define ATTN_PF_KLEAD 4   // K fragment reads issued before the first score MFMA
+#endif
+#ifndef ATTN_PF_VLEAD
+#define ATTN_PF_VLEAD 2   // V^T fragments (2 reads each) issued before the first P.V MFMA
+#endif
+#ifndef ATTN_PF_VALU0
+#define ATTN_PF_VALU0 40  // softmax vector instructions before the first P.V MFMA
+#endif
+#ifndef ATTN_PF_VALU1
+#define ATTN_PF_VALU1 5   // softmax vector instructions after each P.V MFMA
 #endif
 
 // LDS ring: the V tiles of all stages first, then the K tiles, so that every
@@ -91,47 +103,65 @@ __device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
   return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
 }
 
-// 4 x 16-bit from LDS, transposed across each group of 16 lanes: lane i of a
-// group receives element i % 4 of the 8-byte pieces addressed by lanes
-// 4r + i/4 (r = 0..3) of its group.  Issued as inline assembly: the compiler
-// treats its builtin as possibly reading data still in flight from the
-// buffer-to-LDS loads and waits for all of them before it, which would
-// serialise the ring; here the ring's own waits and barriers order it.  The
-// result is only valid after lds_wait() ties it.
-template <int OFF>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// 4 x 16-bit from LDS byte address `addr`, transposed across each group of 16
+// lanes: lane i of a group receives element i % 4 of the 8-byte pieces
+// addressed by lanes 4r + i/4 (r = 0..3) of its group.
 __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "DS offset");
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+  return __builtin_bit_cast(u32x2, v);
 }
 
-// waits for every outstanding LDS read and marks the given registers as
-// produced by that wait, so their consumers cannot move above it
-__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d, u32x2& e, u32x2& f,
-                                         u32x2& g, u32x2& h) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
-}
-
-// workgroup barrier without a memory fence: the compiler's fence would wait for
-// every buffer-to-LDS load in flight, including the ones for tiles not needed
-// yet.  The ring orders LDS itself: a tile's loads are waited for (vmcnt)
-// before the barrier that publishes it, and every wave has consumed all of its
-// LDS reads of a stage before the barrier after which that stage is refilled.
-// The clobber keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+// 16 bytes from LDS byte address `addr`
+__device__ __forceinline__ u32x4 lds_load16(uint32_t addr) { return *(lds_u32x4*)addr; }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
 }
 
+// an LDS address the compiler may not see through: keeps a per-lane base
+// address whole in its register, so that only the (< 64 KiB) stage and
+// sub-tile offsets are folded into the instructions' immediate offsets (the
+// mask tells it the address is small and non-negative, which that folding
+// requires)
+__device__ __forceinline__ uint32_t opaque_lds(uint32_t x) {
+  asm("" : "+v"(x));
+  return x & 0x3ffff;
+}
+
+// buffer resource words (raw, unswizzled, range-checked against `bytes`) for
+// the inline-assembly loads below; every field is made wave-uniform
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return i32x4{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
+               (int)(__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffff),
+               (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes), 0x00020000};
+}
+
 // one 16-byte global load per lane straight into LDS: lane l's data lands at
-// lds + 16 l bytes; loads at or past the resource's range write zeros
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, int32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+// LDS byte address lds_base + 16 l (lds_base wave-uniform, passed in m0);
+// loads at or past the resource's range write zeros.  Issued as inline
+// assembly so that the compiler does not track it as a pending LDS write: its
+// tracking would put a wait for every such load in flight (including the ones
+// for tiles needed later) in front of the transposing LDS reads and of any
+// fenced barrier.  The ring's explicit vmcnt waits and barriers order it.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds_base, int32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds_base));
+}
+
+// workgroup barrier without a memory fence: a tile's loads are waited for
+// (vmcnt) before the barrier that publishes it, and every wave has consumed
+// all of its LDS reads of a stage before the barrier after which that stage
+// is refilled.  The clobber keeps the compiler from moving memory accesses
+// across it, the scheduling barriers every other instruction.
+__device__ __forceinline__ void barrier_nofence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, bool BF16, bool CAUSAL>
@@ -160,7 +190,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;  // wave 0..kWaves-1
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave 0..kWaves-1 (uniform)
   const int n = lane & 31;   // this lane's query column within the wave
   const int hh = lane >> 5;  // which half of the wave
   const int q0 = qb * kBM;
@@ -197,21 +227,24 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
     dk[i] = row * (int32_t)a.skn * 2 + 16 * chunk;
     dv[i] = row * (int32_t)a.svn * 2 + 16 * chunk;
   }
+  const uint32_t lds_k = lds_addr(smem + L::K0) + 1024 * NB * w;  // this wave's first block, stage 0
+  const uint32_t lds_v = lds_addr(smem + L::V0) + 1024 * NB * w;
   auto dma_tile = [&](int t, int stage) {
     const int64_t ko = (int64_t)t * kBN * a.skn, vo = (int64_t)t * kBN * a.svn;
-    const auto rk = make_rsrc(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
-    const auto rv = make_rsrc(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
+    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
+    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rk, smem + L::K0 + stage * L::TILE + 512 * (NB * w + i), dk[i]);
+    for (int i = 0; i < NB; ++i) dma16(rk, lds_k + 2 * stage * L::TILE + 1024 * i, dk[i]);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rv, smem + L::V0 + stage * L::TILE + 512 * (NB * w + i), dv[i]);
+    for (int i = 0; i < NB; ++i) dma16(rv, lds_v + 2 * stage * L::TILE + 1024 * i, dv[i]);
   };
 
   // ---- LDS operand addresses (elements, relative to a 32-row subtile / 16-key chunk)
   // K operand of S^T: lane (n, hh) reads row n, chunk 2*ks + hh
-  int ka[KS];
+  uint32_t ka[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) ka[ks] = n * D + (((2 * ks + hh) ^ swz<D>(n)) << 3);
+  for (int ks = 0; ks < KS; ++ks)
+    ka[ks] = opaque_lds(lds_addr(smem + L::K0) + 2 * (n * D + (((2 * ks + hh) ^ swz<D>(n)) << 3)));
   // V^T operand of P.V via transposed reads: lane (group g = lane/16, i = lane%16)
   // addresses row 8u + 4*(g/2) + i/4 of the 16-key chunk, head dims
   // 32*dt + 16*(g%2) + 4*(i%4) .. +3; read u = 0 / 1 give MFMA k-slots 0-3 / 4-7
@@ -224,7 +257,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
       for (int u = 0; u < 2; ++u) {
         const int row = 8 * u + 4 * (g >> 1) + (i >> 2);
         const int d = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
-        va[dt][u] = lds_addr(smem + L::V0 + row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7)));
+        va[dt][u] = opaque_lds(lds_addr(smem + L::V0) + 2 * (row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7))));
       }
   }
 
@@ -238,10 +271,35 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   const float c = a.c;  // > 0
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
 
+  // instruction order hints for the two MFMA phases of a tile (masks: 0x008
+  // MFMA, 0x100 LDS read, 0x002 VALU): LDS reads run several MFMAs ahead of
+  // their use, since a loaded LDS read takes some 250 cycles
+  auto schedule_scores = [&]() __attribute__((always_inline)) {
+#if ATTN_PF_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, ATTN_PF_KLEAD, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#endif
+  };
+  auto schedule_pv = [&]() __attribute__((always_inline)) {
+#if ATTN_PF_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * ATTN_PF_VLEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, ATTN_PF_VALU0, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, ATTN_PF_VALU1, 0);
+    }
+#endif
+  };
+
   auto compute = [&](auto stage_tag, int t, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int STG = decltype(stage_tag)::value;
-    const uint16_t* Ks = smem + L::K0 + STG * L::TILE;
     const int kb = t * kBN;
     bool act1 = true;
     if constexpr (MASKED) {
@@ -251,35 +309,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
     // S^T = K Q^T for the two 32-key subtiles; score register e of lane
     // (n, hh) is key 8*(e/4) + 4*hh + e%4 of its subtile
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-#if ATTN_PF_KBATCH
-    if (act1) {
-      // all K fragments of both subtiles first, then the two MFMA chains interleaved
-      u32x4 kf0[KS], kf1[KS];
+    {
+      constexpr uint32_t off0 = 2 * STG * L::TILE, off1 = off0 + 2 * 32 * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kf0[ks] = load16(Ks + ka[ks]);
-        kf1[ks] = load16(Ks + 32 * D + ka[ks]);
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off0), qf[ks], s0);
+      if (act1) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off1), qf[ks], s1);
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s0 = mfma_32x32x16<BF16>(kf0[ks], qf[ks], s0);
-        s1 = mfma_32x32x16<BF16>(kf1[ks], qf[ks], s1);
-      }
-    } else {
-      u32x4 kf0[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf0[ks] = load16(Ks + ka[ks]);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(kf0[ks], qf[ks], s0);
+      schedule_scores();
     }
-#else
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(load16(Ks + ka[ks]), qf[ks], s0);
-    if (act1) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(load16(Ks + 32 * D + ka[ks]), qf[ks], s1);
-    }
-#endif
     if constexpr (MASKED) {
       // mask before the row max
 #pragma unroll
@@ -326,29 +365,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
     l += rs0 + rs1;
 
     // O^T += V^T P^T : A = V^T from transposed LDS reads, B = P^T from registers
-    auto pv = [&](auto kk_tag) {
-      constexpr int kk = decltype(kk_tag)::value;
-      constexpr int off = 2 * (STG * L::TILE + 16 * kk * D);  // bytes past the V ring base
-      u32x2 lo[DT], hi[DT];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        lo[dt] = lds_read_tr16<off>(va[dt][0]);
-        hi[dt] = lds_read_tr16<off>(va[dt][1]);
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 2 || act1) {
+        constexpr uint32_t base = 2 * STG * L::TILE;
+        const uint32_t off = base + 2 * 16 * kk * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x2 lo = lds_read_tr16(va[dt][0] + off);
+          const u32x2 hi = lds_read_tr16(va[dt][1] + off);
+          oacc[dt] = mfma_32x32x16<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kk], oacc[dt]);
+        }
       }
-      if constexpr (DT == 4)
-        lds_wait(lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
-      else
-        lds_wait(lo[0], hi[0], lo[1], hi[1]);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        oacc[dt] = mfma_32x32x16<BF16>(u32x4{lo[dt][0], lo[dt][1], hi[dt][0], hi[dt][1]}, pf[kk], oacc[dt]);
-    };
-    pv(std::integral_constant<int, 0>{});
-    pv(std::integral_constant<int, 1>{});
-    if (act1) {
-      pv(std::integral_constant<int, 2>{});
-      pv(std::integral_constant<int, 3>{});
     }
+    schedule_pv();
   };
   using full_t = std::false_type;
   using mask_t = std::true_type;
