@@ -86,16 +86,15 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   const int k0 = split * a.rows_per_split;
   const int k1 = min(a.cache_len, k0 + a.rows_per_split);
 
-  // q heads as the B operand (columns beyond nh are zero)
+  // q heads as the B operand.  Columns beyond nh repeat the group's last head:
+  // MFMA columns never mix, and those columns' results are never stored.  (A
+  // load predicated on col < nh makes the compiler wait for it before issuing
+  // anything else, costing every workgroup one memory latency.)
   u32x4 qf[KS];
   {
-    const uint16_t* qp = a.q + (int64_t)b * a.sqb + (int64_t)(h0 + col) * a.sqh;
-    const bool ok = col < nh;
+    const uint16_t* qp = a.q + (int64_t)b * a.sqb + (int64_t)(h0 + min(col, nh - 1)) * a.sqh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 x = ok ? load16(qp + 32 * ks + 8 * rg) : u32x4{0, 0, 0, 0};
-      qf[ks] = x ^ a.qsign;
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = load16(qp + 32 * ks + 8 * rg) ^ a.qsign;
   }
 
   const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
