@@ -20,7 +20,7 @@ definition, written out in float64 with numpy (BLAS matmul as the only library
 step), in the obvious two-pass form:
 
     S[i, j]  = scale * sum_d Q[b, h, i, d] * K[b, kvh, j, d]
-    vis(i,j) = (j < N_kv) and (not causal or j <= i)          top-left causal
+    vis(i,j) = (j < N_kv) and (not causal or j <= i + off)    causal, off = 0 top-left
     m_i      = max over visible j of S[i, j]
     P[i, j]  = exp(S[i, j] - m_i) / sum over visible j' of exp(S[i, j'] - m_i)
     O[b,h,i] = sum_j P[i, j] * V[b, kvh, j, :]
@@ -30,12 +30,17 @@ step), in the obvious two-pass form:
 Readings taken where the pages leave a step open (each also listed in the design doc):
 
 * Causal mask is top-left aligned, kv position <= q position ([P1] step 5c; [P2]
-  "Common Pitfalls": the comparison is >=, not >).
+  "Common Pitfalls": the comparison is >=, not >).  The widening to
+  N_q < N_kv (chunked prefill, multi-token verify against a cache) aligns the
+  mask bottom-right: query i is the token at sequence position i + off with
+  off = N_kv - N_q, so it sees keys j <= i + off.  The pages fix only the
+  top-left form; off = 0 reproduces it exactly.
 * ``scale`` multiplies the fp32 dot product; the oracle widens the exact float32
   scale to float64 ([P1] "Inputs" item 4 and "Kernel design rules").
 * lse uses the natural log of the sum of exp of *scaled* scores ([P1] step 8).
-* A row with no visible key (unreachable with N_kv >= 1 and top-left causal)
-  gets O = 0 and lse = -inf by convention.
+* A row with no visible key (unreachable with N_kv >= 1 and top-left causal;
+  the first N_q - N_kv rows of a bottom-right mask with N_q > N_kv) gets O = 0
+  and lse = -inf by convention.
 * Decode is one query per (batch, head) over the first ``cache_len`` cache
   slots, every slot visible, no causal loop ([P3] decode phase).
 * GQA maps q head h to kv head h // group, i.e. repeat_interleave expansion of
@@ -74,16 +79,17 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def visibility(q_pos: np.ndarray, Nkv: int, causal: bool) -> np.ndarray:
+def visibility(q_pos: np.ndarray, Nkv: int, causal: bool, offset: int = 0) -> np.ndarray:
     """Boolean (len(q_pos), Nkv): may query at position i attend to key j?
 
     Keys exist only for j < Nkv ([P1] "Correctness requirements", KV boundary
-    bullet); with ``causal`` a key is visible when j <= i ([P1] step 5c).
+    bullet); with ``causal`` a key is visible when j <= i + offset ([P1] step
+    5c has offset 0; the bottom-right alignment uses offset = Nkv - Nq).
     """
     j = np.arange(Nkv)
     vis = np.ones((q_pos.shape[0], Nkv), dtype=bool)
     if causal:
-        vis &= j[None, :] <= q_pos[:, None]
+        vis &= j[None, :] <= q_pos[:, None] + offset
     return vis
 
 
@@ -110,14 +116,14 @@ def _masked_softmax(S: np.ndarray, vis: np.ndarray):
     return P, lse
 
 
-def attention_probs(q, k, scale: float, causal: bool) -> np.ndarray:
+def attention_probs(q, k, scale: float, causal: bool, causal_offset: int = 0) -> np.ndarray:
     """Full softmax matrix P (B, Hq, Nq, Nkv) for small shapes (pin P1 uses it)."""
     q = _f64(q)
     k = _f64(k)
     B, Hq, Nq, _ = q.shape
     Hkv, Nkv = k.shape[1], k.shape[2]
     out = np.zeros((B, Hq, Nq, Nkv))
-    vis = visibility(np.arange(Nq), Nkv, causal)
+    vis = visibility(np.arange(Nq), Nkv, causal, causal_offset)
     for b in range(B):
         for h in range(Hq):
             kvh = kv_head_of(h, Hq, Hkv)
@@ -125,10 +131,12 @@ def attention_probs(q, k, scale: float, causal: bool) -> np.ndarray:
     return out
 
 
-def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int = 512):
+def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int = 512, causal_offset: int = 0):
     """O1: prefill attention by the plain definition.
 
     q: (B, Hq, Nq, D); k, v: (B, Hkv, Nkv, D), any float dtype (widened exactly).
+    causal_offset: query i sees keys j <= i + causal_offset when causal (0 is the
+    pages' top-left mask; Nkv - Nq aligns it bottom-right).
     rows: optional 1-D array of query positions to evaluate (sampling at large
     sizes); default all Nq positions.  Evaluated in row chunks so that the score
     block stays small; chunking does not change any value.
@@ -154,7 +162,7 @@ def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int
             for r0 in range(0, R, chunk):
                 sel = rows[r0:r0 + chunk]
                 S = _scores(q[b, h, sel], kb, scale)
-                P, ls = _masked_softmax(S, visibility(sel, Nkv, causal))
+                P, ls = _masked_softmax(S, visibility(sel, Nkv, causal, causal_offset))
                 O[b, h, r0:r0 + chunk] = P @ vb
                 lse[b, h, r0:r0 + chunk] = ls
     return O, lse

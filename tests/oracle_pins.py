@@ -161,8 +161,10 @@ def pin_gqa_equals_expanded_mha():
             np.testing.assert_array_equal(lse, lsee)
 
 
-def _brute(q, k, v, scale, causal):
-    """Independent evaluation: explicit loops, exp without max subtraction at 40 digits."""
+def _brute(q, k, v, scale, causal, offset=0):
+    """Independent evaluation: explicit loops, exp without max subtraction at 40 digits.
+
+    A row with no visible key gets O = 0 and lse = -inf (the convention)."""
     mpmath.mp.dps = 40
     B, Hq, Nq, D = q.shape
     Hkv, Nkv = k.shape[1], k.shape[2]
@@ -173,7 +175,10 @@ def _brute(q, k, v, scale, causal):
         for h in range(Hq):
             kvh = (h * Hkv) // Hq
             for i in range(Nq):
-                keys = [j for j in range(Nkv) if (not causal) or j <= i]
+                keys = [j for j in range(Nkv) if (not causal) or j <= i + offset]
+                if not keys:
+                    lse[b, h, i] = -np.inf
+                    continue
                 w = []
                 for j in keys:
                     dot = mpmath.mpf(math.fsum(float(q[b, h, i, d]) * float(k[b, kvh, j, d]) for d in range(D)))
@@ -198,6 +203,35 @@ def pin_brute_force_tiny():
             Ob, lseb = _brute(q, k, v, 0.7, causal)
             np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
             np.testing.assert_allclose(lse, lseb, rtol=1e-12, atol=1e-12)
+
+
+def pin_brute_force_bottom_right():
+    """P6b: bottom-right causal (offset Nkv - Nq) against the brute force, for
+    Nq < Nkv, Nq == Nkv and Nq > Nkv (whose first Nq - Nkv rows see no key)."""
+    rng = np.random.default_rng(61)
+    shapes = [(1, 2, 1, 3, 8, 4), (1, 4, 2, 5, 5, 3), (2, 2, 2, 7, 4, 3), (1, 1, 1, 1, 6, 2)]
+    for (B, Hq, Hkv, Nq, Nkv, D) in shapes:
+        q, k, v = _rand(rng, B, Hq, Nq, D), _rand(rng, B, Hkv, Nkv, D), _rand(rng, B, Hkv, Nkv, D)
+        off = Nkv - Nq
+        O, lse = OA.attention_forward(q, k, v, 0.6, True, causal_offset=off)
+        Ob, lseb = _brute(q, k, v, 0.6, True, offset=off)
+        np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lseb, rtol=1e-12, atol=1e-12)
+        if Nq > Nkv:
+            assert np.all(O[:, :, :Nq - Nkv] == 0.0) and np.all(lse[:, :, :Nq - Nkv] == -np.inf)
+
+
+def pin_bottom_right_is_the_tail_of_full_causal():
+    """P6c: chunked prefill -- the last Nq rows of a top-left causal attention over
+    N tokens equal a bottom-right causal attention of those Nq queries against all N keys."""
+    rng = np.random.default_rng(62)
+    B, Hq, Hkv, N, D = 2, 4, 2, 17, 6
+    q, k, v = _rand(rng, B, Hq, N, D), _rand(rng, B, Hkv, N, D), _rand(rng, B, Hkv, N, D)
+    O, lse = OA.attention_forward(q, k, v, 0.5, True)
+    for Nq in (1, 5, 16):
+        Ot, lset = OA.attention_forward(q[:, :, N - Nq:], k, v, 0.5, True, causal_offset=N - Nq)
+        np.testing.assert_allclose(Ot, O[:, :, N - Nq:], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lset, lse[:, :, N - Nq:], rtol=0, atol=1e-13)
 
 
 def pin_shift_invariance():
@@ -282,6 +316,8 @@ ALL_PINS = [
     pin_single_key,
     pin_gqa_equals_expanded_mha,
     pin_brute_force_tiny,
+    pin_brute_force_bottom_right,
+    pin_bottom_right_is_the_tail_of_full_causal,
     pin_shift_invariance,
     pin_permutation_invariance,
     pin_linear_in_v,

@@ -20,20 +20,28 @@ _orig_decode = OA.decode
 _orig_write = OA.kv_cache_write
 
 
-def _vis_strict(q_pos, Nkv, causal):
+def _vis_strict(q_pos, Nkv, causal, offset=0):
     j = np.arange(Nkv)
     vis = np.ones((q_pos.shape[0], Nkv), dtype=bool)
     if causal:
-        vis &= j[None, :] < q_pos[:, None]
+        vis &= j[None, :] < q_pos[:, None] + offset
     return vis
 
 
-def _vis_no_causal(q_pos, Nkv, causal):
+def _vis_no_causal(q_pos, Nkv, causal, offset=0):
     return _orig_vis(q_pos, Nkv, False)
 
 
-def _vis_off_by_one(q_pos, Nkv, causal):
-    return _orig_vis(q_pos + 1, Nkv, causal)
+def _vis_off_by_one(q_pos, Nkv, causal, offset=0):
+    return _orig_vis(q_pos + 1, Nkv, causal, offset)
+
+
+def _vis_offset_ignored(q_pos, Nkv, causal, offset=0):
+    return _orig_vis(q_pos, Nkv, causal, 0)
+
+
+def _vis_offset_sign(q_pos, Nkv, causal, offset=0):
+    return _orig_vis(q_pos, Nkv, causal, -offset)
 
 
 def _kv_head_tiled(h, Hq, Hkv):
@@ -92,6 +100,8 @@ MUTATIONS = {
     "causal_strict_lt": ("visibility", _vis_strict),
     "causal_ignored": ("visibility", _vis_no_causal),
     "causal_off_by_one": ("visibility", _vis_off_by_one),
+    "causal_offset_ignored": ("visibility", _vis_offset_ignored),
+    "causal_offset_sign": ("visibility", _vis_offset_sign),
     "gqa_tiled_heads": ("kv_head_of", _kv_head_tiled),
     "scale_dropped": ("_scores", _scores_unscaled),
     "scale_twice": ("_scores", _scores_scaled_twice),
