@@ -102,12 +102,20 @@ def _default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
+_CAUSAL_ALIGN = {"top_left": 1, "bottom_right": 2}
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool, scale: float | None = None,
-             return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+             return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+             causal_align: str = "top_left"):
     """Fused attention forward.  q (B,Hq,Nq,D), k/v (B,Hkv,Nkv,D), any strides with stride(-1) == 1.
 
+    ``causal_align`` (when ``causal``): "top_left" -- query i sees keys j <= i;
+    "bottom_right" -- j <= i + Nkv - Nq (the queries are the last Nq positions).
     Returns ``out`` (B,Hq,Nq,D), or ``(out, lse)`` with lse fp32 (B,Hq,Nq) when ``return_lse``.
     """
+    if causal_align not in _CAUSAL_ALIGN:
+        raise ValueError("causal_align must be 'top_left' or 'bottom_right'")
     lib = load_library()
     B, Hq, Nq, D = q.shape
     Hkv, Nkv = k.shape[1], k.shape[2]
@@ -125,7 +133,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool,
     st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       lse.data_ptr() if lse is not None else None,
                       B, Hq, Hkv, Nq, Nkv, D, _strides4(q), _strides4(k), _strides4(v), _strides4(out),
-                      s, 1 if causal else 0, code, _stream(q))
+                      s, _CAUSAL_ALIGN[causal_align] if causal else 0, code, _stream(q))
     _check(st, "attn_fwd")
     return (out, lse) if return_lse else out
 

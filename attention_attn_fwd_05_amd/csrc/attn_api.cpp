@@ -91,6 +91,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (causal < ATTN_CAUSAL_NONE || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_ERR_UNSUPPORTED;
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
@@ -120,6 +121,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   const int64_t per_unit = (int64_t)a.group * nqb;
   a.remap = (nblocks % 8 == 0) && per_xcd > 0 &&
             ((per_xcd % per_unit == 0) || (!causal && per_unit % per_xcd == 0));
+  a.causal_off = (causal == ATTN_CAUSAL_BOTTOM_RIGHT) ? Nkv - Nq : 0;
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
   a.q_bytes = slice_bytes(Nq, sq.n, D);

@@ -19,9 +19,10 @@ struct FwdArgs {
   int64_t svb, svh, svn;
   int64_t sob, soh, son;
   int Hq, Hkv, Nq, Nkv, group;
-  int nqb;      // number of 128-row query blocks
+  int nqb;      // number of query blocks (rows per workgroup: see the kernel)
   int nblocks;  // grid size
   int remap;    // 1: XCD-aware block remap is valid for this grid
+  int causal_off;  // causal: query i sees keys j <= i + causal_off
   float c;      // |scale| * log2(e), or a tiny positive value when scale == 0
   uint32_t qsign;  // 0x80008000 when scale < 0: flip Q's sign bits (exact)
   // bytes from a (batch, head) slice's first element to the end of its last

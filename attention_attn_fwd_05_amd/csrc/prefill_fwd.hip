@@ -33,6 +33,9 @@
 //   * causal: the KV loop stops at the block's diagonal; tiles below every
 //     row's diagonal take a path with no per-element compare, and on the last
 //     tiles each wave skips 32-key subtiles that lie wholly above its rows.
+//     The diagonal may be shifted (query i sees keys j <= i + off): off = 0 is
+//     the pages' top-left mask, off = Nkv - Nq aligns it bottom-right (a chunk
+//     of queries at the end of a longer sequence, as in chunked prefill).
 #include <type_traits>
 
 #include "kernel_common.hpp"
@@ -209,11 +212,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
 
   const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
   const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
-  const int kv_end = CAUSAL ? min(a.Nkv, q0 + kBM) : a.Nkv;
+  // causal: query row i sees keys j <= i + off (off = 0 top-left, Nkv - Nq
+  // bottom-right); keys past the block's last row + off are never visited
+  const int off = CAUSAL ? a.causal_off : 0;
+  const int kv_end = CAUSAL ? max(0, min(a.Nkv, q0 + kBM + off)) : a.Nkv;
   const int ntiles = (kv_end + kBN - 1) / kBN;
   // tiles every row of this block sees in full (no mask): below the block's
   // diagonal and before the key tail
-  const int n_full = CAUSAL ? min(q0, a.Nkv) / kBN : a.Nkv / kBN;
+  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, a.Nkv)) / kBN : a.Nkv / kBN;
 
   // ---- DMA geometry: wave w fills 1 KiB blocks NB*w .. NB*w+NB-1 of each
   //      K and V tile; lane l of block bk writes row RPB*bk + l/C, slot l%C,
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   float m = -INFINITY;
   float l = 0.f;
   const float c = a.c;  // > 0
-  const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  const int wq_hi = q0 + 32 * w + 31 + off;  // last key any of this wave's rows sees
 
   // instruction order hints for the two MFMA phases of a tile (masks: 0x008
   // MFMA, 0x100 LDS read, 0x002 VALU): LDS reads run several MFMAs ahead of
@@ -325,8 +331,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
       for (int e = 0; e < 16; ++e) {
         const int kv0 = kb + 8 * (e >> 2) + 4 * hh + (e & 3);
         const int kv1 = kv0 + 32;
-        const bool vis0 = kv0 < a.Nkv && (!CAUSAL || kv0 <= qrow);
-        const bool vis1 = act1 && kv1 < a.Nkv && (!CAUSAL || kv1 <= qrow);
+        const bool vis0 = kv0 < a.Nkv && (!CAUSAL || kv0 <= qrow + off);
+        const bool vis1 = act1 && kv1 < a.Nkv && (!CAUSAL || kv1 <= qrow + off);
         s0[e] = vis0 ? s0[e] : -INFINITY;
         s1[e] = vis1 ? s1[e] : -INFINITY;
       }

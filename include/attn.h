@@ -51,6 +51,15 @@ typedef struct {
   int64_t b, h, n, d;
 } attn_strides;
 
+/* causal argument of attn_fwd */
+enum {
+  ATTN_CAUSAL_NONE = 0,         /* every key j < Nkv is visible */
+  ATTN_CAUSAL_TOP_LEFT = 1,     /* j <= i: the pages' mask ([P1] step 5c) */
+  ATTN_CAUSAL_BOTTOM_RIGHT = 2  /* j <= i + (Nkv - Nq): the Nq queries are the last
+                                   Nq positions of the Nkv-token sequence (chunked
+                                   prefill, multi-token verification) */
+};
+
 /*
  * attn_fwd -- O = softmax(scale * Q K^T + mask) V, one fused kernel.
  *
@@ -65,8 +74,11 @@ typedef struct {
  *   lse  nullable; if given, contiguous fp32 (B, Hq, Nq):
  *        lse[b,h,i] = ln sum_{visible j} exp(scale * q_i . k_j)   ([P1] step 8)
  *   Hq % Hkv == 0; q head h reads kv head h / (Hq / Hkv).
- *   causal != 0: key j is visible to query i iff j <= i (top-left aligned,
- *        [P1] step 5c); blocks wholly above the diagonal are never visited.
+ *   causal: ATTN_CAUSAL_NONE, ATTN_CAUSAL_TOP_LEFT (key j visible to query i
+ *        iff j <= i, [P1] step 5c) or ATTN_CAUSAL_BOTTOM_RIGHT (j <= i + Nkv - Nq;
+ *        with Nq > Nkv the first Nq - Nkv rows see no key and get o = 0 and
+ *        lse = -inf); other values give ATTN_ERR_UNSUPPORTED.  Blocks wholly
+ *        above the diagonal are never visited.
  *   scale: multiplies the fp32 scores (any finite value, 0 and negative
  *        included; the caller typically passes 1/sqrt(D)).
  *   D in {64, 128}.  Nq, Nkv >= 1, any value (ragged tails are masked).

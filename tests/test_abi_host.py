@@ -73,6 +73,7 @@ def fwd(lib, **kw):
     (dict(Hq=3, Hkv=2), SHAPE),
     (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP),
     (dict(dtype=2), UNSUP), (dict(scale=float("nan")), UNSUP), (dict(scale=float("inf")), UNSUP),
+    (dict(causal=3), UNSUP), (dict(causal=-1), UNSUP),
     (dict(sq=S(8320, 4160, 64, 2)), UNSUP), (dict(sk=S(4160, 4160, 60, 1)), UNSUP),
     (dict(so=S(-8, 4160, 64, 1)), UNSUP),
     (dict(q=FAKE + 2), UNSUP), (dict(o=FAKE + 8), UNSUP), (dict(lse=FAKE + 2), UNSUP),

@@ -187,3 +187,53 @@ def test_whole_output_properties_8192():
     assert (o.float().abs() <= vmax[:, :, None, :] * (1 + 1e-3) + 1e-3).all()
     # lse of row i is at least the (scaled) score of its diagonal key and at most that plus ln(i+1) + max gap
     assert math.isfinite(float(l.max()))
+
+
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, Nq, Nkv, D, dtype -- causal aligned bottom-right: query i sees keys j <= i + Nkv - Nq
+    (1, 4, 2, 100, 300, 128, "fp16"),    # a ragged chunk at the end of a longer sequence
+    (2, 8, 2, 257, 1000, 64, "bf16"),
+    (1, 2, 1, 64, 4096, 128, "fp16"),    # short chunk, long context: mostly full tiles
+    (1, 2, 1, 300, 4133, 128, "fp16"),   # diagonal not aligned to a tile
+    (1, 2, 2, 300, 100, 128, "fp16"),    # Nq > Nkv: the first 200 rows see no key
+    (2, 4, 4, 513, 513, 64, "fp16"),     # Nq == Nkv: the top-left mask
+])
+def test_bottom_right_causal(shape):
+    B, Hq, Hkv, Nq, Nkv, D, dt = shape
+    case = W.PrefillCase(f"br_{B}x{Hq}x{Hkv}x{Nq}x{Nkv}x{D}_{dt}", B, Hq, Hkv, Nq, Nkv, D, dt, True,
+                         seed=3000 + Nq + Nkv + D)
+    q, k, v = W.prefill_inputs(case)
+    _say(f"{case.name} seed={case.seed} causal=bottom_right")
+    o, l = A.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, causal_align="bottom_right",
+                      scale=case.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    off = Nkv - Nq
+    Oref, Lref = oracle.attention_forward(_np(q), _np(k), _np(v), case.softmax_scale, True, causal_offset=off)
+    empty = max(0, -off)  # leading rows with no visible key
+    if empty:
+        assert torch.all(o[:, :, :empty] == 0), "rows with no visible key must be zero"
+        assert torch.all(l[:, :, :empty] == float("-inf")), "rows with no visible key have lse = -inf"
+    e = check_o(o[:, :, empty:], Oref[:, :, empty:], case.torch_dtype)
+    r = check_lse(l[:, :, empty:], Lref[:, :, empty:])
+    print(f"    max|dO| = {e:.3e}, worst lse err/bound = {r:.3f}", flush=True)
+    if Nq == Nkv:
+        o2, l2 = A.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=case.softmax_scale, return_lse=True)
+        assert torch.equal(o, o2) and torch.equal(l, l2), "bottom-right with Nq == Nkv must equal top-left bitwise"
+
+
+def test_bottom_right_single_query_matches_decode():
+    """One query aligned bottom-right against Nkv keys is a decode step over a cache of Nkv rows."""
+    B, Hq, Hkv, N, D = 2, 32, 8, 777, 128
+    case = W.PrefillCase("br_vs_decode", B, Hq, Hkv, 1, N, D, "fp16", True, seed=3333)
+    q, k, v = W.prefill_inputs(case)
+    _say(f"{case.name} seed={case.seed}")
+    o, l = A.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, causal_align="bottom_right",
+                      scale=case.softmax_scale, return_lse=True)
+    od, ld = A.attn_decode(q[:, :, 0].contiguous().to(DEV), k.to(DEV), v.to(DEV), N, scale=case.softmax_scale,
+                           return_lse=True)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.decode(_np(q[:, :, 0]), _np(k), _np(v), N, case.softmax_scale)
+    check_o(o[:, :, 0], Oref, torch.float16)
+    check_o(od, Oref, torch.float16)
+    check_lse(l[:, :, 0], Lref)
+    check_lse(ld, Lref)
