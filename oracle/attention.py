@@ -42,7 +42,9 @@ Readings taken where the pages leave a step open (each also listed in the design doc)
   the first N_q - N_kv rows of a bottom-right mask with N_q > N_kv) gets O = 0
   and lse = -inf by convention.
 * Decode is one query per (batch, head) over the first ``cache_len`` cache
-  slots, every slot visible, no causal loop ([P3] decode phase).
+  slots, every slot visible, no causal loop ([P3] decode phase).  The widening
+  to per-sequence lengths (the pages' first deferred scope item) gives batch
+  element b its own ``cache_lens[b]``; a length of 0 leaves no visible key.
 * GQA maps q head h to kv head h // group, i.e. repeat_interleave expansion of
   K/V, not tiling ([P1] step 1; [P3] GQA phase).
 
@@ -60,6 +62,7 @@ __all__ = [
     "attention_probs",
     "attention_forward",
     "decode",
+    "decode_varlen",
     "kv_cache_write",
 ]
 
@@ -182,6 +185,31 @@ def decode(q, k_cache, v_cache, cache_len: int, scale: float):
     vc = _f64(np.asarray(v_cache)[:, :, :cache_len])
     O, lse = attention_forward(q[:, :, None, :], kc, vc, scale, causal=False)
     return O[:, :, 0, :], lse[:, :, 0]
+
+
+def decode_varlen(q, k_cache, v_cache, cache_lens, scale: float):
+    """O2 per sequence: batch element b attends over its own slots [0, cache_lens[b]).
+
+    [P3] decode phase, widened as its deferred-scope list names (per-sequence
+    lengths): every slot below a sequence's length is visible, none above it.
+    q: (B, Hq, D); caches (B, Hkv, S_max, D); cache_lens: B integers in
+    [0, S_max].  A sequence of length 0 has no visible key: O = 0, lse = -inf.
+    Returns O (B, Hq, D) and lse (B, Hq), float64.
+    """
+    q = _f64(q)
+    lens = [int(x) for x in np.asarray(cache_lens).reshape(-1)]
+    B, Hq, D = q.shape
+    S_max = np.asarray(k_cache).shape[2]
+    if len(lens) != B or any(L < 0 or L > S_max for L in lens):
+        raise ValueError("cache_lens must hold B values in [0, S_max]")
+    O = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        Ob, lb = decode(q[b:b + 1], np.asarray(k_cache)[b:b + 1], np.asarray(v_cache)[b:b + 1], L, scale)
+        O[b], lse[b] = Ob[0], lb[0]
+    return O, lse
 
 
 def kv_cache_write(k_cache, v_cache, k_new, v_new, pos: int):

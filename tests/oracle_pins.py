@@ -281,6 +281,28 @@ def pin_causal_row_equals_decode():
         np.testing.assert_allclose(lsed, lse[:, :, i], rtol=0, atol=1e-13)
 
 
+def pin_decode_varlen():
+    """P10b: per-sequence lengths -- each batch element against the mpmath brute
+    force over its own prefix; equal lengths reduce to the scalar decode; a
+    length of 0 gives O = 0 and lse = -inf."""
+    rng = np.random.default_rng(101)
+    B, Hq, Hkv, S, D = 4, 4, 2, 9, 5
+    q, kc, vc = _rand(rng, B, Hq, D), _rand(rng, B, Hkv, S, D), _rand(rng, B, Hkv, S, D)
+    lens = [3, 0, 9, 1]
+    O, lse = OA.decode_varlen(q, kc, vc, lens, 0.55)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(O[b] == 0.0) and np.all(lse[b] == -np.inf)
+            continue
+        Ob, lseb = _brute(q[b:b + 1, :, None, :], kc[b:b + 1, :, :L], vc[b:b + 1, :, :L], 0.55, False)
+        np.testing.assert_allclose(O[b], Ob[0, :, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], lseb[0, :, 0], rtol=1e-12, atol=1e-12)
+    Oe, lsee = OA.decode_varlen(q, kc, vc, [6] * B, 0.55)
+    Od, lsed = OA.decode(q, kc, vc, 6, 0.55)
+    np.testing.assert_array_equal(Oe, Od)
+    np.testing.assert_array_equal(lsee, lsed)
+
+
 def pin_row_sampling_matches_full():
     """Evaluating a subset of rows gives the same values as the full evaluation."""
     rng = np.random.default_rng(11)
@@ -322,6 +344,7 @@ ALL_PINS = [
     pin_permutation_invariance,
     pin_linear_in_v,
     pin_causal_row_equals_decode,
+    pin_decode_varlen,
     pin_row_sampling_matches_full,
     pin_cache_write_touches_only_its_slots,
 ]

@@ -18,6 +18,7 @@ _orig_soft = OA._masked_softmax
 _orig_scores = OA._scores
 _orig_decode = OA.decode
 _orig_write = OA.kv_cache_write
+_orig_varlen = OA.decode_varlen
 
 
 def _vis_strict(q_pos, Nkv, causal, offset=0):
@@ -86,6 +87,16 @@ def _decode_reads_one_more(q, k_cache, v_cache, cache_len, scale):
     return _orig_decode(q, k_cache, v_cache, n, scale)
 
 
+def _varlen_longest_for_all(q, k_cache, v_cache, cache_lens, scale):
+    L = max(int(x) for x in cache_lens)
+    return _orig_varlen(q, k_cache, v_cache, [L] * len(cache_lens), scale)
+
+
+def _varlen_off_by_one(q, k_cache, v_cache, cache_lens, scale):
+    S = np.asarray(k_cache).shape[2]
+    return _orig_varlen(q, k_cache, v_cache, [min(int(x) + 1, S) for x in cache_lens], scale)
+
+
 def _write_shifted(k_cache, v_cache, k_new, v_new, pos):
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
@@ -111,6 +122,8 @@ MUTATIONS = {
     "masked_keys_in_sum": ("_masked_softmax", _soft_mask_ignored_in_sum),
     "decode_reads_past_cache_len": ("decode", _decode_reads_one_more),
     "cache_write_off_by_one": ("kv_cache_write", _write_shifted),
+    "varlen_longest_for_all": ("decode_varlen", _varlen_longest_for_all),
+    "varlen_reads_one_more": ("decode_varlen", _varlen_off_by_one),
 }
 
 
