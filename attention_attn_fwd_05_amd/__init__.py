@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
 * ``attn_fwd(q, k, v, *, causal, scale=None, return_lse=False, out=None)``
 * ``attn_decode(q, k_cache, v_cache, cache_len, *, scale=None, workspace=None,
   num_splits=0, return_lse=False, out=None)``
+* ``attn_decode_varlen(q, k_cache, v_cache, cache_lens, max_cache_len=None, ...)``
+  (one cache length per sequence, read on the device)
 * ``attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)`` /
   ``decode_workspace(...)`` (a uint8 scratch tensor of that size)
 * ``kv_cache_write(k_cache, v_cache, k_new, v_new, pos)``
@@ -20,6 +22,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     Status,
     attn_decode,
+    attn_decode_varlen,
     attn_decode_workspace_bytes,
     attn_fwd,
     decode_workspace,
@@ -33,6 +36,7 @@ __all__ = [
     "Status",
     "attn_fwd",
     "attn_decode",
+    "attn_decode_varlen",
     "attn_decode_workspace_bytes",
     "decode_workspace",
     "kv_cache_write",

@@ -56,6 +56,9 @@ def load_library():
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32,
                                 vp, ctypes.c_size_t, vp]
     lib.attn_decode.restype = i32
+    lib.attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, S, S, S, S, f32, i32,
+                                       i32, vp, ctypes.c_size_t, vp]
+    lib.attn_decode_varlen.restype = i32
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, i32, vp]
     lib.kv_cache_write.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -182,6 +185,45 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, c
                          s, code, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                          _stream(q))
     _check(st, "attn_decode")
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_lens: torch.Tensor,
+                       max_cache_len: int | None = None, *, scale: float | None = None,
+                       workspace: torch.Tensor | None = None, num_splits: int = 0, return_lse: bool = False,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Decode one token per (batch, q head); batch element b attends over slots [0, cache_lens[b]).
+
+    ``cache_lens``: int32 tensor of B lengths on the same GPU (read by the kernel,
+    no host sync; each is clamped to [0, max_cache_len]).  ``max_cache_len``:
+    host bound on the lengths that sizes the split grid (default: S_max).
+    """
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,) or not cache_lens.is_contiguous():
+        raise ValueError("cache_lens must be a contiguous int32 tensor of shape (B,)")
+    mcl = S_max if max_cache_len is None else int(max_cache_len)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq)")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, S_max, D, q.device)
+    _on_gpu(q, k_cache, v_cache, out, workspace, cache_lens, *([lse] if lse is not None else []))
+    code = _dtype_code(q, k_cache, v_cache, out)
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, caches and out")
+    s = _default_scale(D) if scale is None else float(scale)
+    st = lib.attn_decode_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None,
+                                B, Hq, Hkv, S_max, cache_lens.data_ptr(), mcl, D,
+                                _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out),
+                                s, code, int(num_splits), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(q))
+    _check(st, "attn_decode_varlen")
     return (out, lse) if return_lse else out
 
 

@@ -138,8 +138,12 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D) {
   return g.part_bytes;
 }
 
-attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                        int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+namespace {
+
+// shared by attn_decode (lens == nullptr: every sequence has cache_len slots)
+// and attn_decode_varlen (sequence b has min(max(lens[b], 0), cache_len))
+attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        int B, int Hq, int Hkv, int S_max, int cache_len, const int32_t* lens, int D,
                         attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
                         float scale, attn_dtype dtype, int num_splits,
                         void* workspace, size_t workspace_bytes, void* stream) {
@@ -155,6 +159,7 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!strides_ok(sq3) || !strides_ok(skc) || !strides_ok(svc) || !strides_ok(so3)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
+  if (lens && (reinterpret_cast<uintptr_t>(lens) & 3u)) return ATTN_ERR_UNSUPPORTED;
   const DecodeGeometry g = decode_geometry(B, Hq, Hkv, S_max, D);
   if (!workspace || !aligned16(workspace) || workspace_bytes < g.part_bytes)
     return ATTN_ERR_WORKSPACE;
@@ -178,6 +183,7 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.v = static_cast<const uint16_t*>(v_cache);
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
+  a.lens = lens;
   a.sqb = sq.b; a.sqh = sq.h;
   a.skb = skc.b; a.skh = skc.h; a.skn = skc.n;
   a.svb = svc.b; a.svh = svc.h; a.svn = svc.n;
@@ -194,6 +200,27 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
 
   const hipError_t e = attn::launch_decode(a, B, D, dtype == ATTN_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+                        attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
+                        float scale, attn_dtype dtype, int num_splits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, cache_len, nullptr, D, sq, skc, svc, so,
+                     scale, dtype, num_splits, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                               int B, int Hq, int Hkv, int S_max, const int32_t* cache_lens, int max_cache_len,
+                               int D, attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
+                               float scale, attn_dtype dtype, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache_lens) return ATTN_ERR_NULL;
+  return decode_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, max_cache_len, cache_lens, D, sq, skc, svc,
+                     so, scale, dtype, num_splits, workspace, workspace_bytes, stream);
 }
 
 attn_status kv_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

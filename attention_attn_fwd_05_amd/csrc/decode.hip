@@ -83,8 +83,12 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   const int col = lane & 15;  // MFMA column = q head within the group
   const int rg = lane >> 4;   // 4-row group of the MFMA output / k-group of operands
 
+  // this sequence's length (per-sequence lengths are clamped to [0, cache_len]);
+  // a split at or past it loads nothing (out-of-range buffer loads) and
+  // publishes an empty partial: m = -inf, l = 0
+  const int seq_len = a.lens ? min(max(a.lens[b], 0), a.cache_len) : a.cache_len;
   const int k0 = split * a.rows_per_split;
-  const int k1 = min(a.cache_len, k0 + a.rows_per_split);
+  const int k1 = min(seq_len, k0 + a.rows_per_split);
 
   // q heads as the B operand.  Columns beyond nh repeat the group's last head:
   // MFMA columns never mix, and those columns' results are never stored.  (A

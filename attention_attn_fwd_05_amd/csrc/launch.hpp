@@ -38,11 +38,12 @@ struct DecodeArgs {
   const uint16_t* v;
   uint16_t* o;
   float* lse;  // nullable, contiguous (B, Hq)
+  const int32_t* lens;  // nullable: per-sequence lengths, clamped to [0, cache_len]
   int64_t sqb, sqh;
   int64_t skb, skh, skn;
   int64_t svb, svh, svn;
   int64_t sob, soh;
-  int Hq, Hkv, group, cache_len;
+  int Hq, Hkv, group, cache_len;  // cache_len: every sequence's length, or the bound on lens
   int heads_per_wg;  // q heads handled by one workgroup (<= 16)
   int hgroups;       // head groups per kv head
   int nsplit;          // chunks along the cache (<= max_splits)

@@ -26,6 +26,11 @@ FETCH_SIZE and WRITE_SIZE counters measured (scaled by a plain copy's reading),
 taken from the committed summaries under profiles/; null once the kernel
 sources differ from the ones those counters were taken with.
 
+The default run also times two widened workloads (not the headline):
+decode with per-sequence cache lengths over a 16-sequence batch, and a
+chunked prefill (1024 queries at the end of an 8192-token context, causal
+aligned bottom-right); they are printed under "widened".
+
 Flags: --only prefill|decode|copy runs just that launch (for rocprofv3 runs),
 --no-cpu skips the oracle baseline.  Prints one JSON line.
 """
@@ -243,6 +248,56 @@ def main():
         torch.cuda.synchronize()
         dec_warm = e0.elapsed_time(e1) / R
 
+    # widened rows (not the headline): decode with per-sequence lengths over a
+    # 16-sequence batch, and a chunked prefill (causal aligned bottom-right)
+    widened = None
+    if args.only == "all":
+        widened = {}
+        vc_case = W.decode_varlen_case()
+        vq, vk, vv = W.decode_inputs(vc_case)
+        vlens_h = W.decode_varlen_lens(vc_case)
+        vq, vk, vv, vlens = vq.to(dev), vk.to(dev), vv.to(dev), vlens_h.to(dev)
+        vo = torch.empty_like(vq)
+        vws = A.decode_workspace(vc_case.B, vc_case.Hq, vc_case.Hkv, vc_case.S_max, vc_case.D, dev)
+        vbytes = 2 * vc_case.Hkv * int(vlens_h.sum()) * vc_case.D * 2 + 2 * vc_case.B * vc_case.Hq * vc_case.D * 2
+        for _ in range(3):
+            A.attn_decode_varlen(vq, vk, vv, vlens, vc_case.S_max, workspace=vws, out=vo)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            A.attn_decode_varlen(vq, vk, vv, vlens, vc_case.S_max, workspace=vws, out=vo)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vt = e0.elapsed_time(e1) / 20
+        widened["decode_varlen"] = {
+            "workload": vc_case.name, "B": vc_case.B, "Hq": vc_case.Hq, "Hkv": vc_case.Hkv, "D": vc_case.D,
+            "S_max": vc_case.S_max, "lengths": "seeded uniform [1, 8192]", "sum_lengths": int(vlens_h.sum()),
+            "bytes_per_call": vbytes, "us_per_call": round(vt * 1e3, 2),
+            "gbs": round(vbytes / (vt * 1e-3) / 1e9, 1), "frac_of_8000_gbs": round(vbytes / (vt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del vq, vk, vv, vo, vws
+        cp = W.chunked_prefill_case()
+        cq, ck, cv = (t.to(dev) for t in W.prefill_inputs(cp))
+        co = torch.empty_like(cq)
+        cflops = 4 * cp.D * cp.B * cp.Hq * W.bottom_right_pairs(cp.Nq, cp.Nkv)
+        for _ in range(3):
+            A.attn_fwd(cq, ck, cv, causal=True, causal_align="bottom_right", scale=cp.softmax_scale, out=co)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0.record(stream)
+        for _ in range(10):
+            A.attn_fwd(cq, ck, cv, causal=True, causal_align="bottom_right", scale=cp.softmax_scale, out=co)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ct_ = e0.elapsed_time(e1) / 10
+        widened["chunked_prefill"] = {
+            "workload": cp.name, "B": cp.B, "Hq": cp.Hq, "Hkv": cp.Hkv, "Nq": cp.Nq, "Nkv": cp.Nkv, "D": cp.D,
+            "causal": "bottom_right", "flops_per_launch": cflops, "ms_per_launch": round(ct_, 4),
+            "tflops": round(cflops / (ct_ * 1e-3) / 1e12, 1),
+            "frac_of_2500_tflops": round(cflops / (ct_ * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+        del cq, ck, cv, co
+
     # context: achievable HBM rate of a plain 256 MiB device copy (read + write)
     copy_gbs = None
     if args.only == "all":
@@ -319,6 +374,8 @@ def main():
                          "timing": "back-to-back calls over rotating caches (split kernel + combine kernel)",
                          "kernel": "decode_kernel<128, f16> + decode_combine_kernel<128, f16>",
                          "traffic": measured_traffic("decode_L8192_hkv8_d128_fp16.md", DECODE_SOURCES)}
+    if widened:
+        out["widened"] = widened
     if copy_gbs is not None:
         out["context"] = {"hbm_copy_gbs": round(copy_gbs, 1),
                           "note": "plain 256 MiB device copy (read+write bytes) on this box: an achievable HBM rate; "

@@ -127,6 +127,29 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_varlen -- attn_decode with a length per sequence: batch element
+ * b attends to its cache slots [0, cache_lens[b]).  Per-sequence lengths are
+ * the first item of [P3]'s deferred scope ("Out of scope for now": decode for
+ * sequences of different lengths in one batch); everything else is
+ * attn_decode's definition.
+ *
+ *   cache_lens     device pointer to B int32 values, 4-byte aligned; each is
+ *                  used as min(max(cache_lens[b], 0), max_cache_len).  A
+ *                  sequence of length 0 gets o = 0 and lse = -inf.
+ *   max_cache_len  host bound, 1 <= max_cache_len <= S_max; it sizes the
+ *                  split grid (passing S_max is always valid; a tighter bound
+ *                  launches fewer empty chunks).  Slots at or beyond a
+ *                  sequence's length are never read.
+ *   Other arguments, the workspace rules and the error codes are attn_decode's;
+ *   a null cache_lens gives ATTN_ERR_NULL.
+ */
+attn_status attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                               int B, int Hq, int Hkv, int S_max, const int32_t* cache_lens, int max_cache_len,
+                               int D, attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
+                               float scale, attn_dtype dtype, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kv_cache_write -- copy T new rows per (batch, kv head) into cache slots
  * [pos, pos + T) of K and V ([P3] decode phase: the preallocated-cache write
  * helper kept separate from the attention kernel).  A bit-exact copy; every

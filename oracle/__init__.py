@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_probs,
     decode,
+    decode_varlen,
     kv_cache_write,
     kv_head_of,
     visibility,

@@ -42,8 +42,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "kv_cache_write",
-                          "attn_status_string"}
+    assert set(names) == {"attn_fwd", "attn_decode", "attn_decode_varlen", "attn_decode_workspace_bytes",
+                          "kv_cache_write", "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -105,6 +105,27 @@ def dec(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, code):
     assert dec(lib, **kw) == code
+
+
+def decv(lib, **kw):
+    B, Hq, Hkv, Smax, D = 2, 32, 8, 8192, 128
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, B=B, Hq=Hq, Hkv=Hkv, S_max=Smax, lens=FAKE, mcl=100, D=D,
+             sq=S(Hq * D, D, 0, 1), skc=c4(D, Smax, Hkv), svc=c4(D, Smax, Hkv), so=S(Hq * D, D, 0, 1),
+             scale=0.088, dtype=0, num_splits=0, ws=FAKE,
+             ws_bytes=lib.attn_decode_workspace_bytes(B, Hq, Hkv, Smax, D), stream=None)
+    a.update(kw)
+    return lib.attn_decode_varlen(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["S_max"],
+                                  a["lens"], a["mcl"], a["D"], a["sq"], a["skc"], a["svc"], a["so"], a["scale"],
+                                  a["dtype"], a["num_splits"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=None), NULL), (dict(q=None), NULL), (dict(lens=FAKE + 2), UNSUP),
+    (dict(mcl=0), SHAPE), (dict(mcl=8193), SHAPE), (dict(Hq=30), SHAPE),
+    (dict(D=96), UNSUP), (dict(ws=None), WS), (dict(ws_bytes=1024), WS),
+])
+def test_decode_varlen_rejects(lib, kw, code):
+    assert decv(lib, **kw) == code
 
 
 def cw(lib, **kw):

@@ -149,3 +149,82 @@ def test_autoregressive_equivalence(Hkv):
     check_o(o_dec, Oref, torch.float16, "decode")
     d = (o_pre.float() - o_dec.float()).abs().max().item()
     assert d <= 2e-3, d
+
+
+# ---- per-sequence cache lengths (attn_decode_varlen)
+
+def _poison_per_seq(cache: torch.Tensor, lens) -> torch.Tensor:
+    c = cache.clone()
+    for b, L in enumerate(lens):
+        c[b, :, L:] = float("nan")
+    return c
+
+
+def run_varlen(case: W.DecodeCase, lens, max_len=None, num_splits=0):
+    q, kc, vc = W.decode_inputs(case)
+    _say(f"{case.name} varlen lens={list(lens)} max_len={max_len} splits={num_splits}")
+    eff = [min(max(int(L), 0), max_len if max_len is not None else case.S_max) for L in lens]
+    kd, vd = _poison_per_seq(kc, eff).to(DEV), _poison_per_seq(vc, eff).to(DEV)
+    ld = torch.tensor(list(lens), dtype=torch.int32, device=DEV)
+    o, l = A.attn_decode_varlen(q.to(DEV), kd, vd, ld, max_len, scale=case.softmax_scale,
+                                num_splits=num_splits, return_lse=True)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.decode_varlen(_np(q), _np(kc), _np(vc), eff, case.softmax_scale)
+    live = [b for b, L in enumerate(eff) if L > 0]
+    for b, L in enumerate(eff):
+        if L == 0:
+            assert torch.all(o[b] == 0) and torch.all(l[b] == float("-inf")), f"sequence {b} of length 0"
+    if live:
+        e = check_o(o[live], Oref[live], case.torch_dtype)
+        r = check_lse(l[live], Lref[live])
+        print(f"    max|dO| = {e:.3e}, worst lse err/bound = {r:.3f}", flush=True)
+    return o, l
+
+
+@pytest.mark.parametrize("lens", [
+    [8192, 1],
+    [0, 777],
+    [129, 128],
+])
+def test_decode_varlen_serving_shape(lens):
+    run_varlen(W.decode_case(8192), lens)
+
+
+def test_decode_varlen_mixed_batch():
+    """A 9-sequence batch with lengths across tile and split boundaries, incl. 0."""
+    case = W.DecodeCase("varlen_b9", 9, 16, 4, 2048, 2048, 128, "fp16", seed=W.BASE_SEED + 71)
+    run_varlen(case, [0, 1, 31, 127, 128, 129, 1000, 2047, 2048])
+
+
+@pytest.mark.parametrize("dtype,D,Hkv", [("bf16", 128, 1), ("fp16", 64, 2), ("bf16", 64, 8)])
+def test_decode_varlen_dtypes_heads(dtype, D, Hkv):
+    case = W.DecodeCase(f"varlen_{dtype}_d{D}_hkv{Hkv}", 4, 8, Hkv, 1500, 1500, D, dtype, seed=W.BASE_SEED + 72 + D)
+    run_varlen(case, [1500, 3, 700, 0])
+
+
+def test_decode_varlen_max_len_clamps_and_bounds_grid():
+    """Lengths above max_cache_len are clamped to it; a tighter bound gives the same result as S_max."""
+    case = W.DecodeCase("varlen_clamp", 3, 8, 8, 4096, 4096, 128, "fp16", seed=W.BASE_SEED + 75)
+    run_varlen(case, [4000, 900, 2500], max_len=1000)     # 4000 and 2500 read as 1000
+    o1, l1 = run_varlen(case, [300, 17, 999], max_len=1000)
+    o2, l2 = run_varlen(case, [300, 17, 999], max_len=None)
+    assert torch.allclose(o1.float(), o2.float(), atol=2e-3, rtol=0)
+
+
+def test_decode_varlen_equal_lengths_is_decode_bitwise():
+    case = W.decode_case(4096)
+    q, kc, vc = W.decode_inputs(case)
+    _say("varlen equal lengths vs attn_decode")
+    qd, kd, vd = q.to(DEV), kc.to(DEV), vc.to(DEV)
+    for L in (4096, 1000, 1):
+        o1, l1 = A.attn_decode(qd, kd, vd, L, scale=case.softmax_scale, return_lse=True)
+        lens = torch.full((case.B,), L, dtype=torch.int32, device=DEV)
+        o2, l2 = A.attn_decode_varlen(qd, kd, vd, lens, L, scale=case.softmax_scale, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"L={L}"
+
+
+@pytest.mark.parametrize("ns", [1, 3, 64])
+def test_decode_varlen_split_counts(ns):
+    run_varlen(W.DecodeCase("varlen_splits", 5, 8, 4, 3000, 3000, 128, "fp16", seed=W.BASE_SEED + 76),
+               [3000, 2999, 1, 1537, 0], num_splits=ns)

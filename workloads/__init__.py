@@ -157,4 +157,29 @@ def decode_case(cache_len: int, dtype: str = "fp16", Hkv: int = 8, seed_offset: 
                       seed=BASE_SEED + 20 + seed_offset)
 
 
+def decode_varlen_case():
+    """Per-sequence lengths: a 16-sequence serving batch, Hq=32, Hkv=8, D=128,
+    8192-slot caches; lengths drawn by ``decode_varlen_lens``."""
+    return DecodeCase("decode_varlen_b16_hkv8_fp16", 16, 32, 8, 8192, 8192, 128, "fp16", seed=BASE_SEED + 30)
+
+
+def decode_varlen_lens(case: DecodeCase) -> torch.Tensor:
+    """Seeded cache lengths, uniform in [1, S_max], int32 (B,)."""
+    g = _gen(case.seed + 1000)
+    return torch.randint(1, case.S_max + 1, (case.B,), generator=g, dtype=torch.int32)
+
+
+def chunked_prefill_case(nq: int = 1024, nkv: int = 8192):
+    """Causal aligned bottom-right: the last ``nq`` queries of an ``nkv``-token
+    sequence against all its keys (chunked prefill), serving heads."""
+    return PrefillCase(f"chunk_q{nq}_kv{nkv}_d128_fp16_bottom_right", 2, 32, 8, nq, nkv, 128, "fp16", True,
+                       seed=BASE_SEED + 31)
+
+
+def bottom_right_pairs(Nq: int, Nkv: int) -> int:
+    """Visible (query, key) pairs per head of a bottom-right causal mask."""
+    off = Nkv - Nq
+    return sum(max(0, min(Nkv, i + off + 1)) for i in range(Nq))
+
+
 AR_TOKENS = 512
