@@ -22,6 +22,10 @@ constexpr int kDecodeMaxSplits = 64;     // partials one combine merges
 #define ATTN_DECODE_TARGET_WGS 512
 #endif
 constexpr int kDecodeTargetWorkgroups = ATTN_DECODE_TARGET_WGS;  // decode workgroups that fill MI355X (2 per CU)
+// with per-sequence lengths, default chunks hold at most this many tiles (768
+// rows): the chunks covering a sequence then number in proportion to its
+// length and the last workgroups to finish hold little work
+constexpr int kDecodeVarlenChunkTiles = 6;
 constexpr int kDecodePartPad = 4;       // floats ahead of o[D] in a per-head partial
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -163,14 +167,19 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   const DecodeGeometry g = decode_geometry(B, Hq, Hkv, S_max, D);
   if (!workspace || !aligned16(workspace) || workspace_bytes < g.part_bytes)
     return ATTN_ERR_WORKSPACE;
-  if ((int64_t)B * Hkv > 65535 || g.hgroups > 65535) return ATTN_ERR_SHAPE;  // grid y/z limits
+  // B * Hkv goes in grid x (limit 2^31 - 1) or z (limit 65535); head groups in y
+  if ((int64_t)B * Hkv > 0x7fffffff || g.hgroups > 65535) return ATTN_ERR_SHAPE;
 
   const int tiles = (cache_len + kDecodeTile - 1) / kDecodeTile;
   // default: enough chunks for ~kDecodeTargetWorkgroups workgroups (two per CU,
   // each with two 128-row tiles in flight), at most max_splits per (batch, kv
   // head, head group)
-  const int slots = B * Hkv * g.hgroups;
-  int want = num_splits > 0 ? num_splits : (kDecodeTargetWorkgroups + slots - 1) / slots;
+  const int64_t slots = (int64_t)B * Hkv * g.hgroups;
+  int want = num_splits > 0 ? num_splits : (int)((kDecodeTargetWorkgroups + slots - 1) / slots);
+  if (num_splits == 0 && lens) {
+    const int floor_splits = (tiles + kDecodeVarlenChunkTiles - 1) / kDecodeVarlenChunkTiles;
+    if (want < floor_splits) want = floor_splits;
+  }
   if (want > g.max_splits) want = g.max_splits;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
@@ -194,6 +203,7 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.nsplit = nsplit;
   a.max_splits = g.max_splits;
   a.rows_per_split = tiles_per_split * kDecodeTile;
+  a.unit_fast = (lens != nullptr || (int64_t)B * Hkv > 65535) ? 1 : 0;
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
   a.part = static_cast<float*>(workspace);

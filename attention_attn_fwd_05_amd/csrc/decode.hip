@@ -52,7 +52,7 @@ __device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
   return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool VARLEN>
 __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel(const DecodeArgs a) {
   constexpr int KS = D / 32;                 // k-steps of the score MFMA
   constexpr int NDT = D / 16;                // 16-wide head-dim tiles of O
@@ -69,9 +69,15 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];  // V^T stage, then the merges
   uint16_t* const vt = reinterpret_cast<uint16_t*>(lds);
 
-  const int split = blockIdx.x;
+  // Consecutive workgroups are dealt round-robin to the XCDs.  With one length
+  // for every sequence the chunk index runs fastest (each (batch, kv head)
+  // spread over all XCDs).  With per-sequence lengths the (batch, kv head)
+  // index runs fastest: all kv heads of a sequence share its length, so the
+  // chunks that cover short sequences spread over every XCD instead of piling
+  // onto the XCDs that chunks 0, 1, ... would map to.
+  const int unit = a.unit_fast ? blockIdx.x : blockIdx.z;
   const int hgi = blockIdx.y;
-  const int unit = blockIdx.z;
+  const int split = a.unit_fast ? blockIdx.z : blockIdx.x;
   const int b = unit / a.Hkv;
   const int kvh = unit - b * a.Hkv;
   const int h0 = kvh * a.group + hgi * a.heads_per_wg;  // first q head of this workgroup
@@ -83,12 +89,16 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   const int col = lane & 15;  // MFMA column = q head within the group
   const int rg = lane >> 4;   // 4-row group of the MFMA output / k-group of operands
 
-  // this sequence's length (per-sequence lengths are clamped to [0, cache_len]);
-  // a split at or past it loads nothing (out-of-range buffer loads) and
-  // publishes an empty partial: m = -inf, l = 0
-  const int seq_len = a.lens ? min(max(a.lens[b], 0), a.cache_len) : a.cache_len;
+  // this sequence's length (VARLEN: per-sequence lengths clamped to [0,
+  // cache_len]).  A chunk wholly past it has nothing to do: with several chunks
+  // the combine merges only the chunks that cover the sequence, so it writes
+  // nothing; a single chunk (length 0) still writes o = 0 and lse = -inf below.
+  // Without per-sequence lengths every chunk is non-empty and none of this is
+  // compiled in (the test would delay the first loads).
+  const int seq_len = VARLEN ? min(max(a.lens[b], 0), a.cache_len) : a.cache_len;
   const int k0 = split * a.rows_per_split;
   const int k1 = min(seq_len, k0 + a.rows_per_split);
+  if (VARLEN && a.nsplit > 1 && k0 >= seq_len) return;  // uniform over the workgroup
 
   // q heads as the B operand.  Columns beyond nh repeat the group's last head:
   // MFMA columns never mix, and those columns' results are never stored.  (A
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
 // sum_s e^(m_s - M) l_s and lse = M + ln(sum_s e^(m_s - M) l_s) (log2 domain
 // inside).  Thread -> (4-wide column of o, group of splits strided by G); all
 // of a thread's partial loads are issued before the (m, l) reduction.
-template <int D, bool BF16>
+template <int D, bool BF16, bool VARLEN>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a) {
   constexpr int HP = D + kPartPad;
   constexpr int C4 = D / 4;    // 4-wide columns
@@ -313,15 +323,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
   constexpr int PER = (kMaxSplits + G - 1) / G;  // splits per thread at most
   __shared__ float sm[kMaxSplits], sw[kMaxSplits], sl[kMaxSplits];
   __shared__ __attribute__((aligned(16))) float sacc[G * D];
-  const int hx = blockIdx.x;  // head within the group
+  const int unit = a.unit_fast ? blockIdx.x : blockIdx.z;  // batch x kv head
   const int hgi = blockIdx.y;
-  const int unit = blockIdx.z;
+  const int hx = a.unit_fast ? blockIdx.z : blockIdx.x;  // head within the group
   const int nh = min(a.heads_per_wg, a.group - hgi * a.heads_per_wg);
   if (hx >= nh) return;  // whole workgroup: uniform
   const int b = unit / a.Hkv;
   const int kvh = unit - b * a.Hkv;
   const int h = kvh * a.group + hgi * a.heads_per_wg + hx;
-  const int ns = a.nsplit;
+  // chunks that cover this sequence (all of them without per-sequence lengths)
+  int ns = a.nsplit;
+  if (VARLEN) {
+    const int seq_len = min(max(a.lens[b], 0), a.cache_len);
+    ns = min(ns, (seq_len + a.rows_per_split - 1) / a.rows_per_split);
+  }
   const int64_t slot = (int64_t)unit * a.hgroups + hgi;
   const float* base = a.part + (slot * a.max_splits * a.heads_per_wg + hx) * HP;
   const int64_t sstride = (int64_t)a.heads_per_wg * HP;  // between splits
@@ -365,13 +380,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
   }
 }
 
+template <int D, bool BF16, bool VARLEN>
+hipError_t launch_v(const DecodeArgs& a, int B, hipStream_t stream) {
+  const unsigned units = (unsigned)(B * a.Hkv);
+  const dim3 g1 = a.unit_fast ? dim3(units, a.hgroups, a.nsplit) : dim3(a.nsplit, a.hgroups, units);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, VARLEN>), g1, dim3(256), 0, stream, a);
+  if (a.nsplit > 1) {
+    const dim3 g2 = a.unit_fast ? dim3(units, a.hgroups, a.heads_per_wg) : dim3(a.heads_per_wg, a.hgroups, units);
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, VARLEN>), g2, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool BF16>
 hipError_t launch_t(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, BF16>), dim3(a.nsplit, a.hgroups, B * a.Hkv), dim3(256), 0, stream, a);
-  if (a.nsplit > 1)
-    hipLaunchKernelGGL((decode_combine_kernel<D, BF16>), dim3(a.heads_per_wg, a.hgroups, B * a.Hkv), dim3(256), 0,
-                       stream, a);
-  return hipGetLastError();
+  return a.lens ? launch_v<D, BF16, true>(a, B, stream) : launch_v<D, BF16, false>(a, B, stream);
 }
 
 // ---- cache writer: a plain 16-byte-vector copy of T rows per (batch, kv head)

@@ -49,6 +49,7 @@ struct DecodeArgs {
   int nsplit;          // chunks along the cache (<= max_splits)
   int max_splits;      // partial slots per (unit, head group) in the workspace (<= 64)
   int rows_per_split;  // multiple of the 128-row tile
+  int unit_fast;       // grid order: 1 = (unit, head group, chunk), 0 = (chunk, head group, unit)
   float c;
   uint32_t qsign;
   float* part;  // workspace: partial (m, l, pad, pad, o[D]) per (unit, head group, split, head)

@@ -228,3 +228,30 @@ def test_decode_varlen_equal_lengths_is_decode_bitwise():
 def test_decode_varlen_split_counts(ns):
     run_varlen(W.DecodeCase("varlen_splits", 5, 8, 4, 3000, 3000, 128, "fp16", seed=W.BASE_SEED + 76),
                [3000, 2999, 1, 1537, 0], num_splits=ns)
+
+
+def test_decode_varlen_serving_batch_default_splits():
+    """The 16-sequence serving batch with seeded lengths, at the default chunking."""
+    case = W.decode_varlen_case()
+    run_varlen(case, [int(x) for x in W.decode_varlen_lens(case)])
+
+
+def test_decode_many_units_grid():
+    """B * Hkv above 65535 (more (batch, kv head) units than a grid's y or z
+    extent holds): sampled sequences against the oracle, one length for all."""
+    B, Hq, Hkv, S, L, D = 8193, 8, 8, 32, 20, 64
+    _say(f"decode B={B} Hkv={Hkv} L={L}")
+    g = torch.Generator().manual_seed(W.BASE_SEED + 77)
+    q = torch.randn(B, Hq, D, generator=g).half()
+    kc = torch.randn(B, Hkv, S, D, generator=g).half()
+    vc = torch.randn(B, Hkv, S, D, generator=g).half()
+    scale = D ** -0.5
+    o, l = A.attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), L, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    o, l = o.cpu(), l.cpu()
+    pick = [0, 1, 4095, 8191, 8192]
+    Oref, Lref = oracle.decode(_np(q[pick]), _np(kc[pick]), _np(vc[pick]), L, scale)
+    e = check_o(o[pick], Oref, torch.float16)
+    r = check_lse(l[pick], Lref)
+    print(f"    max|dO| = {e:.3e}, worst lse err/bound = {r:.3f}", flush=True)
+    assert torch.isfinite(o.float()).all()
