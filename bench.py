@@ -372,7 +372,7 @@ def main():
         out["decode"] = {"achieved": round(g, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "bound": "hbm",
                          "frac": round(g / HBM_PEAK_GBS, 4), "us_per_call": round(dec_ss * 1e3, 2),
                          "timing": "back-to-back calls over rotating caches (split kernel + combine kernel)",
-                         "kernel": "decode_kernel<128, f16> + decode_combine_kernel<128, f16>",
+                         "kernel": "decode_kernel<128, f16, uniform lengths> + decode_combine_kernel<128, f16, uniform lengths>",
                          "traffic": measured_traffic("decode_L8192_hkv8_d128_fp16.md", DECODE_SOURCES)}
     if widened:
         out["widened"] = widened
