@@ -7,9 +7,12 @@ may import this package.  The HIP product path never does.
 from .attention import (  # noqa: F401
     attention_forward,
     attention_probs,
+    attention_varlen,
     decode,
     decode_varlen,
     kv_cache_write,
     kv_head_of,
+    sequence_bounds,
+    varlen_causal_offset,
     visibility,
 )

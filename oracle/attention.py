@@ -47,6 +47,12 @@ Readings taken where the pages leave a step open (each also listed in the design doc)
   element b its own ``cache_lens[b]``; a length of 0 leaves no visible key.
 * GQA maps q head h to kv head h // group, i.e. repeat_interleave expansion of
   K/V, not tiling ([P1] step 1; [P3] GQA phase).
+* Packed variable-length prefill (the pages' deferred "varlen" scope item):
+  sequence b owns the packed query rows [cu_q[b], cu_q[b+1]) and key rows
+  [cu_k[b], cu_k[b+1]); attention never crosses sequences, and each sequence
+  is the plain definition above on its own rows, with the causal offset taken
+  from its own lengths (0 top-left, L_k - L_q bottom-right).  A sequence with
+  no keys gets O = 0 and lse = -inf on its rows.
 
 Pins: tests/test_oracle_pins.py checks this module against closed forms,
 hand-derived fixtures (tests/golden/), invariants and an mpmath brute force.
@@ -63,6 +69,9 @@ __all__ = [
     "attention_forward",
     "decode",
     "decode_varlen",
+    "sequence_bounds",
+    "varlen_causal_offset",
+    "attention_varlen",
     "kv_cache_write",
 ]
 
@@ -209,6 +218,67 @@ def decode_varlen(q, k_cache, v_cache, cache_lens, scale: float):
             continue
         Ob, lb = decode(q[b:b + 1], np.asarray(k_cache)[b:b + 1], np.asarray(v_cache)[b:b + 1], L, scale)
         O[b], lse[b] = Ob[0], lb[0]
+    return O, lse
+
+
+def sequence_bounds(cu_seqlens, b: int):
+    """Packed rows [cu[b], cu[b+1]) belong to sequence b (cumulative-length offsets)."""
+    cu = np.asarray(cu_seqlens).reshape(-1)
+    return int(cu[b]), int(cu[b + 1])
+
+
+def varlen_causal_offset(Lq: int, Lk: int, bottom_right: bool) -> int:
+    """Causal offset of one packed sequence: query i sees keys j <= i + offset.
+
+    Top-left ([P1] step 5c) is 0; bottom-right treats the L_q queries as the
+    last L_q of the sequence's L_k positions, offset L_k - L_q."""
+    return Lk - Lq if bottom_right else 0
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
+                     bottom_right: bool = False, rows=None):
+    """O1 over a batch of packed sequences of different lengths.
+
+    The pages defer variable-length batches ([P3] deferred scope); this is the
+    plain definition of ``attention_forward`` applied to each sequence's own
+    rows.  q: (T_q, Hq, D) packed query rows; k, v: (T_k, Hkv, D) packed key
+    rows; cu_seqlens_q / cu_seqlens_k: B + 1 non-decreasing offsets from 0 to
+    T_q / T_k.  causal with ``bottom_right`` uses ``varlen_causal_offset``.
+    rows: optional packed query-row indices to evaluate (sampling at large
+    sizes); default all T_q rows.
+
+    Returns O (R, Hq, D) and lse (Hq, R), float64, R = number of evaluated rows.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    Tq, Hq, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64).reshape(-1)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64).reshape(-1)
+    B = cq.shape[0] - 1
+    if (Dk != D or v.shape != k.shape or Hq % Hkv != 0 or B < 1 or ck.shape[0] != B + 1
+            or cq[0] != 0 or ck[0] != 0 or cq[-1] != Tq or ck[-1] != Tk
+            or np.any(np.diff(cq) < 0) or np.any(np.diff(ck) < 0)):
+        raise ValueError("shape or offsets mismatch")
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    O = np.zeros((R, Hq, D))
+    lse = np.full((Hq, R), -np.inf)
+    seq_of_row = np.searchsorted(cq, rows, side="right") - 1
+    for b in range(B):
+        q0, q1 = sequence_bounds(cq, b)
+        k0, k1 = sequence_bounds(ck, b)
+        pick = np.nonzero((seq_of_row == b) & (rows >= q0) & (rows < q1))[0]
+        if pick.size == 0 or k1 == k0:
+            continue  # no rows asked for, or no keys: O = 0, lse = -inf
+        off = varlen_causal_offset(q1 - q0, k1 - k0, bottom_right) if causal else 0
+        qs = q[q0:q1].transpose(1, 0, 2)[None]
+        ks = k[k0:k1].transpose(1, 0, 2)[None]
+        vs = v[k0:k1].transpose(1, 0, 2)[None]
+        Ob, lb = attention_forward(qs, ks, vs, scale, causal, rows=rows[pick] - q0, causal_offset=off)
+        O[pick] = Ob[0].transpose(1, 0, 2)
+        lse[:, pick] = lb[0]
     return O, lse
 
 

@@ -303,6 +303,39 @@ def pin_decode_varlen():
     np.testing.assert_array_equal(lsee, lsed)
 
 
+def pin_prefill_varlen():
+    """P6d: packed sequences of different lengths -- each sequence against the
+    mpmath brute force on its own rows only (no key of another sequence may
+    contribute), for no mask, top-left and bottom-right causal.  Lengths cover
+    empty query sets, empty key sets (O = 0, lse = -inf), L_q < L_k and L_q > L_k."""
+    rng = np.random.default_rng(63)
+    Hq, Hkv, D = 4, 2, 3
+    lens = [(3, 3), (0, 2), (4, 0), (2, 6), (5, 2), (1, 1)]
+    cq = np.concatenate([[0], np.cumsum([a for a, _ in lens])])
+    ck = np.concatenate([[0], np.cumsum([b for _, b in lens])])
+    q, k, v = _rand(rng, int(cq[-1]), Hq, D), _rand(rng, int(ck[-1]), Hkv, D), _rand(rng, int(ck[-1]), Hkv, D)
+    for causal, br in ((False, False), (True, False), (True, True)):
+        O, lse = OA.attention_varlen(q, k, v, cq, ck, 0.8, causal, bottom_right=br)
+        assert O.shape == q.shape and lse.shape == (Hq, q.shape[0])
+        for b, (Lq, Lk) in enumerate(lens):
+            rq, rk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+            if Lq == 0:
+                continue
+            if Lk == 0:
+                assert np.all(O[rq] == 0.0) and np.all(lse[:, rq] == -np.inf)
+                continue
+            qs, ks, vs = (x.transpose(1, 0, 2)[None] for x in (q[rq], k[rk], v[rk]))
+            Ob, lseb = _brute(qs, ks, vs, 0.8, causal, offset=(Lk - Lq) if br else 0)
+            np.testing.assert_allclose(O[rq], Ob[0].transpose(1, 0, 2), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[:, rq], lseb[0], rtol=1e-12, atol=1e-12)
+    # sampled rows give the same values as the full evaluation (up to the
+    # matmul's blocking over a different number of rows)
+    rows = np.array([0, 2, 7, 9, 13, int(cq[-1]) - 1])
+    Os, ls = OA.attention_varlen(q, k, v, cq, ck, 0.8, True, bottom_right=True, rows=rows)
+    np.testing.assert_allclose(Os, O[rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ls, lse[:, rows], rtol=0, atol=1e-14)
+
+
 def pin_row_sampling_matches_full():
     """Evaluating a subset of rows gives the same values as the full evaluation."""
     rng = np.random.default_rng(11)
@@ -345,6 +378,7 @@ ALL_PINS = [
     pin_linear_in_v,
     pin_causal_row_equals_decode,
     pin_decode_varlen,
+    pin_prefill_varlen,
     pin_row_sampling_matches_full,
     pin_cache_write_touches_only_its_slots,
 ]

@@ -19,6 +19,8 @@ _orig_scores = OA._scores
 _orig_decode = OA.decode
 _orig_write = OA.kv_cache_write
 _orig_varlen = OA.decode_varlen
+_orig_bounds = OA.sequence_bounds
+_orig_vcoff = OA.varlen_causal_offset
 
 
 def _vis_strict(q_pos, Nkv, causal, offset=0):
@@ -97,6 +99,26 @@ def _varlen_off_by_one(q, k_cache, v_cache, cache_lens, scale):
     return _orig_varlen(q, k_cache, v_cache, [min(int(x) + 1, S) for x in cache_lens], scale)
 
 
+def _bounds_from_zero(cu_seqlens, b):
+    # every sequence starts at packed row 0 (offsets read as lengths)
+    _, e = _orig_bounds(cu_seqlens, b)
+    return 0, e - _orig_bounds(cu_seqlens, b)[0]
+
+
+def _bounds_one_past(cu_seqlens, b):
+    s, e = _orig_bounds(cu_seqlens, b)
+    n = int(np.asarray(cu_seqlens).reshape(-1)[-1])
+    return s, min(e + 1, n) if e > s else e
+
+
+def _vcoff_swapped(Lq, Lk, bottom_right):
+    return _orig_vcoff(Lk, Lq, bottom_right)
+
+
+def _vcoff_always_top_left(Lq, Lk, bottom_right):
+    return 0
+
+
 def _write_shifted(k_cache, v_cache, k_new, v_new, pos):
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
@@ -124,6 +146,10 @@ MUTATIONS = {
     "cache_write_off_by_one": ("kv_cache_write", _write_shifted),
     "varlen_longest_for_all": ("decode_varlen", _varlen_longest_for_all),
     "varlen_reads_one_more": ("decode_varlen", _varlen_off_by_one),
+    "packed_offsets_as_lengths": ("sequence_bounds", _bounds_from_zero),
+    "packed_row_past_sequence": ("sequence_bounds", _bounds_one_past),
+    "packed_causal_offset_swapped": ("varlen_causal_offset", _vcoff_swapped),
+    "packed_bottom_right_ignored": ("varlen_causal_offset", _vcoff_always_top_left),
 }
 
 
