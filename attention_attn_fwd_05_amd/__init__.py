@@ -9,6 +9,8 @@ every call raises.
 Entry points (same names as the C ABI):
 
 * ``attn_fwd(q, k, v, *, causal, scale=None, return_lse=False, out=None)``
+* ``attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, *,
+  causal, ...)`` (packed sequences of different lengths, offsets on the device)
 * ``attn_decode(q, k_cache, v_cache, cache_len, *, scale=None, workspace=None,
   num_splits=0, return_lse=False, out=None)``
 * ``attn_decode_varlen(q, k_cache, v_cache, cache_lens, max_cache_len=None, ...)``
@@ -25,6 +27,7 @@ from ._binding import (  # noqa: F401
     attn_decode_varlen,
     attn_decode_workspace_bytes,
     attn_fwd,
+    attn_fwd_varlen,
     decode_workspace,
     kv_cache_write,
     lib_path,
@@ -35,6 +38,7 @@ __all__ = [
     "AttnError",
     "Status",
     "attn_fwd",
+    "attn_fwd_varlen",
     "attn_decode",
     "attn_decode_varlen",
     "attn_decode_workspace_bytes",

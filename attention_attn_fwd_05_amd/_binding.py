@@ -51,6 +51,9 @@ def load_library():
     vp, i32, f32, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, Strides
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, S, S, S, S, f32,
+                                    i32, i32, vp]
+    lib.attn_fwd_varlen.restype = i32
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32,
@@ -138,6 +141,61 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool,
                       B, Hq, Hkv, Nq, Nkv, D, _strides4(q), _strides4(k), _strides4(v), _strides4(out),
                       s, _CAUSAL_ALIGN[causal_align] if causal else 0, code, _stream(q))
     _check(st, "attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def _strides_packed(t: torch.Tensor) -> Strides:
+    s = t.stride()
+    return Strides(0, s[1], s[0], s[2])
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int | None = None, *, causal: bool,
+                    scale: float | None = None, return_lse: bool = False, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | None = None, causal_align: str = "top_left"):
+    """Fused attention forward over packed sequences of different lengths.
+
+    q (total_q, Hq, D), k/v (total_k, Hkv, D), any strides with stride(-1) == 1;
+    cu_seqlens_q / cu_seqlens_k: int32 (B + 1,) device offsets (sequence b owns
+    rows [cu[b], cu[b+1])).  ``max_seqlen_q`` bounds every sequence's query
+    count; when None it is read from ``cu_seqlens_q`` (a device-to-host copy).
+    ``causal_align`` is per sequence ("bottom_right": j <= i + L_k - L_q).
+    Returns ``out`` (total_q, Hq, D), or ``(out, lse)`` with lse fp32 (Hq, total_q).
+    """
+    if causal_align not in _CAUSAL_ALIGN:
+        raise ValueError("causal_align must be 'top_left' or 'bottom_right'")
+    lib = load_library()
+    Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if k.shape != v.shape or k.shape[2] != D:
+        raise ValueError("shape mismatch between q, k and v")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    B = cu_seqlens_q.shape[0] - 1
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B > 0 else 0
+        max_seqlen_q = max(max_seqlen_q, 1)
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape (Hq, total_q)")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _on_gpu(q, k, v, out, cu_seqlens_q, cu_seqlens_k, *([lse] if lse is not None else []))
+    code = _dtype_code(q, k, v, out)
+    s = _default_scale(D) if scale is None else float(scale)
+    st = lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None,
+                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, int(max_seqlen_q), Tq, Tk,
+                             Hq, Hkv, D, _strides_packed(q), _strides_packed(k), _strides_packed(v),
+                             _strides_packed(out), s, _CAUSAL_ALIGN[causal_align] if causal else 0, code,
+                             _stream(q))
+    _check(st, "attn_fwd_varlen")
     return (out, lse) if return_lse else out
 
 

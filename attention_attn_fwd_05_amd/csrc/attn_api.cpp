@@ -132,7 +132,66 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   a.k_bytes = slice_bytes(Nkv, sk.n, D);
   a.v_bytes = slice_bytes(Nkv, sv.n, D);
 
-  const hipError_t e = attn::launch_prefill(a, D, dtype == ATTN_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  a.units = B * Hkv;
+
+  const hipError_t e =
+      attn::launch_prefill(a, D, dtype == ATTN_BF16, causal != 0, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int max_seqlen_q,
+                            int total_q, int total_k, int Hq, int Hkv, int D,
+                            attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            float scale, int causal, attn_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seqlen_q <= 0 || total_q <= 0 || total_k < 0 || D <= 0)
+    return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (causal < ATTN_CAUSAL_NONE || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_ERR_UNSUPPORTED;
+  // packed (token, head, dim) views: the batch stride is unused and not checked
+  attn_strides sq3 = sq, sk3 = sk, sv3 = sv, so3 = so;
+  sq3.b = sk3.b = sv3.b = so3.b = 0;
+  if (!strides_ok(sq3) || !strides_ok(sk3) || !strides_ok(sv3) || !strides_ok(so3)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return ATTN_ERR_UNSUPPORTED;
+  if (sq.n > kMaxRowStride || sk.n > kMaxRowStride || sv.n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
+  const int64_t nqb = ((int64_t)max_seqlen_q + kPrefillRows - 1) / kPrefillRows;
+  const int64_t units = (int64_t)B * Hkv;
+  const int64_t group = Hq / Hkv;
+  // units rounded up to a multiple of the 8 XCDs (the extra workgroups exit)
+  const int64_t nblocks = (units + 7) / 8 * 8 * group * nqb;
+  if (nblocks > INT_MAX) return ATTN_ERR_SHAPE;
+
+  attn::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.sqh = sq.h; a.sqn = sq.n;
+  a.skh = sk.h; a.skn = sk.n;
+  a.svh = sv.h; a.svn = sv.n;
+  a.soh = so.h; a.son = so.n;
+  a.Hq = Hq; a.Hkv = Hkv; a.group = (int)group;
+  a.Nq = max_seqlen_q;  // per-sequence query rows are capped at this bound
+  a.nqb = (int)nqb;
+  a.nblocks = (int)nblocks;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.units = (int)units;
+  a.causal_br = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? 1 : 0;
+  a.c = score_coef(scale);
+  a.qsign = q_sign_mask(scale);
+
+  const hipError_t e =
+      attn::launch_prefill(a, D, dtype == ATTN_BF16, causal != 0, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

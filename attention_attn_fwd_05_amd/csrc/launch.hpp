@@ -28,9 +28,17 @@ struct FwdArgs {
   // bytes from a (batch, head) slice's first element to the end of its last
   // valid row: buffer loads at or past this offset read zeros
   int64_t q_bytes, k_bytes, v_bytes;
+  // packed variable-length batches (null otherwise): sequence b owns query
+  // rows [cu_q[b], cu_q[b+1]) of total_q and key rows [cu_k[b], cu_k[b+1]) of
+  // total_k; lse is then (Hq, total_q)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
+  int units;      // B * Hkv
+  int causal_br;  // causal offset per sequence: 1 = L_k - L_q, 0 = 0
 };
 
-hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool varlen, hipStream_t stream);
 
 struct DecodeArgs {
   const uint16_t* q;

@@ -167,7 +167,7 @@ __device__ __forceinline__ void barrier_nofence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdArgs a) {
   using L = PrefillLds<D>;
   constexpr int KS = D / 16;        // k-steps of the score MFMA
@@ -179,11 +179,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
 
   // ---- which (batch, q head, query block) this workgroup owns
   const int bid = blockIdx.x;
-  int lid = bid;
-  if (a.remap) lid = (bid & 7) * (a.nblocks >> 3) + (bid >> 3);  // keep a kv head's blocks on one XCD
   const int per_unit = a.group * a.nqb;
-  const int unit = lid / per_unit;
-  const int rem = lid - unit * per_unit;
+  int unit, rem;
+  if constexpr (VARLEN) {
+    // (batch, kv head) units dealt round-robin to the 8 XCDs (workgroup i
+    // runs on XCD i % 8), each unit's blocks on one XCD, latest query block
+    // first: with Hkv a multiple of 8 every XCD holds the same kv head of
+    // every sequence, so the XCDs stay balanced whatever the lengths.
+    // (Ordering an XCD's blocks by query-block rank across all its units
+    // measured no faster.)
+    const int r = (bid >> 3) / per_unit;
+    unit = (bid & 7) + 8 * r;
+    rem = (bid >> 3) - r * per_unit;
+    if (unit >= a.units) return;  // whole workgroup: the grid rounds units up to 8
+  } else {
+    int lid = bid;
+    if (a.remap) lid = (bid & 7) * (a.nblocks >> 3) + (bid >> 3);  // keep a kv head's blocks on one XCD
+    unit = lid / per_unit;
+    rem = lid - unit * per_unit;
+  }
   int qb = rem / a.group;
   const int hg = rem - qb * a.group;
   if (CAUSAL) qb = a.nqb - 1 - qb;  // longest (latest) query blocks first
@@ -199,27 +213,58 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   const int q0 = qb * kBM;
   const int qrow = q0 + 32 * w + n;
 
+  // ---- this (batch, head) slice: its rows, first elements and valid bytes.
+  //      A packed sequence's offsets are clamped into [previous offset, total],
+  //      so no access leaves the packed tensors whatever the offsets hold.
+  int Nq = a.Nq, Nkv = a.Nkv;
+  int off = CAUSAL ? a.causal_off : 0;
+  const uint16_t *qbase, *kbase, *vbase;
+  uint16_t* obase;
+  float* lbase;
+  int64_t q_bytes = a.q_bytes, k_bytes = a.k_bytes, v_bytes = a.v_bytes;
+  if constexpr (VARLEN) {
+    const int t0 = min(max(a.cu_q[b], 0), a.total_q);
+    const int t1 = min(max(a.cu_q[b + 1], t0), a.total_q);
+    const int s0 = min(max(a.cu_k[b], 0), a.total_k);
+    const int s1 = min(max(a.cu_k[b + 1], s0), a.total_k);
+    Nq = t1 - t0;
+    Nkv = s1 - s0;
+    if (CAUSAL) off = a.causal_br ? Nkv - Nq : 0;  // from the sequence's own lengths
+    Nq = min(Nq, a.Nq);    // rows past the caller's max_seqlen_q bound are not computed
+    if (q0 >= Nq) return;  // whole workgroup: block past this sequence's queries
+    qbase = a.q + (int64_t)t0 * a.sqn + (int64_t)h * a.sqh;
+    kbase = a.k + (int64_t)s0 * a.skn + (int64_t)kvh * a.skh;
+    vbase = a.v + (int64_t)s0 * a.svn + (int64_t)kvh * a.svh;
+    obase = a.o + (int64_t)t0 * a.son + (int64_t)h * a.soh;
+    lbase = a.lse ? a.lse + (int64_t)h * a.total_q + t0 : nullptr;
+    q_bytes = ((int64_t)(Nq - 1) * a.sqn + D) * 2;
+    k_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.skn + D) * 2 : 0;
+    v_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.svn + D) * 2 : 0;
+  } else {
+    qbase = a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh;
+    kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
+    vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
+    obase = a.o + (int64_t)b * a.sob + (int64_t)h * a.soh;
+    lbase = a.lse ? a.lse + ((int64_t)b * a.Hq + h) * a.Nq : nullptr;
+  }
+
   // ---- Q fragment, register resident: B operand of S^T = K Q^T (rows >= Nq read as 0)
   u32x4 qf[KS];
   {
     const int64_t qblk = (int64_t)q0 * a.sqn;
-    const auto rq = make_rsrc(a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh + qblk,
-                              clamp_bytes(a.q_bytes - 2 * qblk));
+    const auto rq = make_rsrc(qbase + qblk, clamp_bytes(q_bytes - 2 * qblk));
     const int32_t qoff = (32 * w + n) * (int32_t)a.sqn * 2 + 16 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = bload16(rq, qoff + 32 * ks) ^ a.qsign;
   }
 
-  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
-  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
   // causal: query row i sees keys j <= i + off (off = 0 top-left, Nkv - Nq
   // bottom-right); keys past the block's last row + off are never visited
-  const int off = CAUSAL ? a.causal_off : 0;
-  const int kv_end = CAUSAL ? max(0, min(a.Nkv, q0 + kBM + off)) : a.Nkv;
+  const int kv_end = CAUSAL ? max(0, min(Nkv, q0 + kBM + off)) : Nkv;
   const int ntiles = (kv_end + kBN - 1) / kBN;
   // tiles every row of this block sees in full (no mask): below the block's
   // diagonal and before the key tail
-  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, a.Nkv)) / kBN : a.Nkv / kBN;
+  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, Nkv)) / kBN : Nkv / kBN;
 
   // ---- DMA geometry: wave w fills 1 KiB blocks NB*w .. NB*w+NB-1 of each
   //      K and V tile; lane l of block bk writes row RPB*bk + l/C, slot l%C,
@@ -237,8 +282,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   const uint32_t lds_v = lds_addr(smem + L::V0) + 1024 * NB * w;
   auto dma_tile = [&](int t, int stage) {
     const int64_t ko = (int64_t)t * kBN * a.skn, vo = (int64_t)t * kBN * a.svn;
-    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
-    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
+    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(k_bytes - 2 * ko));
+    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(v_bytes - 2 * vo));
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma16(rk, lds_k + 2 * stage * L::TILE + 1024 * i, dk[i]);
 #pragma unroll
@@ -309,8 +354,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
     const int kb = t * kBN;
     bool act1 = true;
     if constexpr (MASKED) {
-      if (kb >= a.Nkv || (CAUSAL && kb > wq_hi)) return;  // whole tile above this wave's rows
-      act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi);
+      if (kb >= Nkv || (CAUSAL && kb > wq_hi)) return;  // whole tile above this wave's rows
+      act1 = kb + 32 < Nkv && (!CAUSAL || kb + 32 <= wq_hi);
     }
     // S^T = K Q^T for the two 32-key subtiles; score register e of lane
     // (n, hh) is key 8*(e/4) + 4*hh + e%4 of its subtile
@@ -331,8 +376,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
       for (int e = 0; e < 16; ++e) {
         const int kv0 = kb + 8 * (e >> 2) + 4 * hh + (e & 3);
         const int kv1 = kv0 + 32;
-        const bool vis0 = kv0 < a.Nkv && (!CAUSAL || kv0 <= qrow + off);
-        const bool vis1 = act1 && kv1 < a.Nkv && (!CAUSAL || kv1 <= qrow + off);
+        const bool vis0 = kv0 < Nkv && (!CAUSAL || kv0 <= qrow + off);
+        const bool vis1 = act1 && kv1 < Nkv && (!CAUSAL || kv1 <= qrow + off);
         s0[e] = vis0 ? s0[e] : -INFINITY;
         s1[e] = vis1 ? s1[e] : -INFINITY;
       }
@@ -441,9 +486,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
 
   // ---- epilogue: O = O^T / l, cast, store; lse = (m + log2 l) ln 2
   l = sum_xor32(l);
-  if (qrow < a.Nq) {
+  if (qrow < Nq) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    uint16_t* op = a.o + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)qrow * a.son;
+    uint16_t* op = obase + (int64_t)qrow * a.son;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -454,32 +499,36 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
         *reinterpret_cast<u32x2*>(op + d) = v2;
       }
     }
-    if (a.lse != nullptr && hh == 0)
-      a.lse[((int64_t)b * a.Hq + h) * a.Nq + qrow] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    if (lbase != nullptr && hh == 0) lbase[qrow] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL>), dim3(a.nblocks), dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, VARLEN>), dim3(a.nblocks), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool VARLEN>
 hipError_t launch_c(const FwdArgs& a, bool causal, hipStream_t stream) {
-  return causal ? launch_t<D, BF16, true>(a, stream) : launch_t<D, BF16, false>(a, stream);
+  return causal ? launch_t<D, BF16, true, VARLEN>(a, stream) : launch_t<D, BF16, false, VARLEN>(a, stream);
 }
 
-template <int D>
+template <int D, bool VARLEN>
 hipError_t launch_d(const FwdArgs& a, bool bf16, bool causal, hipStream_t stream) {
-  return bf16 ? launch_c<D, true>(a, causal, stream) : launch_c<D, false>(a, causal, stream);
+  return bf16 ? launch_c<D, true, VARLEN>(a, causal, stream) : launch_c<D, false, VARLEN>(a, causal, stream);
+}
+
+template <bool VARLEN>
+hipError_t launch_v(const FwdArgs& a, int D, bool bf16, bool causal, hipStream_t stream) {
+  if (D == 64) return launch_d<64, VARLEN>(a, bf16, causal, stream);
+  return launch_d<128, VARLEN>(a, bf16, causal, stream);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, hipStream_t stream) {
-  if (D == 64) return launch_d<64>(a, bf16, causal, stream);
-  return launch_d<128>(a, bf16, causal, stream);
+hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool varlen, hipStream_t stream) {
+  return varlen ? launch_v<true>(a, D, bf16, causal, stream) : launch_v<false>(a, D, bf16, causal, stream);
 }
 
 }  // namespace attn

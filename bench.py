@@ -26,10 +26,11 @@ FETCH_SIZE and WRITE_SIZE counters measured (scaled by a plain copy's reading),
 taken from the committed summaries under profiles/; null once the kernel
 sources differ from the ones those counters were taken with.
 
-The default run also times two widened workloads (not the headline):
-decode with per-sequence cache lengths over a 16-sequence batch, and a
-chunked prefill (1024 queries at the end of an 8192-token context, causal
-aligned bottom-right); they are printed under "widened".
+The default run also times three widened workloads (not the headline):
+decode with per-sequence cache lengths over a 16-sequence batch, a chunked
+prefill (1024 queries at the end of an 8192-token context, causal aligned
+bottom-right) and a packed prefill of 16 sequences of seeded lengths up to
+4096; they are printed under "widened".
 
 Flags: --only prefill|decode|copy runs just that launch (for rocprofv3 runs),
 --no-cpu skips the oracle baseline.  Prints one JSON line.
@@ -297,6 +298,27 @@ def main():
             "tflops": round(cflops / (ct_ * 1e-3) / 1e12, 1),
             "frac_of_2500_tflops": round(cflops / (ct_ * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
         del cq, ck, cv, co
+        vp = W.varlen_serving_case()
+        pq, pk, pv = (t.to(dev) for t in W.varlen_prefill_inputs(vp))
+        pcq = torch.tensor(vp.cu_q, dtype=torch.int32, device=dev)
+        pck = torch.tensor(vp.cu_k, dtype=torch.int32, device=dev)
+        po = torch.empty_like(pq)
+        for _ in range(3):
+            A.attn_fwd_varlen(pq, pk, pv, pcq, pck, vp.max_q, causal=True, scale=vp.softmax_scale, out=po)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0.record(stream)
+        for _ in range(10):
+            A.attn_fwd_varlen(pq, pk, pv, pcq, pck, vp.max_q, causal=True, scale=vp.softmax_scale, out=po)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pt = e0.elapsed_time(e1) / 10
+        widened["prefill_varlen"] = {
+            "workload": vp.name, "sequences": vp.B, "Hq": vp.Hq, "Hkv": vp.Hkv, "D": vp.D, "causal": "top_left",
+            "lengths": "seeded uniform [1, 4096]", "total_tokens": vp.total_q, "flops_per_launch": vp.flops(),
+            "ms_per_launch": round(pt, 4), "tflops": round(vp.flops() / (pt * 1e-3) / 1e12, 1),
+            "frac_of_2500_tflops": round(vp.flops() / (pt * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+        del pq, pk, pv, po
 
     # context: achievable HBM rate of a plain 256 MiB device copy (read + write)
     copy_gbs = None

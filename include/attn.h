@@ -91,6 +91,43 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      float scale, int causal, attn_dtype dtype, void* stream);
 
 /*
+ * attn_fwd_varlen -- attn_fwd over a batch of packed sequences of different
+ * lengths: sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and
+ * key/value rows [cu_seqlens_k[b], cu_seqlens_k[b+1]) of the packed tensors,
+ * and attends only to its own keys.  Within a sequence the operation is that of
+ * attn_fwd ([P1] "Required reasoning process" steps 1-9, [P2] "Online
+ * Softmax", [P3] GQA design); the packed variable-length batch itself is the
+ * widening that [P3]'s deferred scope names (varlen).
+ *
+ *   q    (total_q, Hq,  D): row t of head h at q[t*sq.n + h*sq.h + d]  (sq.b unused)
+ *   k, v (total_k, Hkv, D) via sk, sv (b unused)
+ *   o    (total_q, Hq,  D) via so (b unused); written, same dtype as q
+ *   lse  nullable; if given, contiguous fp32 (Hq, total_q): lse[h*total_q + t]
+ *   cu_seqlens_q, cu_seqlens_k: DEVICE int32 arrays of B + 1 offsets, expected
+ *        non-decreasing from 0 to total_q (total_k).  They are read on the GPU
+ *        (no host synchronisation); each offset is clamped into [previous
+ *        offset, total], so malformed offsets give empty or shortened sequences
+ *        but never an access outside the packed tensors.
+ *   max_seqlen_q: host bound on the query rows of any sequence; sizes the grid
+ *        (ceil(max_seqlen_q/256) query blocks per (sequence, head)).  Query
+ *        rows at positions >= max_seqlen_q within a sequence are not computed
+ *        and their o rows and lse entries are left untouched; the mask of the
+ *        rows computed is still that of the whole sequence.
+ *   causal: as attn_fwd, per sequence: ATTN_CAUSAL_TOP_LEFT (j <= i) or
+ *        ATTN_CAUSAL_BOTTOM_RIGHT (j <= i + L_k - L_q with the sequence's own
+ *        lengths).  A row with no visible key (a sequence with L_k = 0, or the
+ *        first L_q - L_k rows bottom-right) gets o = 0 and lse = -inf.
+ *   B >= 1, max_seqlen_q >= 1, total_q >= 1, total_k >= 0; D in {64, 128};
+ *   strides, alignment and dtype rules as attn_fwd; the offset arrays must be
+ *   4-byte aligned.
+ */
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int max_seqlen_q,
+                            int total_q, int total_k, int Hq, int Hkv, int D,
+                            attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode needs
  * for a cache of S_max slots (covers every cache_len <= S_max and every split
  * count): U * min(64, ceil(S_max/128)) * ceil(G/ceil(G/16)) * (D + 4) * 4

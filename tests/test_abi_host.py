@@ -42,8 +42,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_decode", "attn_decode_varlen", "attn_decode_workspace_bytes",
-                          "kv_cache_write", "attn_status_string"}
+    assert set(names) == {"attn_fwd", "attn_fwd_varlen", "attn_decode", "attn_decode_varlen",
+                          "attn_decode_workspace_bytes", "kv_cache_write", "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -81,6 +81,31 @@ def fwd(lib, **kw):
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
+
+
+def fwdv(lib, **kw):
+    Hq, Hkv, D = 8, 2, 128
+    pk = lambda H: S(0, D, H * D, 1)  # packed (token, head, dim)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cq=FAKE, ck=FAKE, B=3, msq=300, tq=700, tk=900,
+             Hq=Hq, Hkv=Hkv, D=D, sq=pk(Hq), sk=pk(Hkv), sv=pk(Hkv), so=pk(Hq), scale=0.088, causal=2, dtype=0,
+             stream=None)
+    a.update(kw)
+    return lib.attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"], a["msq"],
+                               a["tq"], a["tk"], a["Hq"], a["Hkv"], a["D"], a["sq"], a["sk"], a["sv"], a["so"],
+                               a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(cq=None), NULL), (dict(ck=None), NULL),
+    (dict(B=0), SHAPE), (dict(msq=0), SHAPE), (dict(tq=0), SHAPE), (dict(tk=-1), SHAPE), (dict(Hq=7), SHAPE),
+    (dict(D=80), UNSUP), (dict(dtype=3), UNSUP), (dict(causal=3), UNSUP), (dict(scale=float("inf")), UNSUP),
+    (dict(cq=FAKE + 2), UNSUP), (dict(ck=FAKE + 1), UNSUP), (dict(lse=FAKE + 2), UNSUP), (dict(k=FAKE + 8), UNSUP),
+    (dict(sq=S(0, 128, 1024, 2)), UNSUP), (dict(sk=S(0, 128, 260, 1)), UNSUP),
+    (dict(sv=S(0, 128, 1 << 23, 1)), UNSUP),
+    (dict(B=1 << 30, Hkv=8, Hq=64, msq=1 << 20), SHAPE),
+])
+def test_fwd_varlen_rejects(lib, kw, code):
+    assert fwdv(lib, **kw) == code
 
 
 def dec(lib, **kw):

@@ -90,6 +90,75 @@ class DecodeCase:
         return 2 * self.B * self.Hkv * self.cache_len * self.D * es + 2 * self.B * self.Hq * self.D * es
 
 
+@dataclass(frozen=True)
+class VarlenPrefillCase:
+    """A packed batch of sequences with their own query and key lengths."""
+    name: str
+    q_lens: tuple
+    k_lens: tuple
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    causal: bool
+    bottom_right: bool = False
+    seed: int = BASE_SEED
+
+    @property
+    def torch_dtype(self):
+        return _DT[self.dtype]
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.D), dtype=torch.float32).item())
+
+    @property
+    def B(self) -> int:
+        return len(self.q_lens)
+
+    @staticmethod
+    def _cu(lens):
+        out = [0]
+        for L in lens:
+            out.append(out[-1] + int(L))
+        return out
+
+    @property
+    def cu_q(self):
+        return self._cu(self.q_lens)
+
+    @property
+    def cu_k(self):
+        return self._cu(self.k_lens)
+
+    @property
+    def total_q(self) -> int:
+        return sum(self.q_lens)
+
+    @property
+    def total_k(self) -> int:
+        return sum(self.k_lens)
+
+    @property
+    def max_q(self) -> int:
+        return max(max(self.q_lens), 1)
+
+    def visible_pairs_per_head(self) -> int:
+        """(query, key) pairs a head must score, summed over the sequences."""
+        tot = 0
+        for Lq, Lk in zip(self.q_lens, self.k_lens):
+            if not self.causal:
+                tot += Lq * Lk
+                continue
+            off = Lk - Lq if self.bottom_right else 0
+            i = torch.arange(Lq, dtype=torch.int64)
+            tot += int(torch.clamp(i + off + 1, 0, Lk).sum())
+        return tot
+
+    def flops(self) -> int:
+        return 4 * self.D * self.Hq * self.visible_pairs_per_head()
+
+
 def _gen(seed: int) -> torch.Generator:
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
@@ -119,6 +188,17 @@ def decode_inputs(case: DecodeCase):
     kc = torch.randn(case.B, case.Hkv, case.S_max, case.D, generator=g).to(dt)
     vc = torch.randn(case.B, case.Hkv, case.S_max, case.D, generator=g).to(dt)
     return q, kc, vc
+
+
+def varlen_prefill_inputs(case: VarlenPrefillCase):
+    """CPU tensors q (total_q, Hq, D), k, v (total_k, Hkv, D): packed rows, drawn
+    in that order."""
+    g = _gen(case.seed)
+    dt = case.torch_dtype
+    q = torch.randn(case.total_q, case.Hq, case.D, generator=g).to(dt)
+    k = torch.randn(case.total_k, case.Hkv, case.D, generator=g).to(dt)
+    v = torch.randn(case.total_k, case.Hkv, case.D, generator=g).to(dt)
+    return q, k, v
 
 
 # ---- the pages' workloads -------------------------------------------------
@@ -180,6 +260,15 @@ def bottom_right_pairs(Nq: int, Nkv: int) -> int:
     """Visible (query, key) pairs per head of a bottom-right causal mask."""
     off = Nkv - Nq
     return sum(max(0, min(Nkv, i + off + 1)) for i in range(Nq))
+
+
+def varlen_serving_case():
+    """Packed serving batch: 16 sequences with seeded lengths uniform in
+    [1, 4096] (queries = keys), Hq=32, Hkv=8, D=128, fp16, causal."""
+    g = _gen(BASE_SEED + 40 + 1000)
+    lens = tuple(int(x) for x in torch.randint(1, 4097, (16,), generator=g))
+    return VarlenPrefillCase("varlen_b16_upto4096_d128_fp16_causal", lens, lens, 32, 8, 128, "fp16", True,
+                             seed=BASE_SEED + 40)
 
 
 AR_TOKENS = 512
