@@ -9,9 +9,13 @@ from .attention import (  # noqa: F401
     attention_probs,
     attention_varlen,
     decode,
+    decode_paged,
     decode_varlen,
+    gather_pages,
     kv_cache_write,
+    kv_cache_write_paged,
     kv_head_of,
+    page_slot,
     sequence_bounds,
     varlen_causal_offset,
     visibility,

@@ -47,6 +47,11 @@ Readings taken where the pages leave a step open (each also listed in the design doc)
   element b its own ``cache_lens[b]``; a length of 0 leaves no visible key.
 * GQA maps q head h to kv head h // group, i.e. repeat_interleave expansion of
   K/V, not tiling ([P1] step 1; [P3] GQA phase).
+* Paged KV cache (the pages' deferred scope item): cache slot r of sequence b
+  lives in page ``block_table[b, r // page_size]``, row ``r % page_size``, of
+  the page pools (num_pages, Hkv, page_size, D).  Decode over a paged cache is
+  the per-sequence-length decode on the rows so gathered; the paged writer
+  stores new rows at slots pos[b], pos[b] + 1, ... of each sequence.
 * Packed variable-length prefill (the pages' deferred "varlen" scope item):
   sequence b owns the packed query rows [cu_q[b], cu_q[b+1]) and key rows
   [cu_k[b], cu_k[b+1]); attention never crosses sequences, and each sequence
@@ -73,6 +78,10 @@ __all__ = [
     "varlen_causal_offset",
     "attention_varlen",
     "kv_cache_write",
+    "page_slot",
+    "gather_pages",
+    "decode_paged",
+    "kv_cache_write_paged",
 ]
 
 
@@ -298,3 +307,61 @@ def kv_cache_write(k_cache, v_cache, k_new, v_new, pos: int):
     kc[:, :, pos:pos + T] = k_new
     vc[:, :, pos:pos + T] = v_new
     return kc, vc
+
+
+def page_slot(block_table, b: int, r: int, page_size: int):
+    """(page, row) that hold cache slot r of sequence b in a paged cache."""
+    return int(np.asarray(block_table)[b, r // page_size]), r % page_size
+
+
+def gather_pages(pages, block_table, b: int, length: int, page_size: int) -> np.ndarray:
+    """Sequence b's first ``length`` cache slots as a contiguous (Hkv, length, D) array."""
+    pages = np.asarray(pages)
+    out = np.zeros((pages.shape[1], length, pages.shape[3]), dtype=pages.dtype)
+    for r in range(length):
+        p, i = page_slot(block_table, b, r, page_size)
+        out[:, r] = pages[p, :, i]
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, cache_lens, page_size: int, scale: float):
+    """O2 over a paged cache: ``decode_varlen`` on each sequence's gathered slots.
+
+    q: (B, Hq, D); k_pages, v_pages: (num_pages, Hkv, page_size, D); block_table:
+    (B, max_pages) page ids; cache_lens: B lengths in [0, max_pages * page_size].
+    Returns O (B, Hq, D) and lse (B, Hq), float64 (length 0: O = 0, lse = -inf).
+    """
+    q = _f64(q)
+    lens = [int(x) for x in np.asarray(cache_lens).reshape(-1)]
+    B = q.shape[0]
+    tbl = np.asarray(block_table)
+    if len(lens) != B or tbl.shape[0] != B or any(L < 0 or L > tbl.shape[1] * page_size for L in lens):
+        raise ValueError("cache_lens must hold B values within the block table's pages")
+    S = max(max(lens), 1)
+    Hkv, D = np.asarray(k_pages).shape[1], np.asarray(k_pages).shape[3]
+    kc = np.zeros((B, Hkv, S, D))
+    vc = np.zeros((B, Hkv, S, D))
+    for b, L in enumerate(lens):
+        kc[b, :, :L] = gather_pages(k_pages, tbl, b, L, page_size)
+        vc[b, :, :L] = gather_pages(v_pages, tbl, b, L, page_size)
+    return decode_varlen(q, kc, vc, lens, scale)
+
+
+def kv_cache_write_paged(k_pages, v_pages, k_new, v_new, block_table, pos, page_size: int):
+    """O3 over a paged cache: copies of the pools with sequence b's slots
+    pos[b] .. pos[b] + T - 1 replaced by its T new rows (B, Hkv, T, D); every
+    other element is left bit-for-bit unchanged."""
+    kp = np.array(k_pages, copy=True)
+    vp = np.array(v_pages, copy=True)
+    kn, vn = np.asarray(k_new), np.asarray(v_new)
+    tbl = np.asarray(block_table)
+    B, _, T, _ = kn.shape
+    for b in range(B):
+        p0 = int(np.asarray(pos).reshape(-1)[b])
+        if p0 < 0 or p0 + T > tbl.shape[1] * page_size:
+            raise ValueError("write outside the sequence's pages")
+        for t in range(T):
+            pg, i = page_slot(tbl, b, p0 + t, page_size)
+            kp[pg, :, i] = kn[b, :, t]
+            vp[pg, :, i] = vn[b, :, t]
+    return kp, vp

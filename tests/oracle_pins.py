@@ -303,6 +303,64 @@ def pin_decode_varlen():
     np.testing.assert_array_equal(lsee, lsed)
 
 
+def _scatter_to_pages(cache, perm, page_size):
+    """Independent scatter of contiguous (B, Hkv, S, D) caches into a page pool:
+    page perm[b * (S // page_size) + j] holds slots [j * ps, (j + 1) * ps) of sequence b."""
+    B, H, S, D = cache.shape
+    npb = S // page_size
+    blocks = cache.reshape(B, H, npb, page_size, D).transpose(0, 2, 1, 3, 4).reshape(B * npb, H, page_size, D)
+    pool = np.full((len(perm) + 3, H, page_size, D), np.nan)  # spare pages stay NaN
+    pool[perm] = blocks
+    table = np.asarray(perm).reshape(B, npb)
+    return pool, table
+
+
+def pin_decode_paged():
+    """P10c: a paged cache scattered from contiguous caches through a shuffled
+    block table decodes exactly like the per-sequence-length decode of the
+    contiguous caches, and each sequence matches the mpmath brute force; the
+    spare pages (NaN) are never read."""
+    rng = np.random.default_rng(102)
+    B, Hq, Hkv, S, D, ps = 3, 4, 2, 12, 5, 4
+    q, kc, vc = _rand(rng, B, Hq, D), _rand(rng, B, Hkv, S, D), _rand(rng, B, Hkv, S, D)
+    perm = rng.permutation(B * (S // ps))
+    kp, tbl = _scatter_to_pages(kc, perm, ps)
+    vp, _ = _scatter_to_pages(vc, perm, ps)
+    lens = [7, 0, 12]
+    O, lse = OA.decode_paged(q, kp, vp, tbl, lens, ps, 0.6)
+    Ov, lsev = OA.decode_varlen(q, kc, vc, lens, 0.6)
+    np.testing.assert_array_equal(O, Ov)
+    np.testing.assert_array_equal(lse, lsev)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(O[b] == 0.0) and np.all(lse[b] == -np.inf)
+            continue
+        Ob, lseb = _brute(q[b:b + 1, :, None, :], kc[b:b + 1, :, :L], vc[b:b + 1, :, :L], 0.6, False)
+        np.testing.assert_allclose(O[b], Ob[0, :, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], lseb[0, :, 0], rtol=1e-12, atol=1e-12)
+
+
+def pin_cache_write_paged():
+    """P10d: the paged writer equals the contiguous writer applied per sequence
+    (at that sequence's position) and scattered through the same block table."""
+    rng = np.random.default_rng(103)
+    B, Hkv, S, D, ps, T = 3, 2, 16, 3, 4, 3
+    kc, vc = _rand(rng, B, Hkv, S, D), _rand(rng, B, Hkv, S, D)
+    kn, vn = _rand(rng, B, Hkv, T, D), _rand(rng, B, Hkv, T, D)
+    perm = rng.permutation(B * (S // ps))
+    kp, tbl = _scatter_to_pages(kc, perm, ps)
+    vp, _ = _scatter_to_pages(vc, perm, ps)
+    pos = [0, 5, S - T]
+    kp2, vp2 = OA.kv_cache_write_paged(kp, vp, kn, vn, tbl, pos, ps)
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in range(B):
+        kc2[b:b + 1], vc2[b:b + 1] = OA.kv_cache_write(kc[b:b + 1], vc[b:b + 1], kn[b:b + 1], vn[b:b + 1], pos[b])
+    ke, _ = _scatter_to_pages(kc2, perm, ps)
+    ve, _ = _scatter_to_pages(vc2, perm, ps)
+    np.testing.assert_array_equal(kp2, ke)
+    np.testing.assert_array_equal(vp2, ve)
+
+
 def pin_prefill_varlen():
     """P6d: packed sequences of different lengths -- each sequence against the
     mpmath brute force on its own rows only (no key of another sequence may
@@ -379,6 +437,8 @@ ALL_PINS = [
     pin_causal_row_equals_decode,
     pin_decode_varlen,
     pin_prefill_varlen,
+    pin_decode_paged,
+    pin_cache_write_paged,
     pin_row_sampling_matches_full,
     pin_cache_write_touches_only_its_slots,
 ]

@@ -21,6 +21,7 @@ _orig_write = OA.kv_cache_write
 _orig_varlen = OA.decode_varlen
 _orig_bounds = OA.sequence_bounds
 _orig_vcoff = OA.varlen_causal_offset
+_orig_pslot = OA.page_slot
 
 
 def _vis_strict(q_pos, Nkv, causal, offset=0):
@@ -119,6 +120,20 @@ def _vcoff_always_top_left(Lq, Lk, bottom_right):
     return 0
 
 
+def _pslot_row_and_page_swapped(block_table, b, r, page_size):
+    return int(np.asarray(block_table)[b, r % page_size]), r // page_size
+
+
+def _pslot_next_sequence(block_table, b, r, page_size):
+    tbl = np.asarray(block_table)
+    return _orig_pslot(tbl, (b + 1) % tbl.shape[0], r, page_size)
+
+
+def _pslot_row_off_by_one(block_table, b, r, page_size):
+    p, i = _orig_pslot(block_table, b, r, page_size)
+    return p, (i + 1) % page_size
+
+
 def _write_shifted(k_cache, v_cache, k_new, v_new, pos):
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
@@ -146,6 +161,9 @@ MUTATIONS = {
     "cache_write_off_by_one": ("kv_cache_write", _write_shifted),
     "varlen_longest_for_all": ("decode_varlen", _varlen_longest_for_all),
     "varlen_reads_one_more": ("decode_varlen", _varlen_off_by_one),
+    "paged_row_and_page_swapped": ("page_slot", _pslot_row_and_page_swapped),
+    "paged_other_sequences_table": ("page_slot", _pslot_next_sequence),
+    "paged_row_off_by_one": ("page_slot", _pslot_row_off_by_one),
     "packed_offsets_as_lengths": ("sequence_bounds", _bounds_from_zero),
     "packed_row_past_sequence": ("sequence_bounds", _bounds_one_past),
     "packed_causal_offset_swapped": ("varlen_causal_offset", _vcoff_swapped),
