@@ -18,18 +18,23 @@ Entry points (same names as the C ABI):
 * ``attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)`` /
   ``decode_workspace(...)`` (a uint8 scratch tensor of that size)
 * ``kv_cache_write(k_cache, v_cache, k_new, v_new, pos)``
+* ``attn_decode_paged(q, k_pages, v_pages, block_table, cache_lens, ...)`` and
+  ``kv_cache_write_paged(k_pages, v_pages, k_new, v_new, block_table, pos)``
+  (a paged KV cache addressed through a device block table)
 """
 
 from ._binding import (  # noqa: F401
     AttnError,
     Status,
     attn_decode,
+    attn_decode_paged,
     attn_decode_varlen,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_varlen,
     decode_workspace,
     kv_cache_write,
+    kv_cache_write_paged,
     lib_path,
     load_library,
 )
@@ -41,6 +46,8 @@ __all__ = [
     "attn_fwd_varlen",
     "attn_decode",
     "attn_decode_varlen",
+    "attn_decode_paged",
+    "kv_cache_write_paged",
     "attn_decode_workspace_bytes",
     "decode_workspace",
     "kv_cache_write",

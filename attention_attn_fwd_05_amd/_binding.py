@@ -62,6 +62,12 @@ def load_library():
     lib.attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, S, S, S, S, f32, i32,
                                        i32, vp, ctypes.c_size_t, vp]
     lib.attn_decode_varlen.restype = i32
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, i32, i32,
+                                      S, S, S, S, f32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_decode_paged.restype = i32
+    lib.kv_cache_write_paged.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, i32, S, S, S, S,
+                                         i32, vp]
+    lib.kv_cache_write_paged.restype = i32
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, i32, vp]
     lib.kv_cache_write.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -301,3 +307,76 @@ def kv_cache_write(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Te
                             _strides4(k_cache), _strides4(v_cache), _strides4(k_new), _strides4(v_new),
                             code, _stream(k_cache))
     _check(st, "kv_cache_write")
+
+
+def _int32_vec(t: torch.Tensor, n: int, what: str):
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{what} must be a contiguous int32 tensor of {n} elements")
+
+
+def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                      cache_lens: torch.Tensor, max_cache_len: int | None = None, *, scale: float | None = None,
+                      workspace: torch.Tensor | None = None, num_splits: int = 0, return_lse: bool = False,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Decode over a paged KV cache.
+
+    q (B, Hq, D); k_pages, v_pages (num_pages, Hkv, page_size, D), any strides
+    with stride(-1) == 1 (a (num_pages, page_size, Hkv, D) pool passes as
+    ``pool.transpose(1, 2)``); block_table int32 (B, max_pages_per_seq);
+    cache_lens int32 (B,).  ``max_cache_len`` defaults to
+    max_pages_per_seq * page_size.  Returns ``out`` (B, Hq, D), or
+    ``(out, lse)`` with lse fp32 (B, Hq).
+    """
+    lib = load_library()
+    B, Hq, D = q.shape
+    P, Hkv, ps, Dk = k_pages.shape
+    if v_pages.shape != k_pages.shape or Dk != D:
+        raise ValueError("page pools must share one shape (num_pages, Hkv, page_size, D) with q's D")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 (B, max_pages_per_seq) tensor")
+    _int32_vec(cache_lens, B, "cache_lens")
+    mbps = block_table.shape[1]
+    if max_cache_len is None:
+        max_cache_len = mbps * ps
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq)")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, int(max_cache_len), D, q.device)
+    _on_gpu(q, k_pages, v_pages, out, block_table, cache_lens, workspace, *([lse] if lse is not None else []))
+    code = _dtype_code(q, k_pages, v_pages, out)
+    s = _default_scale(D) if scale is None else float(scale)
+    st = lib.attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
+                               lse.data_ptr() if lse is not None else None, B, Hq, Hkv, P, ps,
+                               block_table.data_ptr(), mbps, cache_lens.data_ptr(), int(max_cache_len), D,
+                               _strides3(q), _strides4(k_pages), _strides4(v_pages), _strides3(out), s, code,
+                               int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check(st, "attn_decode_paged")
+    return (out, lse) if return_lse else out
+
+
+def kv_cache_write_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                         block_table: torch.Tensor, pos: torch.Tensor):
+    """Store k_new/v_new (B, Hkv, T, D) at slots pos[b] .. pos[b] + T - 1 of each
+    sequence of a paged cache (pools as in ``attn_decode_paged``; pos int32 (B,))."""
+    lib = load_library()
+    P, Hkv, ps, D = k_pages.shape
+    B, Hn, T, Dn = k_new.shape
+    if v_pages.shape != k_pages.shape or v_new.shape != k_new.shape or Hn != Hkv or Dn != D:
+        raise ValueError("shape mismatch between the page pools and the new rows")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 (B, max_pages_per_seq) tensor")
+    _int32_vec(pos, B, "pos")
+    _on_gpu(k_pages, v_pages, k_new, v_new, block_table, pos)
+    code = _dtype_code(k_pages, v_pages, k_new, v_new)
+    st = lib.kv_cache_write_paged(k_pages.data_ptr(), v_pages.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                  B, Hkv, P, ps, block_table.data_ptr(), block_table.shape[1], pos.data_ptr(), D, T,
+                                  _strides4(k_pages), _strides4(v_pages), _strides4(k_new), _strides4(v_new), code,
+                                  _stream(k_pages))
+    _check(st, "kv_cache_write_paged")
+

@@ -203,13 +203,21 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D) {
 
 namespace {
 
-// shared by attn_decode (lens == nullptr: every sequence has cache_len slots)
-// and attn_decode_varlen (sequence b has min(max(lens[b], 0), cache_len))
-attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+// a paged cache: page ids of sequence b at table[b * mbps ...], pages of
+// 2^lg_ps rows, num_pages pages in the pools
+struct PagedSpec {
+  const int32_t* table;
+  int mbps, lg_ps, num_pages;
+};
+
+// shared by attn_decode (lens == nullptr: every sequence has cache_len slots),
+// attn_decode_varlen (sequence b has min(max(lens[b], 0), cache_len)) and
+// attn_decode_paged (the same over a paged cache, pg != nullptr)
+static attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                         int B, int Hq, int Hkv, int S_max, int cache_len, const int32_t* lens, int D,
                         attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
                         float scale, attn_dtype dtype, int num_splits,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream, const PagedSpec* pg = nullptr) {
   if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0 || cache_len < 1 || cache_len > S_max || num_splits < 0) return ATTN_ERR_SHAPE;
@@ -266,6 +274,12 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
   a.part = static_cast<float*>(workspace);
+  if (pg) {
+    a.block_table = pg->table;
+    a.mbps = pg->mbps;
+    a.lg_ps = pg->lg_ps;
+    a.num_pages = pg->num_pages;
+  }
 
   const hipError_t e = attn::launch_decode(a, B, D, dtype == ATTN_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -290,6 +304,69 @@ attn_status attn_decode_varlen(const void* q, const void* k_cache, const void* v
   if (!cache_lens) return ATTN_ERR_NULL;
   return decode_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, max_cache_len, cache_lens, D, sq, skc, svc,
                      so, scale, dtype, num_splits, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// log2 of a supported page size (a power of two, 16 .. 2^20), else -1
+static int page_log2(int page_size) {
+  if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0) return -1;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  return lg;
+}
+
+}  // namespace
+
+attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                              int B, int Hq, int Hkv, int num_pages, int page_size,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* cache_lens, int max_cache_len, int D,
+                              attn_strides sq, attn_strides skp, attn_strides svp, attn_strides so,
+                              float scale, attn_dtype dtype, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!block_table || !cache_lens) return ATTN_ERR_NULL;
+  if (num_pages <= 0 || max_pages_per_seq <= 0 || max_cache_len <= 0) return ATTN_ERR_SHAPE;
+  const int lg = page_log2(page_size);
+  if (lg < 0) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)max_cache_len > (int64_t)max_pages_per_seq * page_size) return ATTN_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(block_table) & 3u) return ATTN_ERR_UNSUPPORTED;
+  const PagedSpec pg{block_table, max_pages_per_seq, lg, num_pages};
+  return decode_impl(q, k_pages, v_pages, o, lse, B, Hq, Hkv, max_cache_len, max_cache_len, cache_lens, D, sq, skp,
+                     svp, so, scale, dtype, num_splits, workspace, workspace_bytes, stream, &pg);
+}
+
+attn_status kv_cache_write_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                                 int B, int Hkv, int num_pages, int page_size, const int32_t* block_table,
+                                 int max_pages_per_seq, const int32_t* pos, int D, int T,
+                                 attn_strides skp, attn_strides svp, attn_strides skn, attn_strides svn,
+                                 attn_dtype dtype, void* stream) {
+  if (!k_pages || !v_pages || !k_new || !v_new || !block_table || !pos) return ATTN_ERR_NULL;
+  if (B <= 0 || Hkv <= 0 || num_pages <= 0 || max_pages_per_seq <= 0 || D <= 0 || T <= 0) return ATTN_ERR_SHAPE;
+  const int lg = page_log2(page_size);
+  if (lg < 0 || D % 8 != 0 || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  if (!strides_ok(skp) || !strides_ok(svp) || !strides_ok(skn) || !strides_ok(svn)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
+    return ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return ATTN_ERR_UNSUPPORTED;
+
+  attn::CacheWritePagedArgs a{};
+  a.kp = static_cast<uint16_t*>(k_pages);
+  a.vp = static_cast<uint16_t*>(v_pages);
+  a.kn = static_cast<const uint16_t*>(k_new);
+  a.vn = static_cast<const uint16_t*>(v_new);
+  a.block_table = block_table;
+  a.pos = pos;
+  a.skpp = skp.b; a.skph = skp.h; a.skpn = skp.n;
+  a.svpp = svp.b; a.svph = svp.h; a.svpn = svp.n;
+  a.sknb = skn.b; a.sknh = skn.h; a.sknn = skn.n;
+  a.svnb = svn.b; a.svnh = svn.h; a.svnn = svn.n;
+  a.rows = (int64_t)B * Hkv * T;
+  a.B = B; a.Hkv = Hkv; a.T = T; a.D = D;
+  a.mbps = max_pages_per_seq; a.lg_ps = lg; a.num_pages = num_pages;
+  const hipError_t e = attn::launch_cache_write_paged(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status kv_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

@@ -52,8 +52,12 @@ __device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
   return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
 }
 
-template <int D, bool BF16, bool VARLEN>
+// MODE 0: one length for every sequence; 1: per-sequence lengths; 2: per-sequence
+// lengths over a paged cache
+template <int D, bool BF16, int MODE>
 __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel(const DecodeArgs a) {
+  constexpr bool VARLEN = MODE >= 1;
+  constexpr bool PAGED = MODE == 2;
   constexpr int KS = D / 32;                 // k-steps of the score MFMA
   constexpr int NDT = D / 16;                // 16-wide head-dim tiles of O
 #if ATTN_DECODE_VSWZ
@@ -111,8 +115,8 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
     for (int ks = 0; ks < KS; ++ks) qf[ks] = load16(qp + 32 * ks + 8 * rg) ^ a.qsign;
   }
 
-  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
-  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
+  const uint16_t* kbase = a.k + (PAGED ? 0 : (int64_t)b * a.skb) + (int64_t)kvh * a.skh;
+  const uint16_t* vbase = a.v + (PAGED ? 0 : (int64_t)b * a.svb) + (int64_t)kvh * a.svh;
   // MFMA row i of key group gi reads key 8*(i/4) + 4*gi + i%4 of the wave's 32,
   // so that lane (col, rg) holds keys 8*rg .. 8*rg+7 in its score registers.
   const int krow = 32 * w + 8 * (col >> 2) + (col & 3);
@@ -159,6 +163,41 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
     u32x4 v[VPT][4];
   };
   auto load_tile = [&](Tile& T, int kb) {
+    if constexpr (PAGED) {
+      // Slot r lives in page block_table[b][r >> lg_ps], row r & (page size - 1).
+      // Rows past the chunk re-read its last row (finite data of this sequence;
+      // their scores are masked, their P is 0), so no load is predicated.  A
+      // wave's 32 K rows and a (wave, j) group of V rows span at most two pages
+      // (page size >= 16, groups aligned): their page ids are uniform loads.
+      const int last = k1 - 1;
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      const int32_t* tb = a.block_table + (int64_t)b * a.mbps;
+      const int rmask = (1 << a.lg_ps) - 1;
+      auto page = [&](int r) __attribute__((always_inline)) {
+        return (int64_t)min(max(tb[r >> a.lg_ps], 0), a.num_pages - 1);
+      };
+      const int kw0 = kb + 32 * wu;
+      const int64_t kp_lo = page(min(kw0, last)), kp_hi = page(min(kw0 + 16, last));
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int rr = min(kb + krow + 4 * gi, last);
+        const int64_t pg = rr >= kw0 + 16 ? kp_hi : kp_lo;
+        const uint16_t* kp = kbase + pg * a.skb + (int64_t)(rr & rmask) * a.skn + 8 * rg;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) T.kf[gi][ks] = load16(kp + 32 * ks);
+      }
+      constexpr int VROWS = 2048 / D;  // V rows one wave loads per j
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int vs = kb + VROWS * (wu + 4 * j);
+        const int64_t vp_lo = page(min(vs, last)), vp_hi = page(min(vs + 16, last));
+        const int g0 = kb + 4 * vkvg[j];
+        const uint16_t* vb = vbase + (g0 >= vs + 16 ? vp_hi : vp_lo) * a.svb + 8 * vdc[j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) T.v[j][r] = load16(vb + (int64_t)(min(g0 + r, last) & rmask) * a.svn);
+      }
+      return;
+    }
     const int64_t ko = (int64_t)kb * a.skn, vo = (int64_t)kb * a.svn;
     const int64_t rows = k1 - kb;  // keys of this split from kb on
     const auto rk = make_rsrc(kbase + ko, clamp_bytes(((rows - 1) * a.skn + D) * 2));
@@ -228,7 +267,7 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   // tiles of this split, the next tile's loads always issued before the
   // current tile is consumed (two tiles in flight per workgroup)
   Tile ta, tb;
-  load_tile(ta, k0);
+  if (!PAGED || k0 < k1) load_tile(ta, k0);  // (an empty chunk has no row to look up)
   for (int kb = k0; kb < k1; kb += 2 * kDT) {
     const bool has_b = kb + kDT < k1;
     if (has_b) load_tile(tb, kb + kDT);
@@ -380,21 +419,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
   }
 }
 
-template <int D, bool BF16, bool VARLEN>
+template <int D, bool BF16, int MODE>
 hipError_t launch_v(const DecodeArgs& a, int B, hipStream_t stream) {
   const unsigned units = (unsigned)(B * a.Hkv);
   const dim3 g1 = a.unit_fast ? dim3(units, a.hgroups, a.nsplit) : dim3(a.nsplit, a.hgroups, units);
-  hipLaunchKernelGGL((decode_kernel<D, BF16, VARLEN>), g1, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, MODE>), g1, dim3(256), 0, stream, a);
   if (a.nsplit > 1) {
     const dim3 g2 = a.unit_fast ? dim3(units, a.hgroups, a.heads_per_wg) : dim3(a.heads_per_wg, a.hgroups, units);
-    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, VARLEN>), g2, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_combine_kernel<D, BF16, (MODE >= 1)>), g2, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_t(const DecodeArgs& a, int B, hipStream_t stream) {
-  return a.lens ? launch_v<D, BF16, true>(a, B, stream) : launch_v<D, BF16, false>(a, B, stream);
+  if (a.block_table) return launch_v<D, BF16, 2>(a, B, stream);
+  return a.lens ? launch_v<D, BF16, 1>(a, B, stream) : launch_v<D, BF16, 0>(a, B, stream);
 }
 
 // ---- cache writer: a plain 16-byte-vector copy of T rows per (batch, kv head)
@@ -421,7 +461,47 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const CacheWriteArgs a
   }
 }
 
+// ---- paged cache writer: row t of sequence b goes to slot pos[b] + t, i.e. row
+//      (pos[b] + t) & (page size - 1) of page block_table[b][(pos[b] + t) >> lg_ps].
+//      Slots outside [0, mbps * page size) are skipped; page ids are clamped
+//      into the pool.
+__global__ __launch_bounds__(256) void cache_write_paged_kernel(const CacheWritePagedArgs a) {
+  const int cpr = a.D / 8;  // 16-byte chunks per row
+  const int64_t total = a.rows * cpr;
+  const int64_t cap = (int64_t)a.mbps << a.lg_ps;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const bool isv = i >= total;
+    const int64_t j = isv ? i - total : i;
+    const int c8 = (int)(j % cpr);
+    const int64_t r = j / cpr;
+    const int t = (int)(r % a.T);
+    const int64_t bh = r / a.T;
+    const int kvh = (int)(bh % a.Hkv);
+    const int b = (int)(bh / a.Hkv);
+    const int64_t slot = (int64_t)a.pos[b] + t;
+    if (slot < 0 || slot >= cap) continue;
+    const int64_t pg = min(max(a.block_table[(int64_t)b * a.mbps + (slot >> a.lg_ps)], 0), a.num_pages - 1);
+    const int64_t row = slot & ((1 << a.lg_ps) - 1);
+    if (!isv) {
+      const u32x4 x = load16(a.kn + b * a.sknb + kvh * a.sknh + t * a.sknn + 8 * c8);
+      store16(a.kp + pg * a.skpp + kvh * a.skph + row * a.skpn + 8 * c8, x);
+    } else {
+      const u32x4 x = load16(a.vn + b * a.svnb + kvh * a.svnh + t * a.svnn + 8 * c8);
+      store16(a.vp + pg * a.svpp + kvh * a.svph + row * a.svpn + 8 * c8, x);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cache_write_paged(const CacheWritePagedArgs& a, hipStream_t stream) {
+  const int64_t work = 2 * a.rows * (a.D / 8);
+  const int64_t blocks = (work + 255) / 256;
+  const int grid = (int)(blocks < 4096 ? blocks : 4096);
+  hipLaunchKernelGGL(cache_write_paged_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool bf16, hipStream_t stream) {
   if (D == 64) return bf16 ? launch_t<64, true>(a, B, stream) : launch_t<64, false>(a, B, stream);

@@ -61,9 +61,31 @@ struct DecodeArgs {
   float c;
   uint32_t qsign;
   float* part;  // workspace: partial (m, l, pad, pad, o[D]) per (unit, head group, split, head)
+  // paged cache (null otherwise): slot r of sequence b is row r & (2^lg_ps - 1)
+  // of page block_table[b * mbps + (r >> lg_ps)]; k / v then point at page 0
+  // and skb / svb are the page strides
+  const int32_t* block_table;
+  int mbps, lg_ps, num_pages;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool bf16, hipStream_t stream);
+
+struct CacheWritePagedArgs {
+  uint16_t* kp;
+  uint16_t* vp;
+  const uint16_t* kn;
+  const uint16_t* vn;
+  const int32_t* block_table;
+  const int32_t* pos;  // per sequence: slot of its first new row
+  int64_t skpp, skph, skpn;  // page pool strides (page, head, row)
+  int64_t svpp, svph, svpn;
+  int64_t sknb, sknh, sknn;
+  int64_t svnb, svnh, svnn;
+  int64_t rows;  // B * Hkv * T
+  int B, Hkv, T, D, mbps, lg_ps, num_pages;
+};
+
+hipError_t launch_cache_write_paged(const CacheWritePagedArgs& a, hipStream_t stream);
 
 struct CacheWriteArgs {
   uint16_t* kc;

@@ -26,8 +26,9 @@ FETCH_SIZE and WRITE_SIZE counters measured (scaled by a plain copy's reading),
 taken from the committed summaries under profiles/; null once the kernel
 sources differ from the ones those counters were taken with.
 
-The default run also times three widened workloads (not the headline):
-decode with per-sequence cache lengths over a 16-sequence batch, a chunked
+The default run also times four widened workloads (not the headline):
+decode with per-sequence cache lengths over a 16-sequence batch, the same
+batch over a paged cache (16-slot pages in a shuffled pool), a chunked
 prefill (1024 queries at the end of an 8192-token context, causal aligned
 bottom-right) and a packed prefill of 16 sequences of seeded lengths up to
 4096; they are printed under "widened".
@@ -277,7 +278,33 @@ def main():
             "S_max": vc_case.S_max, "lengths": "seeded uniform [1, 8192]", "sum_lengths": int(vlens_h.sum()),
             "bytes_per_call": vbytes, "us_per_call": round(vt * 1e3, 2),
             "gbs": round(vbytes / (vt * 1e-3) / 1e9, 1), "frac_of_8000_gbs": round(vbytes / (vt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        del vq, vk, vv, vo, vws
+        # the same batch over a paged cache: 16-slot pages in a shuffled pool
+        ps = 16
+        npb = vc_case.S_max // ps
+        perm = torch.randperm(vc_case.B * npb, generator=torch.Generator().manual_seed(W.BASE_SEED + 50)).to(dev)
+        kpool = torch.empty(vc_case.B * npb, vc_case.Hkv, ps, vc_case.D, dtype=vk.dtype, device=dev)
+        vpool = torch.empty_like(kpool)
+        kpool[perm] = vk.reshape(vc_case.B, vc_case.Hkv, npb, ps, vc_case.D).permute(0, 2, 1, 3, 4).reshape(
+            -1, vc_case.Hkv, ps, vc_case.D)
+        vpool[perm] = vv.reshape(vc_case.B, vc_case.Hkv, npb, ps, vc_case.D).permute(0, 2, 1, 3, 4).reshape(
+            -1, vc_case.Hkv, ps, vc_case.D)
+        vtbl = perm.reshape(vc_case.B, npb).to(torch.int32)
+        for _ in range(3):
+            A.attn_decode_paged(vq, kpool, vpool, vtbl, vlens, vc_case.S_max, workspace=vws, out=vo)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0.record(stream)
+        for _ in range(20):
+            A.attn_decode_paged(vq, kpool, vpool, vtbl, vlens, vc_case.S_max, workspace=vws, out=vo)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pgt = e0.elapsed_time(e1) / 20
+        widened["decode_paged"] = {
+            "workload": vc_case.name + "_paged16_shuffled", "page_size": ps, "pages": vc_case.B * npb,
+            "lengths": "as decode_varlen", "bytes_per_call": vbytes, "us_per_call": round(pgt * 1e3, 2),
+            "gbs": round(vbytes / (pgt * 1e-3) / 1e9, 1),
+            "frac_of_8000_gbs": round(vbytes / (pgt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del vq, vk, vv, vo, vws, kpool, vpool
         cp = W.chunked_prefill_case()
         cq, ck, cv = (t.to(dev) for t in W.prefill_inputs(cp))
         co = torch.empty_like(cq)

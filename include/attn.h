@@ -187,6 +187,53 @@ attn_status attn_decode_varlen(const void* q, const void* k_cache, const void* v
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_paged -- attn_decode_varlen over a paged KV cache: cache slot r
+ * of sequence b lives in page block_table[b * max_pages_per_seq + r / page_size],
+ * row r % page_size, of the page pools.  The paged cache is the widening that
+ * [P3]'s deferred scope names; per sequence the operation is the decode of
+ * [P3] decode phase over that sequence's first cache_lens[b] slots.
+ *
+ *   q        (B, Hq, D) via sq (sq.n unused);  o (B, Hq, D) via so (so.n unused)
+ *   k_pages, v_pages: page pools (num_pages, Hkv, page_size, D) via skp, svp:
+ *            element (p, h, r, d) at k_pages[p*skp.b + h*skp.h + r*skp.n + d]
+ *            (so (num_pages, page_size, Hkv, D) pools are accepted too)
+ *   block_table: DEVICE int32 (B, max_pages_per_seq), row-major; page ids are
+ *            clamped into [0, num_pages) on the device
+ *   cache_lens: DEVICE int32 (B), clamped to [0, max_cache_len]; a length of 0
+ *            gives o = 0 and lse = -inf
+ *   page_size: a power of two, 16 <= page_size <= 2^20 (else UNSUPPORTED)
+ *   max_cache_len: host bound on the lengths, <= max_pages_per_seq * page_size;
+ *            sizes the split grid
+ *   lse nullable, contiguous fp32 (B, Hq); num_splits as attn_decode
+ *   workspace: attn_decode_workspace_bytes(B, Hq, Hkv, max_cache_len, D) bytes
+ *   Only the pages a sequence's first cache_lens[b] slots map to are read.
+ */
+attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                              int B, int Hq, int Hkv, int num_pages, int page_size,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* cache_lens, int max_cache_len, int D,
+                              attn_strides sq, attn_strides skp, attn_strides svp, attn_strides so,
+                              float scale, attn_dtype dtype, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kv_cache_write_paged -- kv_cache_write for a paged cache: row t of sequence
+ * b (k_new, v_new (B, Hkv, T, D) via skn, svn) is stored at that sequence's
+ * slot pos[b] + t, i.e. row (pos[b] + t) % page_size of page
+ * block_table[b * max_pages_per_seq + (pos[b] + t) / page_size]  ([P3] decode
+ * phase: the cache is written by a separate helper; paged per the deferred
+ * scope).  pos: DEVICE int32 (B).  Slots outside [0, max_pages_per_seq *
+ * page_size) are skipped and page ids are clamped into [0, num_pages) on the
+ * device, so no write leaves the pools.  Pools, strides and page_size as
+ * attn_decode_paged; D a multiple of 8.
+ */
+attn_status kv_cache_write_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,
+                                 int B, int Hkv, int num_pages, int page_size, const int32_t* block_table,
+                                 int max_pages_per_seq, const int32_t* pos, int D, int T,
+                                 attn_strides skp, attn_strides svp, attn_strides skn, attn_strides svn,
+                                 attn_dtype dtype, void* stream);
+
+/*
  * kv_cache_write -- copy T new rows per (batch, kv head) into cache slots
  * [pos, pos + T) of K and V ([P3] decode phase: the preallocated-cache write
  * helper kept separate from the attention kernel).  A bit-exact copy; every

@@ -42,8 +42,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_varlen", "attn_decode", "attn_decode_varlen",
-                          "attn_decode_workspace_bytes", "kv_cache_write", "attn_status_string"}
+    assert set(names) == {"attn_fwd", "attn_fwd_varlen", "attn_decode", "attn_decode_varlen", "attn_decode_paged",
+                          "attn_decode_workspace_bytes", "kv_cache_write", "kv_cache_write_paged",
+                          "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -151,6 +152,51 @@ def decv(lib, **kw):
 ])
 def test_decode_varlen_rejects(lib, kw, code):
     assert decv(lib, **kw) == code
+
+
+def dpg(lib, **kw):
+    B, Hq, Hkv, D, ps, mbps = 2, 32, 8, 128, 16, 64
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, o=FAKE, lse=None, B=B, Hq=Hq, Hkv=Hkv, P=200, ps=ps, tbl=FAKE, mbps=mbps,
+             lens=FAKE, mcl=1000, D=D, sq=S(Hq * D, D, 0, 1), skp=c4(D, ps, Hkv), svp=c4(D, ps, Hkv),
+             so=S(Hq * D, D, 0, 1), scale=0.088, dtype=0, num_splits=0, ws=FAKE,
+             ws_bytes=lib.attn_decode_workspace_bytes(B, Hq, Hkv, 1000, D), stream=None)
+    a.update(kw)
+    return lib.attn_decode_paged(a["q"], a["kp"], a["vp"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["P"],
+                                 a["ps"], a["tbl"], a["mbps"], a["lens"], a["mcl"], a["D"], a["sq"], a["skp"],
+                                 a["svp"], a["so"], a["scale"], a["dtype"], a["num_splits"], a["ws"], a["ws_bytes"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tbl=None), NULL), (dict(lens=None), NULL), (dict(kp=None), NULL),
+    (dict(P=0), SHAPE), (dict(mbps=0), SHAPE), (dict(mcl=0), SHAPE), (dict(mcl=64 * 16 + 1), SHAPE),
+    (dict(Hq=30), SHAPE),
+    (dict(ps=24), UNSUP), (dict(ps=8), UNSUP), (dict(ps=1 << 21), UNSUP), (dict(tbl=FAKE + 2), UNSUP),
+    (dict(lens=FAKE + 1), UNSUP), (dict(D=96), UNSUP), (dict(skp=S(16 * 128 * 8, 16 * 128, 128, 2)), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=4096), WS),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert dpg(lib, **kw) == code
+
+
+def cwp(lib, **kw):
+    B, Hkv, D, ps, T = 2, 8, 128, 16, 3
+    a = dict(kp=FAKE, vp=FAKE, kn=FAKE, vn=FAKE, B=B, Hkv=Hkv, P=40, ps=ps, tbl=FAKE, mbps=20, pos=FAKE, D=D, T=T,
+             skp=c4(D, ps, Hkv), svp=c4(D, ps, Hkv), skn=c4(D, T, Hkv), svn=c4(D, T, Hkv), dtype=0, stream=None)
+    a.update(kw)
+    return lib.kv_cache_write_paged(a["kp"], a["vp"], a["kn"], a["vn"], a["B"], a["Hkv"], a["P"], a["ps"], a["tbl"],
+                                    a["mbps"], a["pos"], a["D"], a["T"], a["skp"], a["svp"], a["skn"], a["svn"],
+                                    a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tbl=None), NULL), (dict(pos=None), NULL), (dict(vn=None), NULL),
+    (dict(B=0), SHAPE), (dict(T=0), SHAPE), (dict(P=0), SHAPE), (dict(mbps=0), SHAPE),
+    (dict(ps=48), UNSUP), (dict(D=60), UNSUP), (dict(dtype=5), UNSUP), (dict(pos=FAKE + 2), UNSUP),
+    (dict(kp=FAKE + 8), UNSUP),
+])
+def test_cache_write_paged_rejects(lib, kw, code):
+    assert cwp(lib, **kw) == code
 
 
 def cw(lib, **kw):
