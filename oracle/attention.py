@@ -52,6 +52,13 @@ Readings taken where the pages leave a step open (each also listed in the design doc)
   the page pools (num_pages, Hkv, page_size, D).  Decode over a paged cache is
   the per-sequence-length decode on the rows so gathered; the paged writer
   stores new rows at slots pos[b], pos[b] + 1, ... of each sequence.
+* Sliding windows (the pages' "windowed attention" use case, deferred in
+  their scope list): query i sits at key position p = i + offset and sees keys
+  j with p - window_left <= j <= p + window_right (-1 leaves a side open); a
+  causal mask is window_right = 0.  For packed sequences the window is aligned
+  like the causal mask (offset from the sequence's own lengths).  Decode's
+  query is the last cached token, so its window keeps the last
+  window_left + 1 slots.
 * Packed variable-length prefill (the pages' deferred "varlen" scope item):
   sequence b owns the packed query rows [cu_q[b], cu_q[b+1]) and key rows
   [cu_k[b], cu_k[b+1]); attention never crosses sequences, and each sequence
@@ -100,17 +107,26 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def visibility(q_pos: np.ndarray, Nkv: int, causal: bool, offset: int = 0) -> np.ndarray:
+def visibility(q_pos: np.ndarray, Nkv: int, causal: bool, offset: int = 0, window_left: int = -1,
+               window_right: int = -1) -> np.ndarray:
     """Boolean (len(q_pos), Nkv): may query at position i attend to key j?
 
     Keys exist only for j < Nkv ([P1] "Correctness requirements", KV boundary
-    bullet); with ``causal`` a key is visible when j <= i + offset ([P1] step
-    5c has offset 0; the bottom-right alignment uses offset = Nkv - Nq).
+    bullet).  Query i sits at key position p = i + offset (0 top-left; the
+    bottom-right alignment uses offset = Nkv - Nq).  With ``causal`` a key is
+    visible when j <= p ([P1] step 5c).  A sliding window ([P1] "Use this
+    when": windowed attention) also bounds j to [p - window_left,
+    p + window_right]; -1 leaves that side open.
     """
-    j = np.arange(Nkv)
+    j = np.arange(Nkv)[None, :]
+    p = q_pos[:, None] + offset
     vis = np.ones((q_pos.shape[0], Nkv), dtype=bool)
     if causal:
-        vis &= j[None, :] <= q_pos[:, None] + offset
+        vis &= j <= p
+    if window_left >= 0:
+        vis &= j >= p - window_left
+    if window_right >= 0:
+        vis &= j <= p + window_right
     return vis
 
 
@@ -152,12 +168,15 @@ def attention_probs(q, k, scale: float, causal: bool, causal_offset: int = 0) ->
     return out
 
 
-def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int = 512, causal_offset: int = 0):
+def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int = 512, causal_offset: int = 0,
+                      window=(-1, -1)):
     """O1: prefill attention by the plain definition.
 
     q: (B, Hq, Nq, D); k, v: (B, Hkv, Nkv, D), any float dtype (widened exactly).
-    causal_offset: query i sees keys j <= i + causal_offset when causal (0 is the
-    pages' top-left mask; Nkv - Nq aligns it bottom-right).
+    causal_offset: query i sits at key position i + causal_offset (0 is the
+    pages' top-left mask; Nkv - Nq aligns it bottom-right).  window: (left,
+    right) sliding-window bounds around that position, -1 for an open side
+    (see ``visibility``).
     rows: optional 1-D array of query positions to evaluate (sampling at large
     sizes); default all Nq positions.  Evaluated in row chunks so that the score
     block stays small; chunking does not change any value.
@@ -183,29 +202,32 @@ def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int
             for r0 in range(0, R, chunk):
                 sel = rows[r0:r0 + chunk]
                 S = _scores(q[b, h, sel], kb, scale)
-                P, ls = _masked_softmax(S, visibility(sel, Nkv, causal, causal_offset))
+                P, ls = _masked_softmax(S, visibility(sel, Nkv, causal, causal_offset, window[0], window[1]))
                 O[b, h, r0:r0 + chunk] = P @ vb
                 lse[b, h, r0:r0 + chunk] = ls
     return O, lse
 
 
-def decode(q, k_cache, v_cache, cache_len: int, scale: float):
+def decode(q, k_cache, v_cache, cache_len: int, scale: float, window_left: int = -1):
     """O2: one query token per (batch, q head) over cache slots [0, cache_len).
 
     [P3] decode phase: every cached position is valid, so there is no causal
-    mask; GQA indexing is the same as prefill.  q: (B, Hq, D); caches
-    (B, Hkv, S_max, D).  Returns O (B, Hq, D) and lse (B, Hq), float64.
+    mask; GQA indexing is the same as prefill.  The query is the token at the
+    last cached position, cache_len - 1; a sliding window of ``window_left``
+    keeps keys j >= cache_len - 1 - window_left (-1: no window).  q: (B, Hq, D);
+    caches (B, Hkv, S_max, D).  Returns O (B, Hq, D) and lse (B, Hq), float64.
     """
     q = _f64(q)
     if not (1 <= cache_len <= np.asarray(k_cache).shape[2]):
         raise ValueError("cache_len out of range")
     kc = _f64(np.asarray(k_cache)[:, :, :cache_len])
     vc = _f64(np.asarray(v_cache)[:, :, :cache_len])
-    O, lse = attention_forward(q[:, :, None, :], kc, vc, scale, causal=False)
+    O, lse = attention_forward(q[:, :, None, :], kc, vc, scale, causal=False, causal_offset=cache_len - 1,
+                               window=(window_left, -1))
     return O[:, :, 0, :], lse[:, :, 0]
 
 
-def decode_varlen(q, k_cache, v_cache, cache_lens, scale: float):
+def decode_varlen(q, k_cache, v_cache, cache_lens, scale: float, window_left: int = -1):
     """O2 per sequence: batch element b attends over its own slots [0, cache_lens[b]).
 
     [P3] decode phase, widened as its deferred-scope list names (per-sequence
@@ -225,7 +247,8 @@ def decode_varlen(q, k_cache, v_cache, cache_lens, scale: float):
     for b, L in enumerate(lens):
         if L == 0:
             continue
-        Ob, lb = decode(q[b:b + 1], np.asarray(k_cache)[b:b + 1], np.asarray(v_cache)[b:b + 1], L, scale)
+        Ob, lb = decode(q[b:b + 1], np.asarray(k_cache)[b:b + 1], np.asarray(v_cache)[b:b + 1], L, scale,
+                        window_left)
         O[b], lse[b] = Ob[0], lb[0]
     return O, lse
 
@@ -245,7 +268,7 @@ def varlen_causal_offset(Lq: int, Lk: int, bottom_right: bool) -> int:
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
-                     bottom_right: bool = False, rows=None):
+                     bottom_right: bool = False, rows=None, window=(-1, -1)):
     """O1 over a batch of packed sequences of different lengths.
 
     The pages defer variable-length batches ([P3] deferred scope); this is the
@@ -281,11 +304,12 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         pick = np.nonzero((seq_of_row == b) & (rows >= q0) & (rows < q1))[0]
         if pick.size == 0 or k1 == k0:
             continue  # no rows asked for, or no keys: O = 0, lse = -inf
-        off = varlen_causal_offset(q1 - q0, k1 - k0, bottom_right) if causal else 0
+        off = varlen_causal_offset(q1 - q0, k1 - k0, bottom_right) if (causal or window != (-1, -1)) else 0
         qs = q[q0:q1].transpose(1, 0, 2)[None]
         ks = k[k0:k1].transpose(1, 0, 2)[None]
         vs = v[k0:k1].transpose(1, 0, 2)[None]
-        Ob, lb = attention_forward(qs, ks, vs, scale, causal, rows=rows[pick] - q0, causal_offset=off)
+        Ob, lb = attention_forward(qs, ks, vs, scale, causal, rows=rows[pick] - q0, causal_offset=off,
+                                   window=window)
         O[pick] = Ob[0].transpose(1, 0, 2)
         lse[:, pick] = lb[0]
     return O, lse
@@ -324,7 +348,8 @@ def gather_pages(pages, block_table, b: int, length: int, page_size: int) -> np.
     return out
 
 
-def decode_paged(q, k_pages, v_pages, block_table, cache_lens, page_size: int, scale: float):
+def decode_paged(q, k_pages, v_pages, block_table, cache_lens, page_size: int, scale: float,
+                 window_left: int = -1):
     """O2 over a paged cache: ``decode_varlen`` on each sequence's gathered slots.
 
     q: (B, Hq, D); k_pages, v_pages: (num_pages, Hkv, page_size, D); block_table:
@@ -344,7 +369,7 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_lens, page_size: int, s
     for b, L in enumerate(lens):
         kc[b, :, :L] = gather_pages(k_pages, tbl, b, L, page_size)
         vc[b, :, :L] = gather_pages(v_pages, tbl, b, L, page_size)
-    return decode_varlen(q, kc, vc, lens, scale)
+    return decode_varlen(q, kc, vc, lens, scale, window_left)
 
 
 def kv_cache_write_paged(k_pages, v_pages, k_new, v_new, block_table, pos, page_size: int):

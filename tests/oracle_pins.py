@@ -303,6 +303,76 @@ def pin_decode_varlen():
     np.testing.assert_array_equal(lsee, lsed)
 
 
+def pin_sliding_window_rows_are_slices():
+    """P6e: with a sliding window each query row equals unmasked attention over
+    the explicit key slice [p - left, p + right] (clipped), p = i + offset, for
+    causal and two-sided windows in both alignments; window sides of -1 stay
+    open and a window covering everything is the plain mask."""
+    rng = np.random.default_rng(64)
+    B, Hq, Hkv, D = 1, 4, 2, 5
+    for (Nq, Nkv, off, causal, wl, wr) in [(9, 9, 0, True, 3, -1), (9, 9, 0, False, 2, 1), (5, 12, 7, True, 4, -1),
+                                            (6, 10, 4, False, 0, 3), (7, 7, 0, False, -1, 2), (8, 5, -3, True, 1, -1)]:
+        q, k, v = _rand(rng, B, Hq, Nq, D), _rand(rng, B, Hkv, Nkv, D), _rand(rng, B, Hkv, Nkv, D)
+        O, lse = OA.attention_forward(q, k, v, 0.7, causal, causal_offset=off, window=(wl, wr))
+        for i in range(Nq):
+            p = i + off
+            lo = 0 if wl < 0 else max(0, p - wl)
+            hi = min(Nkv - 1, p if causal else (Nkv - 1 if wr < 0 else p + wr))
+            if wr >= 0:
+                hi = min(hi, p + wr)
+            if hi < lo:
+                assert np.all(O[:, :, i] == 0.0) and np.all(lse[:, :, i] == -np.inf)
+                continue
+            Os, ls = OA.attention_forward(q[:, :, i:i + 1], k[:, :, lo:hi + 1], v[:, :, lo:hi + 1], 0.7, False)
+            np.testing.assert_allclose(O[:, :, i], Os[:, :, 0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(lse[:, :, i], ls[:, :, 0], rtol=0, atol=1e-13)
+    q, k, v = _rand(rng, 1, 2, 6, 4), _rand(rng, 1, 1, 6, 4), _rand(rng, 1, 1, 6, 4)
+    Ow, lw = OA.attention_forward(q, k, v, 0.5, True, window=(6, -1))
+    Oc, lc = OA.attention_forward(q, k, v, 0.5, True)
+    np.testing.assert_array_equal(Ow, Oc)
+    np.testing.assert_array_equal(lw, lc)
+
+
+def pin_zero_width_window_is_the_diagonal_key():
+    """P6f: window (0, 0) leaves each query exactly one key, j = i + offset:
+    O is that key's V row and lse its scaled score (closed form)."""
+    rng = np.random.default_rng(65)
+    q, k, v = _rand(rng, 1, 2, 5, 4), _rand(rng, 1, 1, 8, 4), _rand(rng, 1, 1, 8, 4)
+    O, lse = OA.attention_forward(q, k, v, 0.9, False, causal_offset=3, window=(0, 0))
+    for i in range(5):
+        np.testing.assert_array_equal(O[0, :, i], np.repeat(v[0, 0, i + 3][None], 2, axis=0))
+        np.testing.assert_allclose(lse[0, :, i], 0.9 * (q[0, :, i] @ k[0, 0, i + 3]), rtol=0, atol=1e-14)
+
+
+def pin_decode_window_is_the_last_slots():
+    """P10e: decode with a window of w keeps the last w + 1 cached slots: it
+    equals decode over the cache shifted to start at slot L - 1 - w, for the
+    contiguous, per-sequence and paged forms."""
+    rng = np.random.default_rng(104)
+    B, Hq, Hkv, S, D, w = 3, 4, 2, 16, 3, 5
+    q, kc, vc = _rand(rng, B, Hq, D), _rand(rng, B, Hkv, S, D), _rand(rng, B, Hkv, S, D)
+    Ow, lw = OA.decode(q, kc, vc, 13, 0.5, window_left=w)
+    Os, ls = OA.decode(q, kc[:, :, 13 - 1 - w:], vc[:, :, 13 - 1 - w:], w + 1, 0.5)
+    np.testing.assert_allclose(Ow, Os, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lw, ls, rtol=0, atol=1e-14)
+    lens = [13, 3, 0]
+    Ov, lv = OA.decode_varlen(q, kc, vc, lens, 0.5, window_left=w)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(Ov[b] == 0.0) and np.all(lv[b] == -np.inf)
+            continue
+        lo = max(0, L - 1 - w)
+        Ob, lb = OA.decode(q[b:b + 1], kc[b:b + 1, :, lo:L], vc[b:b + 1, :, lo:L], L - lo, 0.5)
+        np.testing.assert_allclose(Ov[b], Ob[0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lv[b], lb[0], rtol=0, atol=1e-14)
+    perm = rng.permutation(B * (S // 4))
+    kp, tbl = _scatter_to_pages(kc, perm, 4)
+    vp, _ = _scatter_to_pages(vc, perm, 4)
+    Op, lp = OA.decode_paged(q, kp, vp, tbl, lens, 4, 0.5, window_left=w)
+    np.testing.assert_array_equal(Op, Ov)
+    np.testing.assert_array_equal(lp, lv)
+
+
 def _scatter_to_pages(cache, perm, page_size):
     """Independent scatter of contiguous (B, Hkv, S, D) caches into a page pool:
     page perm[b * (S // page_size) + j] holds slots [j * ps, (j + 1) * ps) of sequence b."""
@@ -439,6 +509,9 @@ ALL_PINS = [
     pin_prefill_varlen,
     pin_decode_paged,
     pin_cache_write_paged,
+    pin_sliding_window_rows_are_slices,
+    pin_zero_width_window_is_the_diagonal_key,
+    pin_decode_window_is_the_last_slots,
     pin_row_sampling_matches_full,
     pin_cache_write_touches_only_its_slots,
 ]

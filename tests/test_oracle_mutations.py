@@ -24,28 +24,40 @@ _orig_vcoff = OA.varlen_causal_offset
 _orig_pslot = OA.page_slot
 
 
-def _vis_strict(q_pos, Nkv, causal, offset=0):
+def _vis_strict(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
     j = np.arange(Nkv)
-    vis = np.ones((q_pos.shape[0], Nkv), dtype=bool)
+    vis = _orig_vis(q_pos, Nkv, False, offset, window_left, window_right)
     if causal:
         vis &= j[None, :] < q_pos[:, None] + offset
     return vis
 
 
-def _vis_no_causal(q_pos, Nkv, causal, offset=0):
-    return _orig_vis(q_pos, Nkv, False)
+def _vis_no_causal(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
+    return _orig_vis(q_pos, Nkv, False, offset, window_left, window_right)
 
 
-def _vis_off_by_one(q_pos, Nkv, causal, offset=0):
-    return _orig_vis(q_pos + 1, Nkv, causal, offset)
+def _vis_off_by_one(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
+    return _orig_vis(q_pos + 1, Nkv, causal, offset, window_left, window_right)
 
 
-def _vis_offset_ignored(q_pos, Nkv, causal, offset=0):
-    return _orig_vis(q_pos, Nkv, causal, 0)
+def _vis_offset_ignored(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
+    return _orig_vis(q_pos, Nkv, causal, 0, window_left, window_right)
 
 
-def _vis_offset_sign(q_pos, Nkv, causal, offset=0):
-    return _orig_vis(q_pos, Nkv, causal, -offset)
+def _vis_offset_sign(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
+    return _orig_vis(q_pos, Nkv, causal, -offset, window_left, window_right)
+
+
+def _vis_window_ignored(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
+    return _orig_vis(q_pos, Nkv, causal, offset)
+
+
+def _vis_window_left_strict(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
+    return _orig_vis(q_pos, Nkv, causal, offset, window_left - 1 if window_left > 0 else window_left, window_right)
+
+
+def _vis_window_sides_swapped(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
+    return _orig_vis(q_pos, Nkv, causal, offset, window_right, window_left)
 
 
 def _kv_head_tiled(h, Hq, Hkv):
@@ -150,6 +162,9 @@ MUTATIONS = {
     "causal_off_by_one": ("visibility", _vis_off_by_one),
     "causal_offset_ignored": ("visibility", _vis_offset_ignored),
     "causal_offset_sign": ("visibility", _vis_offset_sign),
+    "window_ignored": ("visibility", _vis_window_ignored),
+    "window_left_one_short": ("visibility", _vis_window_left_strict),
+    "window_sides_swapped": ("visibility", _vis_window_sides_swapped),
     "gqa_tiled_heads": ("kv_head_of", _kv_head_tiled),
     "scale_dropped": ("_scores", _scores_unscaled),
     "scale_twice": ("_scores", _scores_scaled_twice),
