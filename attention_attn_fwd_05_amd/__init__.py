@@ -8,11 +8,14 @@ every call raises.
 
 Entry points (same names as the C ABI):
 
-* ``attn_fwd(q, k, v, *, causal, scale=None, return_lse=False, out=None)``
+* ``attn_fwd(q, k, v, *, causal, scale=None, return_lse=False, out=None,
+  causal_align="top_left", window=None)`` (``window=(left, right)``: a
+  sliding-window band, through attn_fwd_masked)
 * ``attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, *,
   causal, ...)`` (packed sequences of different lengths, offsets on the device)
 * ``attn_decode(q, k_cache, v_cache, cache_len, *, scale=None, workspace=None,
-  num_splits=0, return_lse=False, out=None)``
+  num_splits=0, return_lse=False, out=None, window_left=-1)`` (every decode
+  form takes ``window_left``, through attn_decode_ex)
 * ``attn_decode_varlen(q, k_cache, v_cache, cache_lens, max_cache_len=None, ...)``
   (one cache length per sequence, read on the device)
 * ``attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)`` /

@@ -31,6 +31,16 @@ class Strides(ctypes.Structure):
     _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64), ("d", ctypes.c_int64)]
 
 
+class Mask(ctypes.Structure):
+    _fields_ = [("align", ctypes.c_int32), ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32)]
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("cache_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("max_pages_per_seq", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("window_left", ctypes.c_int32)]
+
+
 _DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 _LIB = None
 
@@ -51,6 +61,14 @@ def load_library():
     vp, i32, f32, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, Strides
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, Mask, i32, vp]
+    lib.attn_fwd_masked.restype = i32
+    lib.attn_fwd_varlen_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, S, S, S, S,
+                                           f32, Mask, i32, vp]
+    lib.attn_fwd_varlen_masked.restype = i32
+    lib.attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32,
+                                   ctypes.POINTER(DecodeOpts), vp, ctypes.c_size_t, vp]
+    lib.attn_decode_ex.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, S, S, S, S, f32,
                                     i32, i32, vp]
     lib.attn_fwd_varlen.restype = i32
@@ -115,15 +133,33 @@ def _default_scale(D: int) -> float:
 
 
 _CAUSAL_ALIGN = {"top_left": 1, "bottom_right": 2}
+_ALIGN = {"top_left": 0, "bottom_right": 1}
+
+
+def _mask(causal: bool, causal_align: str, window) -> Mask:
+    """attn_mask for a sliding window (left, right) around each query's
+    diagonal position (-1 leaves a side open); ``causal`` closes the right side
+    at the diagonal."""
+    left, right = (int(window[0]), int(window[1]))
+    if left < -1 or right < -1:
+        raise ValueError("window sides must be >= -1")
+    if causal:
+        if right > 0:
+            raise ValueError("a causal mask has no keys right of the diagonal: window right must be -1 or 0")
+        right = 0
+    return Mask(_ALIGN[causal_align], left, right)
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool, scale: float | None = None,
              return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-             causal_align: str = "top_left"):
+             causal_align: str = "top_left", window=None):
     """Fused attention forward.  q (B,Hq,Nq,D), k/v (B,Hkv,Nkv,D), any strides with stride(-1) == 1.
 
     ``causal_align`` (when ``causal``): "top_left" -- query i sees keys j <= i;
     "bottom_right" -- j <= i + Nkv - Nq (the queries are the last Nq positions).
+    ``window=(left, right)``: a sliding window around each query's diagonal
+    position p (keys p - left .. p + right, -1 leaves a side open), aligned by
+    ``causal_align``; calls attn_fwd_masked.
     Returns ``out`` (B,Hq,Nq,D), or ``(out, lse)`` with lse fp32 (B,Hq,Nq) when ``return_lse``.
     """
     if causal_align not in _CAUSAL_ALIGN:
@@ -142,6 +178,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool,
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D or out.shape != q.shape:
         raise ValueError("shape mismatch between q, k, v and out")
     s = _default_scale(D) if scale is None else float(scale)
+    if window is not None:
+        st = lib.attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None,
+                                 B, Hq, Hkv, Nq, Nkv, D, _strides4(q), _strides4(k), _strides4(v), _strides4(out),
+                                 s, _mask(causal, causal_align, window), code, _stream(q))
+        _check(st, "attn_fwd_masked")
+        return (out, lse) if return_lse else out
     st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       lse.data_ptr() if lse is not None else None,
                       B, Hq, Hkv, Nq, Nkv, D, _strides4(q), _strides4(k), _strides4(v), _strides4(out),
@@ -158,14 +201,15 @@ def _strides_packed(t: torch.Tensor) -> Strides:
 def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int | None = None, *, causal: bool,
                     scale: float | None = None, return_lse: bool = False, out: torch.Tensor | None = None,
-                    lse: torch.Tensor | None = None, causal_align: str = "top_left"):
+                    lse: torch.Tensor | None = None, causal_align: str = "top_left", window=None):
     """Fused attention forward over packed sequences of different lengths.
 
     q (total_q, Hq, D), k/v (total_k, Hkv, D), any strides with stride(-1) == 1;
     cu_seqlens_q / cu_seqlens_k: int32 (B + 1,) device offsets (sequence b owns
     rows [cu[b], cu[b+1])).  ``max_seqlen_q`` bounds every sequence's query
     count; when None it is read from ``cu_seqlens_q`` (a device-to-host copy).
-    ``causal_align`` is per sequence ("bottom_right": j <= i + L_k - L_q).
+    ``causal_align`` is per sequence ("bottom_right": j <= i + L_k - L_q);
+    ``window=(left, right)`` as in ``attn_fwd`` (calls attn_fwd_varlen_masked).
     Returns ``out`` (total_q, Hq, D), or ``(out, lse)`` with lse fp32 (Hq, total_q).
     """
     if causal_align not in _CAUSAL_ALIGN:
@@ -195,6 +239,15 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     _on_gpu(q, k, v, out, cu_seqlens_q, cu_seqlens_k, *([lse] if lse is not None else []))
     code = _dtype_code(q, k, v, out)
     s = _default_scale(D) if scale is None else float(scale)
+    if window is not None:
+        st = lib.attn_fwd_varlen_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None,
+                                        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, int(max_seqlen_q), Tq,
+                                        Tk, Hq, Hkv, D, _strides_packed(q), _strides_packed(k), _strides_packed(v),
+                                        _strides_packed(out), s, _mask(causal, causal_align, window), code,
+                                        _stream(q))
+        _check(st, "attn_fwd_varlen_masked")
+        return (out, lse) if return_lse else out
     st = lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr() if lse is not None else None,
                              cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, int(max_seqlen_q), Tq, Tk,
@@ -219,8 +272,12 @@ def decode_workspace(B: int, Hq: int, Hkv: int, S_max: int, D: int, device) -> t
 
 def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: int, *,
                 scale: float | None = None, workspace: torch.Tensor | None = None, num_splits: int = 0,
-                return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+                return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                window_left: int = -1):
     """Decode one token per (batch, q head) over cache slots [0, cache_len).
+
+    ``window_left`` = w >= 0 keeps only the last w + 1 slots (the query is the
+    token in slot cache_len - 1); calls attn_decode_ex.
 
     q (B,Hq,D); caches (B,Hkv,S_max,D).  ``workspace`` is scratch of at least
     ``attn_decode_workspace_bytes`` bytes (see ``decode_workspace``); if omitted
@@ -242,6 +299,15 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, c
     if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D or out.shape != q.shape:
         raise ValueError("shape mismatch between q, caches and out")
     s = _default_scale(D) if scale is None else float(scale)
+    if window_left != -1:
+        opts = DecodeOpts(None, None, 0, 0, 0, int(window_left))
+        st = lib.attn_decode_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, S_max, int(cache_len), D,
+                                _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out), s, code,
+                                int(num_splits), ctypes.byref(opts), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(q))
+        _check(st, "attn_decode_ex")
+        return (out, lse) if return_lse else out
     st = lib.attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                          lse.data_ptr() if lse is not None else None,
                          B, Hq, Hkv, S_max, int(cache_len), D,
@@ -255,8 +321,10 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, c
 def attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_lens: torch.Tensor,
                        max_cache_len: int | None = None, *, scale: float | None = None,
                        workspace: torch.Tensor | None = None, num_splits: int = 0, return_lse: bool = False,
-                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None, window_left: int = -1):
     """Decode one token per (batch, q head); batch element b attends over slots [0, cache_lens[b]).
+
+    ``window_left`` = w >= 0 keeps each sequence's last w + 1 slots (attn_decode_ex).
 
     ``cache_lens``: int32 tensor of B lengths on the same GPU (read by the kernel,
     no host sync; each is clamped to [0, max_cache_len]).  ``max_cache_len``:
@@ -281,6 +349,15 @@ def attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D or out.shape != q.shape:
         raise ValueError("shape mismatch between q, caches and out")
     s = _default_scale(D) if scale is None else float(scale)
+    if window_left != -1:
+        opts = DecodeOpts(cache_lens.data_ptr(), None, 0, 0, 0, int(window_left))
+        st = lib.attn_decode_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, S_max, mcl, D,
+                                _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out), s, code,
+                                int(num_splits), ctypes.byref(opts), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(q))
+        _check(st, "attn_decode_ex")
+        return (out, lse) if return_lse else out
     st = lib.attn_decode_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                                 lse.data_ptr() if lse is not None else None,
                                 B, Hq, Hkv, S_max, cache_lens.data_ptr(), mcl, D,
@@ -317,8 +394,8 @@ def _int32_vec(t: torch.Tensor, n: int, what: str):
 def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                       cache_lens: torch.Tensor, max_cache_len: int | None = None, *, scale: float | None = None,
                       workspace: torch.Tensor | None = None, num_splits: int = 0, return_lse: bool = False,
-                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """Decode over a paged KV cache.
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None, window_left: int = -1):
+    """Decode over a paged KV cache (``window_left`` as in ``attn_decode_varlen``).
 
     q (B, Hq, D); k_pages, v_pages (num_pages, Hkv, page_size, D), any strides
     with stride(-1) == 1 (a (num_pages, page_size, Hkv, D) pool passes as
@@ -350,6 +427,15 @@ def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
     _on_gpu(q, k_pages, v_pages, out, block_table, cache_lens, workspace, *([lse] if lse is not None else []))
     code = _dtype_code(q, k_pages, v_pages, out)
     s = _default_scale(D) if scale is None else float(scale)
+    if window_left != -1:
+        opts = DecodeOpts(cache_lens.data_ptr(), block_table.data_ptr(), mbps, ps, P, int(window_left))
+        st = lib.attn_decode_ex(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, 0, int(max_cache_len), D,
+                                _strides3(q), _strides4(k_pages), _strides4(v_pages), _strides3(out), s, code,
+                                int(num_splits), ctypes.byref(opts), workspace.data_ptr(), workspace.numel(),
+                                _stream(q))
+        _check(st, "attn_decode_ex")
+        return (out, lse) if return_lse else out
     st = lib.attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, P, ps,
                                block_table.data_ptr(), mbps, cache_lens.data_ptr(), int(max_cache_len), D,

@@ -86,16 +86,38 @@ const char* attn_status_string(attn_status s) {
   return "unknown status";
 }
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int Hq, int Hkv, int Nq, int Nkv, int D,
-                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
-                     float scale, int causal, attn_dtype dtype, void* stream) {
+// the kernels' mask: mode 0 none, 1 causal, 2 band; the diagonal aligned
+// top-left (query i at key position i) or bottom-right (i + Nkv - Nq)
+struct MaskSpec {
+  int mode, bottom_right, left, right;
+};
+
+// attn_fwd's causal argument as a mask (mode -1: not a valid value)
+static MaskSpec mask_of_causal(int causal) {
+  if (causal < ATTN_CAUSAL_NONE || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return MaskSpec{-1, 0, -1, -1};
+  return MaskSpec{causal != ATTN_CAUSAL_NONE ? 1 : 0, causal == ATTN_CAUSAL_BOTTOM_RIGHT ? 1 : 0, -1,
+                  causal != ATTN_CAUSAL_NONE ? 0 : -1};
+}
+
+// an attn_mask as the kernels' mask (mode -1: not a valid value)
+static MaskSpec mask_of(attn_mask m) {
+  if ((m.align != ATTN_ALIGN_TOP_LEFT && m.align != ATTN_ALIGN_BOTTOM_RIGHT) || m.window_left < -1 ||
+      m.window_right < -1)
+    return MaskSpec{-1, 0, -1, -1};
+  const int mode = (m.window_left < 0 && m.window_right < 0) ? 0 : (m.window_left < 0 && m.window_right == 0) ? 1 : 2;
+  return MaskSpec{mode, m.align == ATTN_ALIGN_BOTTOM_RIGHT ? 1 : 0, m.window_left, m.window_right};
+}
+
+static attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                            attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            float scale, MaskSpec mk, attn_dtype dtype, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
-  if (causal < ATTN_CAUSAL_NONE || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_ERR_UNSUPPORTED;
+  if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
@@ -124,8 +146,10 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   const int64_t per_xcd = nblocks / 8;
   const int64_t per_unit = (int64_t)a.group * nqb;
   a.remap = (nblocks % 8 == 0) && per_xcd > 0 &&
-            ((per_xcd % per_unit == 0) || (!causal && per_unit % per_xcd == 0));
-  a.causal_off = (causal == ATTN_CAUSAL_BOTTOM_RIGHT) ? Nkv - Nq : 0;
+            ((per_xcd % per_unit == 0) || (mk.mode == 0 && per_unit % per_xcd == 0));
+  a.causal_off = mk.bottom_right ? Nkv - Nq : 0;
+  a.win_left = mk.left;
+  a.win_right = mk.right;
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
   a.q_bytes = slice_bytes(Nq, sq.n, D);
@@ -135,22 +159,37 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   a.units = B * Hkv;
 
   const hipError_t e =
-      attn::launch_prefill(a, D, dtype == ATTN_BF16, causal != 0, false, static_cast<hipStream_t>(stream));
+      attn::launch_prefill(a, D, dtype == ATTN_BF16, mk.mode, false, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int max_seqlen_q,
-                            int total_q, int total_k, int Hq, int Hkv, int D,
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                     float scale, int causal, attn_dtype dtype, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, sq, sk, sv, so, scale, mask_of_causal(causal), dtype,
+                  stream);
+}
+
+attn_status attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                             attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
-                            float scale, int causal, attn_dtype dtype, void* stream) {
+                            float scale, attn_mask mask, attn_dtype dtype, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, sq, sk, sv, so, scale, mask_of(mask), dtype, stream);
+}
+
+static attn_status fwd_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                   int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int D,
+                                   attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                                   float scale, MaskSpec mk, attn_dtype dtype, void* stream) {
   if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seqlen_q <= 0 || total_q <= 0 || total_k < 0 || D <= 0)
     return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
-  if (causal < ATTN_CAUSAL_NONE || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_ERR_UNSUPPORTED;
+  if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
   // packed (token, head, dim) views: the batch stride is unused and not checked
   attn_strides sq3 = sq, sk3 = sk, sv3 = sv, so3 = so;
   sq3.b = sk3.b = sv3.b = so3.b = 0;
@@ -186,13 +225,33 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   a.total_q = total_q;
   a.total_k = total_k;
   a.units = (int)units;
-  a.causal_br = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? 1 : 0;
+  a.causal_br = mk.bottom_right;
+  a.win_left = mk.left;
+  a.win_right = mk.right;
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
 
   const hipError_t e =
-      attn::launch_prefill(a, D, dtype == ATTN_BF16, causal != 0, true, static_cast<hipStream_t>(stream));
+      attn::launch_prefill(a, D, dtype == ATTN_BF16, mk.mode, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int max_seqlen_q,
+                            int total_q, int total_k, int Hq, int Hkv, int D,
+                            attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            float scale, int causal, attn_dtype dtype, void* stream) {
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, total_q, total_k, Hq, Hkv,
+                         D, sq, sk, sv, so, scale, mask_of_causal(causal), dtype, stream);
+}
+
+attn_status attn_fwd_varlen_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                   int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int D,
+                                   attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                                   float scale, attn_mask mask, attn_dtype dtype, void* stream) {
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, total_q, total_k, Hq, Hkv,
+                         D, sq, sk, sv, so, scale, mask_of(mask), dtype, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D) {
@@ -217,7 +276,8 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
                         int B, int Hq, int Hkv, int S_max, int cache_len, const int32_t* lens, int D,
                         attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
                         float scale, attn_dtype dtype, int num_splits,
-                        void* workspace, size_t workspace_bytes, void* stream, const PagedSpec* pg = nullptr) {
+                        void* workspace, size_t workspace_bytes, void* stream, const PagedSpec* pg = nullptr,
+                        int window_left = -1) {
   if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0 || cache_len < 1 || cache_len > S_max || num_splits < 0) return ATTN_ERR_SHAPE;
@@ -237,7 +297,20 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
   // B * Hkv goes in grid x (limit 2^31 - 1) or z (limit 65535); head groups in y
   if ((int64_t)B * Hkv > 0x7fffffff || g.hgroups > 65535) return ATTN_ERR_SHAPE;
 
-  const int tiles = (cache_len + kDecodeTile - 1) / kDecodeTile;
+  if (window_left < -1) return ATTN_ERR_SHAPE;
+  // tiles a chunk grid must cover: with a window a sequence's slots start at
+  // the tile holding slot len - 1 - window_left, so at most window_left + 1
+  // slots plus that tile's lead-in are read
+  int tiles = (cache_len + kDecodeTile - 1) / kDecodeTile;
+  if (window_left >= 0) {
+    if (!lens) {
+      const int kbeg = (cache_len - 1 - window_left > 0 ? cache_len - 1 - window_left : 0) & ~(kDecodeTile - 1);
+      tiles = (cache_len - kbeg + kDecodeTile - 1) / kDecodeTile;
+    } else {
+      const int64_t span = ((int64_t)window_left + 2 * kDecodeTile - 1) / kDecodeTile;
+      if (span < tiles) tiles = (int)span;
+    }
+  }
   // default: enough chunks for ~kDecodeTargetWorkgroups workgroups (two per CU,
   // each with two 128-row tiles in flight), at most max_splits per (batch, kv
   // head, head group)
@@ -274,6 +347,7 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
   a.part = static_cast<float*>(workspace);
+  a.window_left = window_left;
   if (pg) {
     a.block_table = pg->table;
     a.mbps = pg->mbps;
@@ -334,6 +408,27 @@ attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_
   const PagedSpec pg{block_table, max_pages_per_seq, lg, num_pages};
   return decode_impl(q, k_pages, v_pages, o, lse, B, Hq, Hkv, max_cache_len, max_cache_len, cache_lens, D, sq, skp,
                      svp, so, scale, dtype, num_splits, workspace, workspace_bytes, stream, &pg);
+}
+
+attn_status attn_decode_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+                           attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                           float scale, attn_dtype dtype, int num_splits, const attn_decode_opts* opts,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!opts) return ATTN_ERR_NULL;
+  if (opts->block_table) {
+    if (!opts->cache_lens) return ATTN_ERR_NULL;
+    if (opts->num_pages <= 0 || opts->max_pages_per_seq <= 0 || cache_len <= 0) return ATTN_ERR_SHAPE;
+    const int lg = page_log2(opts->page_size);
+    if (lg < 0) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)cache_len > (int64_t)opts->max_pages_per_seq * opts->page_size) return ATTN_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(opts->block_table) & 3u) return ATTN_ERR_UNSUPPORTED;
+    const PagedSpec pg{opts->block_table, opts->max_pages_per_seq, lg, opts->num_pages};
+    return decode_impl(q, k, v, o, lse, B, Hq, Hkv, cache_len, cache_len, opts->cache_lens, D, sq, sk, sv, so,
+                       scale, dtype, num_splits, workspace, workspace_bytes, stream, &pg, opts->window_left);
+  }
+  return decode_impl(q, k, v, o, lse, B, Hq, Hkv, S_max, cache_len, opts->cache_lens, D, sq, sk, sv, so, scale,
+                     dtype, num_splits, workspace, workspace_bytes, stream, nullptr, opts->window_left);
 }
 
 attn_status kv_cache_write_paged(void* k_pages, void* v_pages, const void* k_new, const void* v_new,

@@ -53,8 +53,9 @@ __device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
 }
 
 // MODE 0: one length for every sequence; 1: per-sequence lengths; 2: per-sequence
-// lengths over a paged cache
-template <int D, bool BF16, int MODE>
+// lengths over a paged cache.  WINDOW: a sliding window hides the slots before
+// len - 1 - window_left (without it none of that code is compiled in)
+template <int D, bool BF16, int MODE, bool WINDOW>
 __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel(const DecodeArgs a) {
   constexpr bool VARLEN = MODE >= 1;
   constexpr bool PAGED = MODE == 2;
@@ -100,7 +101,10 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   // Without per-sequence lengths every chunk is non-empty and none of this is
   // compiled in (the test would delay the first loads).
   const int seq_len = VARLEN ? min(max(a.lens[b], 0), a.cache_len) : a.cache_len;
-  const int k0 = split * a.rows_per_split;
+  // sliding window: slots below kvis are hidden and never read; chunks start
+  // at the tile that holds kvis
+  const int kvis = WINDOW ? max(0, seq_len - 1 - a.window_left) : 0;
+  const int k0 = (kvis & ~(kDT - 1)) + split * a.rows_per_split;
   const int k1 = min(seq_len, k0 + a.rows_per_split);
   if (VARLEN && a.nsplit > 1 && k0 >= seq_len) return;  // uniform over the workgroup
 
@@ -165,11 +169,13 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   auto load_tile = [&](Tile& T, int kb) {
     if constexpr (PAGED) {
       // Slot r lives in page block_table[b][r >> lg_ps], row r & (page size - 1).
-      // Rows past the chunk re-read its last row (finite data of this sequence;
-      // their scores are masked, their P is 0), so no load is predicated.  A
+      // Rows past the chunk re-read its last row and rows before the window
+      // its first visible one (their scores are masked, their P is 0), so no
+      // load is predicated and no hidden slot or its page is touched.  A
       // wave's 32 K rows and a (wave, j) group of V rows span at most two pages
       // (page size >= 16, groups aligned): their page ids are uniform loads.
       const int last = k1 - 1;
+      auto row = [&](int r) __attribute__((always_inline)) { return min(WINDOW ? max(r, kvis) : r, last); };
       const int wu = __builtin_amdgcn_readfirstlane(w);
       const int32_t* tb = a.block_table + (int64_t)b * a.mbps;
       const int rmask = (1 << a.lg_ps) - 1;
@@ -177,10 +183,10 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
         return (int64_t)min(max(tb[r >> a.lg_ps], 0), a.num_pages - 1);
       };
       const int kw0 = kb + 32 * wu;
-      const int64_t kp_lo = page(min(kw0, last)), kp_hi = page(min(kw0 + 16, last));
+      const int64_t kp_lo = page(row(kw0)), kp_hi = page(row(kw0 + 16));
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
-        const int rr = min(kb + krow + 4 * gi, last);
+        const int rr = row(kb + krow + 4 * gi);
         const int64_t pg = rr >= kw0 + 16 ? kp_hi : kp_lo;
         const uint16_t* kp = kbase + pg * a.skb + (int64_t)(rr & rmask) * a.skn + 8 * rg;
 #pragma unroll
@@ -190,11 +196,11 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         const int vs = kb + VROWS * (wu + 4 * j);
-        const int64_t vp_lo = page(min(vs, last)), vp_hi = page(min(vs + 16, last));
+        const int64_t vp_lo = page(row(vs)), vp_hi = page(row(vs + 16));
         const int g0 = kb + 4 * vkvg[j];
         const uint16_t* vb = vbase + (g0 >= vs + 16 ? vp_hi : vp_lo) * a.svb + 8 * vdc[j];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) T.v[j][r] = load16(vb + (int64_t)(min(g0 + r, last) & rmask) * a.svn);
+        for (int r = 0; r < 4; ++r) T.v[j][r] = load16(vb + (int64_t)(row(g0 + r) & rmask) * a.svn);
       }
       return;
     }
@@ -202,6 +208,22 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
     const int64_t rows = k1 - kb;  // keys of this split from kb on
     const auto rk = make_rsrc(kbase + ko, clamp_bytes(((rows - 1) * a.skn + D) * 2));
     const auto rv = make_rsrc(vbase + vo, clamp_bytes(((rows - 1) * a.svn + D) * 2));
+    if (WINDOW && kb < kvis) {
+      // the window's lead-in tile: rows before kvis re-read row kvis (their
+      // scores are masked, their P is 0), so hidden slots are never read
+      const int f = kvis - kb;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          T.kf[gi][ks] = bload16(rk, max(krow + 4 * gi, f) * (int32_t)a.skn * 2 + 16 * rg + 64 * ks);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          T.v[j][r] = bload16(rv, max(4 * vkvg[j] + r, f) * (int32_t)a.svn * 2 + 16 * vdc[j]);
+      return;
+    }
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
@@ -225,7 +247,7 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
     }
     __syncthreads();
     const int kw0 = kb + 32 * w;  // first key of this wave
-    if (kw0 >= k1) return;
+    if (kw0 >= k1 || (WINDOW && kw0 + 32 <= kvis)) return;  // no key of this wave in range
     f32x4 s0 = f32x4{}, s1 = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -233,6 +255,14 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
       s1 = mfma_16x16x32<BF16>(T.kf[1][ks], qf[ks], s1);
     }
     // lane (col, rg): s0[e] is key kw0 + 8*rg + e, s1[e] is key kw0 + 8*rg + 4 + e
+    if (WINDOW && kw0 < kvis) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kw0 + 8 * rg + e;
+        s0[e] = (key >= kvis) ? s0[e] : -INFINITY;
+        s1[e] = (key + 4 >= kvis) ? s1[e] : -INFINITY;
+      }
+    }
     if (kw0 + 32 > k1) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -374,7 +404,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
   int ns = a.nsplit;
   if (VARLEN) {
     const int seq_len = min(max(a.lens[b], 0), a.cache_len);
-    ns = min(ns, (seq_len + a.rows_per_split - 1) / a.rows_per_split);
+    const int kbeg = (a.window_left >= 0 ? max(0, seq_len - 1 - a.window_left) : 0) & ~(kDT - 1);
+    ns = min(ns, (seq_len - kbeg + a.rows_per_split - 1) / a.rows_per_split);
   }
   const int64_t slot = (int64_t)unit * a.hgroups + hgi;
   const float* base = a.part + (slot * a.max_splits * a.heads_per_wg + hx) * HP;
@@ -423,7 +454,10 @@ template <int D, bool BF16, int MODE>
 hipError_t launch_v(const DecodeArgs& a, int B, hipStream_t stream) {
   const unsigned units = (unsigned)(B * a.Hkv);
   const dim3 g1 = a.unit_fast ? dim3(units, a.hgroups, a.nsplit) : dim3(a.nsplit, a.hgroups, units);
-  hipLaunchKernelGGL((decode_kernel<D, BF16, MODE>), g1, dim3(256), 0, stream, a);
+  if (a.window_left >= 0)
+    hipLaunchKernelGGL((decode_kernel<D, BF16, MODE, true>), g1, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, BF16, MODE, false>), g1, dim3(256), 0, stream, a);
   if (a.nsplit > 1) {
     const dim3 g2 = a.unit_fast ? dim3(units, a.hgroups, a.heads_per_wg) : dim3(a.heads_per_wg, a.hgroups, units);
     hipLaunchKernelGGL((decode_combine_kernel<D, BF16, (MODE >= 1)>), g2, dim3(256), 0, stream, a);

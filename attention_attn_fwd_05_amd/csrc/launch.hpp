@@ -36,9 +36,13 @@ struct FwdArgs {
   int total_q, total_k;
   int units;      // B * Hkv
   int causal_br;  // causal offset per sequence: 1 = L_k - L_q, 0 = 0
+  // band mask (mask mode 2): query i sees keys i + off - win_left <= j <=
+  // i + off + win_right; -1 leaves that side open
+  int win_left, win_right;
 };
 
-hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool varlen, hipStream_t stream);
+// mask: 0 none, 1 causal, 2 band
+hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, int mask, bool varlen, hipStream_t stream);
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -66,6 +70,9 @@ struct DecodeArgs {
   // and skb / svb are the page strides
   const int32_t* block_table;
   int mbps, lg_ps, num_pages;
+  // sliding window: -1 none; w >= 0 keeps slots >= len - 1 - w (the query is
+  // the last slot); chunks then start at the 128-slot tile holding that slot
+  int window_left;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool bf16, hipStream_t stream);

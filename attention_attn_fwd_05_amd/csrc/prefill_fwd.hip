@@ -167,8 +167,12 @@ __device__ __forceinline__ void barrier_nofence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+// MASK 0: every key below Nkv; 1: causal (j <= i + off); 2: a band of keys
+// i + off - win_left <= j <= i + off + win_right (either side may be open)
+template <int D, bool BF16, int MASK, bool VARLEN>
 __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdArgs a) {
+  constexpr bool CAUSAL = MASK == 1;
+  constexpr bool BAND = MASK == 2;
   using L = PrefillLds<D>;
   constexpr int KS = D / 16;        // k-steps of the score MFMA
   constexpr int DT = D / 32;        // 32-wide head-dim tiles of O
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   }
   int qb = rem / a.group;
   const int hg = rem - qb * a.group;
-  if (CAUSAL) qb = a.nqb - 1 - qb;  // longest (latest) query blocks first
+  if (MASK != 0) qb = a.nqb - 1 - qb;  // longest (latest) query blocks first
   const int b = unit / a.Hkv;
   const int kvh = unit - b * a.Hkv;
   const int h = kvh * a.group + hg;  // q heads [kvh*group, (kvh+1)*group) share kv head kvh
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   //      A packed sequence's offsets are clamped into [previous offset, total],
   //      so no access leaves the packed tensors whatever the offsets hold.
   int Nq = a.Nq, Nkv = a.Nkv;
-  int off = CAUSAL ? a.causal_off : 0;
+  int off = MASK != 0 ? a.causal_off : 0;
   const uint16_t *qbase, *kbase, *vbase;
   uint16_t* obase;
   float* lbase;
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
     const int s1 = min(max(a.cu_k[b + 1], s0), a.total_k);
     Nq = t1 - t0;
     Nkv = s1 - s0;
-    if (CAUSAL) off = a.causal_br ? Nkv - Nq : 0;  // from the sequence's own lengths
+    if (MASK != 0) off = a.causal_br ? Nkv - Nq : 0;  // from the sequence's own lengths
     Nq = min(Nq, a.Nq);    // rows past the caller's max_seqlen_q bound are not computed
     if (q0 >= Nq) return;  // whole workgroup: block past this sequence's queries
     qbase = a.q + (int64_t)t0 * a.sqn + (int64_t)h * a.sqh;
@@ -259,12 +263,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   }
 
   // causal: query row i sees keys j <= i + off (off = 0 top-left, Nkv - Nq
-  // bottom-right); keys past the block's last row + off are never visited
-  const int kv_end = CAUSAL ? max(0, min(Nkv, q0 + kBM + off)) : Nkv;
+  // bottom-right); keys past the block's last row + off are never visited.
+  // band: row i sees i + off - WL <= j <= i + off + WR (an open side is a
+  // bound no key reaches); tiles wholly left of the block's first row's band
+  // or right of its last row's are never visited
+  constexpr int kOpen = 1 << 30;
+  const int WL = BAND ? (a.win_left < 0 ? kOpen : a.win_left) : 0;
+  const int WR = BAND ? (a.win_right < 0 ? kOpen : a.win_right) : 0;
+  const int kv_end = CAUSAL ? max(0, min(Nkv, q0 + kBM + off))
+                            : (BAND ? max(0, min(Nkv, q0 + kBM + off + WR)) : Nkv);
   const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int t_begin = BAND ? min(max(0, q0 + off - WL) / kBN, ntiles) : 0;
   // tiles every row of this block sees in full (no mask): below the block's
-  // diagonal and before the key tail
-  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, Nkv)) / kBN : Nkv / kBN;
+  // diagonal (band: and at or past its last row's lower bound) and before the
+  // key tail
+  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, Nkv)) / kBN
+                            : (BAND ? max(0, min(Nkv, q0 + off + WR + 1)) / kBN : Nkv / kBN);
+  const int full_lo = BAND ? (max(0, q0 + kBM - 1 + off - WL) + kBN - 1) / kBN : 0;
 
   // ---- DMA geometry: wave w fills 1 KiB blocks NB*w .. NB*w+NB-1 of each
   //      K and V tile; lane l of block bk writes row RPB*bk + l/C, slot l%C,
@@ -321,6 +336,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   float l = 0.f;
   const float c = a.c;  // > 0
   const int wq_hi = q0 + 32 * w + 31 + off;  // last key any of this wave's rows sees
+  const int wq_lo = q0 + 32 * w + off;       // band: this wave's first row's position
 
   // instruction order hints for the two MFMA phases of a tile (masks: 0x008
   // MFMA, 0x100 LDS read, 0x002 VALU): LDS reads run several MFMAs ahead of
@@ -355,7 +371,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
     bool act1 = true;
     if constexpr (MASKED) {
       if (kb >= Nkv || (CAUSAL && kb > wq_hi)) return;  // whole tile above this wave's rows
-      act1 = kb + 32 < Nkv && (!CAUSAL || kb + 32 <= wq_hi);
+      if (BAND && (kb > wq_hi + WR || kb + kBN - 1 < wq_lo - WL)) return;  // outside this wave's band
+      act1 = kb + 32 < Nkv && (!CAUSAL || kb + 32 <= wq_hi) && (!BAND || kb + 32 <= wq_hi + WR);
     }
     // S^T = K Q^T for the two 32-key subtiles; score register e of lane
     // (n, hh) is key 8*(e/4) + 4*hh + e%4 of its subtile
@@ -376,8 +393,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
       for (int e = 0; e < 16; ++e) {
         const int kv0 = kb + 8 * (e >> 2) + 4 * hh + (e & 3);
         const int kv1 = kv0 + 32;
-        const bool vis0 = kv0 < Nkv && (!CAUSAL || kv0 <= qrow + off);
-        const bool vis1 = act1 && kv1 < Nkv && (!CAUSAL || kv1 <= qrow + off);
+        const bool vis0 = kv0 < Nkv && (!CAUSAL || kv0 <= qrow + off) &&
+                          (!BAND || (kv0 >= qrow + off - WL && kv0 <= qrow + off + WR));
+        const bool vis1 = act1 && kv1 < Nkv && (!CAUSAL || kv1 <= qrow + off) &&
+                          (!BAND || (kv1 >= qrow + off - WL && kv1 <= qrow + off + WR));
         s0[e] = vis0 ? s0[e] : -INFINITY;
         s1[e] = vis1 ? s1[e] : -INFINITY;
       }
@@ -461,28 +480,36 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
       __builtin_amdgcn_s_waitcnt(kWaitAll);
     barrier_nofence();
   };
-  if (ntiles > 0) dma_tile(0, 0);
-  if (ntiles > 1) dma_tile(1, 1);
-  if (ntiles > 1)
+  // tile t sits in ring stage (t - t_begin) % 3
+  if (t_begin < ntiles) dma_tile(t_begin, 0);
+  if (t_begin + 1 < ntiles) dma_tile(t_begin + 1, 1);
+  if (t_begin + 1 < ntiles)
     __builtin_amdgcn_s_waitcnt(kWaitAllButTile);
   else
     __builtin_amdgcn_s_waitcnt(kWaitAll);
   barrier_nofence();
-  int t = 0;
+  int t = t_begin;
+  auto masked_step = [&](int tt) __attribute__((always_inline)) {
+    const int r = (tt - t_begin) % 3;
+    if (r == 0)
+      step(tt, st0{}, mask_t{});
+    else if (r == 1)
+      step(tt, st1{}, mask_t{});
+    else
+      step(tt, st2{}, mask_t{});
+  };
+  if constexpr (BAND) {
+    // band: the masked tiles left of the full ones, and as many more as put
+    // the first full triple in stage 0
+    const int f_start = t_begin + 3 * ((max(full_lo - t_begin, 0) + 2) / 3);
+    for (; t < f_start && t < ntiles; ++t) masked_step(t);
+  }
   for (; t + 2 < n_full; t += 3) {
     step(t, st0{}, full_t{});
     step(t + 1, st1{}, full_t{});
     step(t + 2, st2{}, full_t{});
   }
-  for (; t < ntiles; ++t) {
-    const int r = t % 3;
-    if (r == 0)
-      step(t, st0{}, mask_t{});
-    else if (r == 1)
-      step(t, st1{}, mask_t{});
-    else
-      step(t, st2{}, mask_t{});
-  }
+  for (; t < ntiles; ++t) masked_step(t);
 
   // ---- epilogue: O = O^T / l, cast, store; lse = (m + log2 l) ln 2
   l = sum_xor32(l);
@@ -503,32 +530,33 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, int MASK, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, CAUSAL, VARLEN>), dim3(a.nblocks), dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN>), dim3(a.nblocks), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, bool BF16, bool VARLEN>
-hipError_t launch_c(const FwdArgs& a, bool causal, hipStream_t stream) {
-  return causal ? launch_t<D, BF16, true, VARLEN>(a, stream) : launch_t<D, BF16, false, VARLEN>(a, stream);
+hipError_t launch_c(const FwdArgs& a, int mask, hipStream_t stream) {
+  if (mask == 2) return launch_t<D, BF16, 2, VARLEN>(a, stream);
+  return mask == 1 ? launch_t<D, BF16, 1, VARLEN>(a, stream) : launch_t<D, BF16, 0, VARLEN>(a, stream);
 }
 
 template <int D, bool VARLEN>
-hipError_t launch_d(const FwdArgs& a, bool bf16, bool causal, hipStream_t stream) {
-  return bf16 ? launch_c<D, true, VARLEN>(a, causal, stream) : launch_c<D, false, VARLEN>(a, causal, stream);
+hipError_t launch_d(const FwdArgs& a, bool bf16, int mask, hipStream_t stream) {
+  return bf16 ? launch_c<D, true, VARLEN>(a, mask, stream) : launch_c<D, false, VARLEN>(a, mask, stream);
 }
 
 template <bool VARLEN>
-hipError_t launch_v(const FwdArgs& a, int D, bool bf16, bool causal, hipStream_t stream) {
-  if (D == 64) return launch_d<64, VARLEN>(a, bf16, causal, stream);
-  return launch_d<128, VARLEN>(a, bf16, causal, stream);
+hipError_t launch_v(const FwdArgs& a, int D, bool bf16, int mask, hipStream_t stream) {
+  if (D == 64) return launch_d<64, VARLEN>(a, bf16, mask, stream);
+  return launch_d<128, VARLEN>(a, bf16, mask, stream);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, bool causal, bool varlen, hipStream_t stream) {
-  return varlen ? launch_v<true>(a, D, bf16, causal, stream) : launch_v<false>(a, D, bf16, causal, stream);
+hipError_t launch_prefill(const FwdArgs& a, int D, bool bf16, int mask, bool varlen, hipStream_t stream) {
+  return varlen ? launch_v<true>(a, D, bf16, mask, stream) : launch_v<false>(a, D, bf16, mask, stream);
 }
 
 }  // namespace attn

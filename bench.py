@@ -26,12 +26,13 @@ FETCH_SIZE and WRITE_SIZE counters measured (scaled by a plain copy's reading),
 taken from the committed summaries under profiles/; null once the kernel
 sources differ from the ones those counters were taken with.
 
-The default run also times four widened workloads (not the headline):
+The default run also times five widened workloads (not the headline):
 decode with per-sequence cache lengths over a 16-sequence batch, the same
 batch over a paged cache (16-slot pages in a shuffled pool), a chunked
 prefill (1024 queries at the end of an 8192-token context, causal aligned
-bottom-right) and a packed prefill of 16 sequences of seeded lengths up to
-4096; they are printed under "widened".
+bottom-right), a packed prefill of 16 sequences of seeded lengths up to
+4096, and a causal sliding window of 4096 keys on the 8192-token serving
+shape; they are printed under "widened".
 
 Flags: --only prefill|decode|copy runs just that launch (for rocprofv3 runs),
 --no-cpu skips the oracle baseline.  Prints one JSON line.
@@ -346,6 +347,29 @@ def main():
             "ms_per_launch": round(pt, 4), "tflops": round(vp.flops() / (pt * 1e-3) / 1e12, 1),
             "frac_of_2500_tflops": round(vp.flops() / (pt * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
         del pq, pk, pv, po
+        # causal sliding window of 4096 keys on the serving shape (N = 8192)
+        wc = W.serving(8192, True)
+        wq, wk, wv = (t.to(dev) for t in W.prefill_inputs(wc))
+        wo = torch.empty_like(wq)
+        wwin = 4095
+        wpairs = sum(min(i, wwin) + 1 for i in range(wc.Nq))
+        wflops = 4 * wc.D * wc.B * wc.Hq * wpairs
+        for _ in range(3):
+            A.attn_fwd(wq, wk, wv, causal=True, window=(wwin, -1), scale=wc.softmax_scale, out=wo)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0.record(stream)
+        for _ in range(10):
+            A.attn_fwd(wq, wk, wv, causal=True, window=(wwin, -1), scale=wc.softmax_scale, out=wo)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wt = e0.elapsed_time(e1) / 10
+        widened["prefill_window"] = {
+            "workload": "serve_n8192_d128_causal_window4096", "B": wc.B, "Hq": wc.Hq, "Hkv": wc.Hkv, "N": wc.Nq,
+            "D": wc.D, "window_left": wwin, "flops_per_launch": wflops, "ms_per_launch": round(wt, 4),
+            "tflops": round(wflops / (wt * 1e-3) / 1e12, 1),
+            "frac_of_2500_tflops": round(wflops / (wt * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+        del wq, wk, wv, wo
 
     # context: achievable HBM rate of a plain 256 MiB device copy (read + write)
     copy_gbs = None

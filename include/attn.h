@@ -60,6 +60,25 @@ enum {
                                    prefill, multi-token verification) */
 };
 
+/* alignment of a mask's diagonal: query i sits at key position p = i + off */
+enum {
+  ATTN_ALIGN_TOP_LEFT = 0,     /* off = 0 */
+  ATTN_ALIGN_BOTTOM_RIGHT = 1  /* off = Nkv - Nq (per sequence for packed batches) */
+};
+
+/*
+ * A band mask around each query's position p: key j is visible iff
+ * p - window_left <= j <= p + window_right (and j < Nkv); -1 leaves a side
+ * open.  {align, -1, 0} is the causal mask ([P1] step 5c with align top-left),
+ * {align, -1, -1} no mask, {align, w - 1, 0} a causal sliding window of w keys
+ * ([P1] "Use this when": windowed attention; [P3] deferred scope).
+ */
+typedef struct {
+  int32_t align;         /* ATTN_ALIGN_TOP_LEFT or ATTN_ALIGN_BOTTOM_RIGHT */
+  int32_t window_left;   /* >= -1 */
+  int32_t window_right;  /* >= -1 */
+} attn_mask;
+
 /*
  * attn_fwd -- O = softmax(scale * Q K^T + mask) V, one fused kernel.
  *
@@ -89,6 +108,18 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                      attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
                      float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * attn_fwd_masked -- attn_fwd with a band mask (attn_mask) in place of the
+ * causal argument.  Tiles wholly outside the band of a block's rows are never
+ * visited on either side.  Rows that see no key get o = 0 and lse = -inf.
+ * Other arguments, layouts and errors as attn_fwd; an align outside the enum
+ * or a window bound below -1 gives ATTN_ERR_UNSUPPORTED.
+ */
+attn_status attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                            attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            float scale, attn_mask mask, attn_dtype dtype, void* stream);
 
 /*
  * attn_fwd_varlen -- attn_fwd over a batch of packed sequences of different
@@ -126,6 +157,17 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             int total_q, int total_k, int Hq, int Hkv, int D,
                             attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
                             float scale, int causal, attn_dtype dtype, void* stream);
+
+/*
+ * attn_fwd_varlen_masked -- attn_fwd_varlen with a band mask (attn_mask); the
+ * diagonal of each sequence follows mask.align with that sequence's own
+ * lengths.  Otherwise as attn_fwd_varlen and attn_fwd_masked.
+ */
+attn_status attn_fwd_varlen_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                                   int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int D,
+                                   attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                                   float scale, attn_mask mask, attn_dtype dtype, void* stream);
 
 /*
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode needs
@@ -215,6 +257,38 @@ attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_
                               attn_strides sq, attn_strides skp, attn_strides svp, attn_strides so,
                               float scale, attn_dtype dtype, int num_splits,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Options of attn_decode_ex: which cache form, and an optional sliding window. */
+typedef struct {
+  const int32_t* cache_lens;   /* DEVICE int32 (B), or NULL: every sequence has cache_len slots */
+  const int32_t* block_table;  /* DEVICE int32 (B, max_pages_per_seq), or NULL: contiguous caches */
+  int32_t max_pages_per_seq;   /* paged caches only */
+  int32_t page_size;           /* paged caches only: a power of two, 16 .. 2^20 */
+  int32_t num_pages;           /* paged caches only */
+  int32_t window_left;         /* -1: every slot; w >= 0: only slots >= len - 1 - w */
+} attn_decode_opts;
+
+/*
+ * attn_decode_ex -- attn_decode, attn_decode_varlen and attn_decode_paged in
+ * one entry point, with an optional sliding window ([P1] "Use this when":
+ * windowed attention; [P3] deferred scope).  The query of sequence b is the
+ * token in its last slot, len - 1 (as after kv_cache_write of that token), so
+ * a window of w keeps the last w + 1 slots; slots before them (and, paged, the
+ * block-table entries and pages that hold only such slots) are never read.
+ *   cache_lens NULL, block_table NULL: as attn_decode (cache_len for all, caches
+ *     (B, Hkv, S_max, D)).
+ *   cache_lens set, block_table NULL: as attn_decode_varlen (cache_len is the
+ *     bound max_cache_len).
+ *   block_table set (cache_lens required): as attn_decode_paged (k, v are the
+ *     page pools, cache_len is max_cache_len, S_max unused).
+ *   workspace: attn_decode_workspace_bytes(B, Hq, Hkv, S, D) with S = S_max
+ *     (contiguous) or cache_len (paged).  window_left < -1: ATTN_ERR_SHAPE.
+ */
+attn_status attn_decode_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+                           attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                           float scale, attn_dtype dtype, int num_splits, const attn_decode_opts* opts,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kv_cache_write_paged -- kv_cache_write for a paged cache: row t of sequence

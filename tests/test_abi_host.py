@@ -42,9 +42,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_varlen", "attn_decode", "attn_decode_varlen", "attn_decode_paged",
-                          "attn_decode_workspace_bytes", "kv_cache_write", "kv_cache_write_paged",
-                          "attn_status_string"}
+    assert set(names) == {"attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_varlen_masked", "attn_decode",
+                          "attn_decode_varlen", "attn_decode_paged", "attn_decode_ex", "attn_decode_workspace_bytes",
+                          "kv_cache_write", "kv_cache_write_paged", "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -82,6 +82,52 @@ def fwd(lib, **kw):
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
+
+
+def fwdm(lib, mask=(0, 63, 0), **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=2, Hkv=1, Nq=65, Nkv=65, D=64,
+             sq=c4(64, 65, 2), sk=c4(64, 65, 1), sv=c4(64, 65, 1), so=c4(64, 65, 2),
+             scale=0.125, dtype=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                               a["Nkv"], a["D"], a["sq"], a["sk"], a["sv"], a["so"], a["scale"], bd.Mask(*mask),
+                               a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("mask,kw,code", [
+    ((2, -1, 0), {}, UNSUP), ((-1, -1, 0), {}, UNSUP), ((0, -2, 0), {}, UNSUP), ((1, 5, -3), {}, UNSUP),
+    ((0, 4, 4), dict(q=None), NULL), ((1, 4, 4), dict(Nkv=0), SHAPE), ((0, 0, 0), dict(D=80), UNSUP),
+])
+def test_fwd_masked_rejects(lib, mask, kw, code):
+    assert fwdm(lib, mask, **kw) == code
+
+
+def decx(lib, opts, **kw):
+    B, Hq, Hkv, Smax, D = 2, 32, 8, 8192, 128
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=B, Hq=Hq, Hkv=Hkv, S_max=Smax, cl=100, D=D,
+             sq=S(Hq * D, D, 0, 1), sk=c4(D, Smax, Hkv), sv=c4(D, Smax, Hkv), so=S(Hq * D, D, 0, 1),
+             scale=0.088, dtype=0, num_splits=0, ws=FAKE,
+             ws_bytes=lib.attn_decode_workspace_bytes(B, Hq, Hkv, Smax, D), stream=None)
+    a.update(kw)
+    return lib.attn_decode_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["S_max"],
+                              a["cl"], a["D"], a["sq"], a["sk"], a["sv"], a["so"], a["scale"], a["dtype"],
+                              a["num_splits"], ctypes.byref(opts) if opts is not None else None, a["ws"],
+                              a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("opts,kw,code", [
+    (None, {}, NULL),
+    (bd.DecodeOpts(None, FAKE, 64, 16, 200, -1), {}, NULL),          # paged needs lengths
+    (bd.DecodeOpts(None, None, 0, 0, 0, -2), {}, SHAPE),            # window below -1
+    (bd.DecodeOpts(FAKE, FAKE, 64, 24, 200, 10), {}, UNSUP),        # page size not a power of two
+    (bd.DecodeOpts(FAKE, FAKE, 4, 16, 200, 10), {}, SHAPE),         # 100 slots > 4 pages of 16
+    (bd.DecodeOpts(FAKE, FAKE, 64, 16, 0, 10), {}, SHAPE),          # no pages
+    (bd.DecodeOpts(FAKE + 2, None, 0, 0, 0, 10), {}, UNSUP),        # misaligned lengths
+    (bd.DecodeOpts(None, None, 0, 0, 0, 10), dict(cl=0), SHAPE),
+    (bd.DecodeOpts(None, None, 0, 0, 0, 10), dict(ws_bytes=64), WS),
+])
+def test_decode_ex_rejects(lib, opts, kw, code):
+    assert decx(lib, opts, **kw) == code
 
 
 def fwdv(lib, **kw):
