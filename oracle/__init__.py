@@ -5,6 +5,7 @@ may import this package.  The HIP product path never does.
 """
 
 from .attention import (  # noqa: F401
+    attention_backward,
     attention_forward,
     attention_probs,
     attention_varlen,

@@ -59,6 +59,11 @@ Readings taken where the pages leave a step open (each also listed in the design doc)
   like the causal mask (offset from the sequence's own lengths).  Decode's
   query is the last cached token, so its window keeps the last
   window_left + 1 slots.
+* Backward (the pages name it as a separate, later kernel pair and defer GQA
+  backward): the gradients of the plain definition with respect to Q, K and V
+  for an upstream gradient dO, with the textbook softmax Jacobian
+  dS = P * (dP - rowsum(P * dP)), dP = dO V^T; a kv head's dK and dV sum the
+  contributions of every q head of its group.
 * Packed variable-length prefill (the pages' deferred "varlen" scope item):
   sequence b owns the packed query rows [cu_q[b], cu_q[b+1]) and key rows
   [cu_k[b], cu_k[b+1]); attention never crosses sequences, and each sequence
@@ -85,6 +90,7 @@ __all__ = [
     "varlen_causal_offset",
     "attention_varlen",
     "kv_cache_write",
+    "attention_backward",
     "page_slot",
     "gather_pages",
     "decode_paged",
@@ -206,6 +212,41 @@ def attention_forward(q, k, v, scale: float, causal: bool, rows=None, chunk: int
                 O[b, h, r0:r0 + chunk] = P @ vb
                 lse[b, h, r0:r0 + chunk] = ls
     return O, lse
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool, causal_offset: int = 0, window=(-1, -1)):
+    """Gradients of ``attention_forward``'s O with respect to Q, K and V.
+
+    For each (b, h) with kv head g = h // (Hq / Hkv), in float64:
+        P   = the masked softmax of scale * Q K^T (as in the forward)
+        dV[g] += P^T dO
+        dP  = dO V^T
+        dS  = P * (dP - rowsum(P * dP))        (softmax Jacobian applied to dP)
+        dQ  = scale * dS K
+        dK[g] += scale * dS^T Q
+    Rows with no visible key have P = 0 and contribute nothing.  q, do:
+    (B, Hq, Nq, D); k, v: (B, Hkv, Nkv, D).  Returns (dQ, dK, dV) float64 with
+    the shapes of q, k, v.
+    """
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if do.shape != q.shape or v.shape != k.shape or k.shape[0] != B or k.shape[3] != D or Hq % Hkv != 0:
+        raise ValueError("shape mismatch")
+    vis = visibility(np.arange(Nq), Nkv, causal, causal_offset, window[0], window[1])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            P, _ = _masked_softmax(_scores(q[b, h], k[b, g], scale), vis)
+            dv[b, g] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, g].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[b, h] = np.float64(scale) * (dS @ k[b, g])
+            dk[b, g] += np.float64(scale) * (dS.T @ q[b, h])
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, cache_len: int, scale: float, window_left: int = -1):

@@ -373,6 +373,81 @@ def pin_decode_window_is_the_last_slots():
     np.testing.assert_array_equal(lp, lv)
 
 
+_BWD_MASKS = [(False, 0, (-1, -1)), (True, 0, (-1, -1)), (True, 2, (-1, -1)), (False, 1, (2, 1)), (True, 0, (1, -1))]
+
+
+def pin_backward_finite_differences():
+    """P11a: the backward equals central finite differences of the forward
+    (L = sum(O * G)) for every element of Q, K and V, with no mask, causal in
+    both alignments and sliding windows, GQA group of 2."""
+    rng = np.random.default_rng(111)
+    B, Hq, Hkv, Nq, Nkv, D, sc = 1, 2, 1, 4, 6, 3, 0.8
+    q, k, v, g = _rand(rng, B, Hq, Nq, D), _rand(rng, B, Hkv, Nkv, D), _rand(rng, B, Hkv, Nkv, D), _rand(rng, B, Hq, Nq, D)
+    eps = 1e-6
+    for causal, off, win in _BWD_MASKS:
+        def loss(qq, kk, vv):
+            O, _ = OA.attention_forward(qq, kk, vv, sc, causal, causal_offset=off, window=win)
+            return float((O * g).sum())
+        dq, dk, dv = OA.attention_backward(q, k, v, g, sc, causal, causal_offset=off, window=win)
+        for x, dx, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            np.testing.assert_allclose(dx, num, rtol=0, atol=2e-8)
+
+
+def pin_backward_matches_torch_autograd():
+    """P11b: the backward equals torch.autograd through an explicit float64
+    attention on the CPU (GQA by repeat_interleave, masks as -inf scores)."""
+    import torch
+    rng = np.random.default_rng(112)
+    B, Hq, Hkv, Nq, Nkv, D, sc = 2, 4, 2, 7, 9, 5, 0.6
+    q, k, v, g = _rand(rng, B, Hq, Nq, D), _rand(rng, B, Hkv, Nkv, D), _rand(rng, B, Hkv, Nkv, D), _rand(rng, B, Hq, Nq, D)
+    for causal, off, win in [(True, 0, (-1, -1)), (True, 2, (3, -1)), (False, 0, (1, 2))]:
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+        vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+        S = sc * tq @ kk.transpose(-1, -2)
+        i = torch.arange(Nq)[:, None] + off
+        j = torch.arange(Nkv)[None, :]
+        keep = torch.ones(Nq, Nkv, dtype=torch.bool)
+        if causal:
+            keep &= j <= i
+        if win[0] >= 0:
+            keep &= j >= i - win[0]
+        if win[1] >= 0:
+            keep &= j <= i + win[1]
+        S = S.masked_fill(~keep, float("-inf"))
+        P = torch.softmax(S, dim=-1).nan_to_num(0.0)
+        (P @ vv * torch.tensor(g)).sum().backward()
+        dq, dk, dv = OA.attention_backward(q, k, v, g, sc, causal, causal_offset=off, window=win)
+        np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_backward_gqa_is_group_sum():
+    """P11c: GQA dK / dV are the sums over each group's q heads of the MHA
+    gradients on K / V repeated per head; dQ is unchanged; and dK summed over
+    keys is zero (O does not change when one vector is added to every key)."""
+    rng = np.random.default_rng(113)
+    B, Hq, Hkv, N, D = 1, 6, 2, 8, 4
+    q, k, v, g = _rand(rng, B, Hq, N, D), _rand(rng, B, Hkv, N, D), _rand(rng, B, Hkv, N, D), _rand(rng, B, Hq, N, D)
+    dq, dk, dv = OA.attention_backward(q, k, v, g, 0.5, True)
+    ke, ve = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    dqe, dke, dve = OA.attention_backward(q, ke, ve, g, 0.5, True)
+    np.testing.assert_allclose(dq, dqe, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, dke.reshape(B, Hkv, Hq // Hkv, N, D).sum(axis=2), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, dve.reshape(B, Hkv, Hq // Hkv, N, D).sum(axis=2), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-12)
+
+
 def _scatter_to_pages(cache, perm, page_size):
     """Independent scatter of contiguous (B, Hkv, S, D) caches into a page pool:
     page perm[b * (S // page_size) + j] holds slots [j * ps, (j + 1) * ps) of sequence b."""
@@ -509,6 +584,9 @@ ALL_PINS = [
     pin_prefill_varlen,
     pin_decode_paged,
     pin_cache_write_paged,
+    pin_backward_finite_differences,
+    pin_backward_matches_torch_autograd,
+    pin_backward_gqa_is_group_sum,
     pin_sliding_window_rows_are_slices,
     pin_zero_width_window_is_the_diagonal_key,
     pin_decode_window_is_the_last_slots,

@@ -22,6 +22,30 @@ _orig_varlen = OA.decode_varlen
 _orig_bounds = OA.sequence_bounds
 _orig_vcoff = OA.varlen_causal_offset
 _orig_pslot = OA.page_slot
+_orig_bwd = OA.attention_backward
+
+
+def _bwd_variant(drop_rowsum=False, dk_unscaled=False, gqa_overwrite=False, dq_uses_v=False):
+    def bwd(q, k, v, do, scale, causal, causal_offset=0, window=(-1, -1)):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, Hq, Nq, D = q.shape
+        Hkv, Nkv = k.shape[1], k.shape[2]
+        vis = OA.visibility(np.arange(Nq), Nkv, causal, causal_offset, window[0], window[1])
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            for h in range(Hq):
+                g = OA.kv_head_of(h, Hq, Hkv)
+                P, _ = OA._masked_softmax(OA._scores(q[b, h], k[b, g], scale), vis)
+                dP = do[b, h] @ v[b, g].T
+                dS = P * dP if drop_rowsum else P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                if gqa_overwrite:
+                    dv[b, g] = P.T @ do[b, h]
+                else:
+                    dv[b, g] += P.T @ do[b, h]
+                dq[b, h] = scale * (dS @ (v[b, g] if dq_uses_v else k[b, g]))
+                dk[b, g] += (1.0 if dk_unscaled else scale) * (dS.T @ q[b, h])
+        return dq, dk, dv
+    return bwd
 
 
 def _vis_strict(q_pos, Nkv, causal, offset=0, window_left=-1, window_right=-1):
@@ -179,6 +203,10 @@ MUTATIONS = {
     "paged_row_and_page_swapped": ("page_slot", _pslot_row_and_page_swapped),
     "paged_other_sequences_table": ("page_slot", _pslot_next_sequence),
     "paged_row_off_by_one": ("page_slot", _pslot_row_off_by_one),
+    "bwd_softmax_jacobian_rowsum_dropped": ("attention_backward", _bwd_variant(drop_rowsum=True)),
+    "bwd_dk_scale_dropped": ("attention_backward", _bwd_variant(dk_unscaled=True)),
+    "bwd_gqa_dv_overwritten": ("attention_backward", _bwd_variant(gqa_overwrite=True)),
+    "bwd_dq_uses_v": ("attention_backward", _bwd_variant(dq_uses_v=True)),
     "packed_offsets_as_lengths": ("sequence_bounds", _bounds_from_zero),
     "packed_row_past_sequence": ("sequence_bounds", _bounds_one_past),
     "packed_causal_offset_swapped": ("varlen_causal_offset", _vcoff_swapped),
