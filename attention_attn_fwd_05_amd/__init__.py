@@ -21,6 +21,8 @@ Entry points (same names as the C ABI):
 * ``attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)`` /
   ``decode_workspace(...)`` (a uint8 scratch tensor of that size)
 * ``kv_cache_write(k_cache, v_cache, k_new, v_new, pos)``
+* ``attn_bwd(q, k, v, o, dout, lse, *, causal, ...)`` -> (dq, dk, dv), the
+  backward of attn_fwd (GQA gradients summed over each group)
 * ``attn_decode_paged(q, k_pages, v_pages, block_table, cache_lens, ...)`` and
   ``kv_cache_write_paged(k_pages, v_pages, k_new, v_new, block_table, pos)``
   (a paged KV cache addressed through a device block table)
@@ -29,6 +31,7 @@ Entry points (same names as the C ABI):
 from ._binding import (  # noqa: F401
     AttnError,
     Status,
+    attn_bwd,
     attn_decode,
     attn_decode_paged,
     attn_decode_varlen,
@@ -46,6 +49,7 @@ __all__ = [
     "AttnError",
     "Status",
     "attn_fwd",
+    "attn_bwd",
     "attn_fwd_varlen",
     "attn_decode",
     "attn_decode_varlen",

@@ -86,6 +86,11 @@ def load_library():
     lib.kv_cache_write_paged.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, i32, S, S, S, S,
                                          i32, vp]
     lib.kv_cache_write_paged.restype = i32
+    lib.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, S, S, S, S,
+                             f32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = i32
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, i32, vp]
     lib.kv_cache_write.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -465,4 +470,45 @@ def kv_cache_write_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, k_new: to
                                   _strides4(k_pages), _strides4(v_pages), _strides4(k_new), _strides4(v_new), code,
                                   _stream(k_pages))
     _check(st, "kv_cache_write_paged")
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+             lse: torch.Tensor, *, causal: bool, scale: float | None = None, causal_align: str = "top_left",
+             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv) of attn_fwd's output for an upstream gradient ``dout``.
+
+    q, o, dout (B,Hq,Nq,D); k, v (B,Hkv,Nkv,D); lse fp32 (B,Hq,Nq) from attn_fwd
+    with the same inputs, mask and scale.  A kv head's dk, dv sum its group's q heads.
+    """
+    if causal_align not in _CAUSAL_ALIGN:
+        raise ValueError("causal_align must be 'top_left' or 'bottom_right'")
+    lib = load_library()
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch between q, k, v, o and dout")
+    if lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, Nq)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient buffers must have the shapes of q, k, v")
+    if workspace is None:
+        n = int(lib.attn_bwd_workspace_bytes(B, Hq, Nq))
+        if n == 0:
+            raise ValueError("invalid sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _on_gpu(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    code = _dtype_code(q, k, v, o, dout, dq, dk, dv)
+    s = _default_scale(D) if scale is None else float(scale)
+    st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D,
+                      _strides4(q), _strides4(k), _strides4(v), _strides4(o), _strides4(dout),
+                      _strides4(dq), _strides4(dk), _strides4(dv), s,
+                      _CAUSAL_ALIGN[causal_align] if causal else 0, code, workspace.data_ptr(),
+                      workspace.numel(), _stream(q))
+    _check(st, "attn_bwd")
+    return dq, dk, dv
 

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "prefill_fwd.hip", "decode.hip"]
+SOURCES = ["attn_api.cpp", "prefill_fwd.hip", "decode.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 

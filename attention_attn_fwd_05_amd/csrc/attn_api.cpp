@@ -464,6 +464,72 @@ attn_status kv_cache_write_paged(void* k_pages, void* v_pages, const void* k_new
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0) return 0;
+  return (size_t)B * Hq * Nq * 8;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
+                     attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale, int causal,
+                     attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (causal < ATTN_CAUSAL_NONE || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_ERR_UNSUPPORTED;
+  for (const attn_strides* st : {&sq, &sk, &sv, &so, &sdo, &sdq, &sdk, &sdv})
+    if (!strides_ok(*st) || st->n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
+  for (const void* p : {q, k, v, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  const int64_t nqb = ((int64_t)Nq + 255) / 256;   // dq: 256 query rows per workgroup
+  const int64_t nkb = ((int64_t)Nkv + 127) / 128;  // dkdv: 128 keys per workgroup
+  const int64_t dq_blocks = nqb * Hq * B, dkv_blocks = nkb * Hkv * B;
+  if (dq_blocks > INT_MAX || dkv_blocks > INT_MAX || (int64_t)B * Hq * Nq > INT_MAX) return ATTN_ERR_SHAPE;
+
+  attn::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.ld = static_cast<float*>(workspace);
+  a.sqb = sq.b; a.sqh = sq.h; a.sqn = sq.n;
+  a.skb = sk.b; a.skh = sk.h; a.skn = sk.n;
+  a.svb = sv.b; a.svh = sv.h; a.svn = sv.n;
+  a.sob = so.b; a.soh = so.h; a.son = so.n;
+  a.sdob = sdo.b; a.sdoh = sdo.h; a.sdon = sdo.n;
+  a.sdqb = sdq.b; a.sdqh = sdq.h; a.sdqn = sdq.n;
+  a.sdkb = sdk.b; a.sdkh = sdk.h; a.sdkn = sdk.n;
+  a.sdvb = sdv.b; a.sdvh = sdv.h; a.sdvn = sdv.n;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv; a.group = Hq / Hkv;
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  a.dq_blocks = (unsigned)dq_blocks;
+  a.dkv_blocks = (unsigned)dkv_blocks;
+  a.causal = causal != ATTN_CAUSAL_NONE;
+  a.causal_off = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0;
+  a.bf16 = dtype == ATTN_BF16;
+  a.c = scale * kLog2e;
+  a.scale = scale;
+  a.q_bytes = slice_bytes(Nq, sq.n, D);
+  a.k_bytes = slice_bytes(Nkv, sk.n, D);
+  a.v_bytes = slice_bytes(Nkv, sv.n, D);
+  a.do_bytes = slice_bytes(Nq, sdo.n, D);
+  const hipError_t e = attn::launch_bwd(a, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status kv_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            int B, int Hkv, int S_max, int D, int pos, int T,
                            attn_strides skc, attn_strides svc, attn_strides skn, attn_strides svn,

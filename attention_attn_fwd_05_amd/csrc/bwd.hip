@@ -1,0 +1,525 @@
+// Fused attention backward for gfx950: dQ, dK, dV of O = softmax(scale Q K^T +
+// causal mask) V for an upstream gradient dO.
+//
+// What it computes ("Skill: Write a Triton Attention Kernel", Do not use this
+// when: the backward recomputes the attention weights from the forward's
+// logsumexp; "Triton-FlashAttention" README, Phase 1 (separate dq and dk/dv
+// kernels, masked loads for ragged lengths) and its deferred scope (GQA
+// backward accumulates every q head of a group into the shared dK, dV)):
+//   P  = exp(scale S - lse)                 (S = Q K^T, lse from the forward)
+//   dV = P^T dO,  dP = dO V^T,  dS = P (dP - delta),  delta = rowsum(dO * O)
+//   dQ = scale dS K,  dK = scale dS^T Q    (dK, dV summed over a kv head's group)
+//
+// gfx950 design, three kernels, no atomics:
+//   * bwd_prep: per query row, lse * log2(e) and delta, as (float, float) pairs.
+//   * bwd_dq: the forward's shape.  A workgroup of 8 waves owns 256 query rows
+//     of one q head; Q and dO are register-resident B operands, K and V tiles
+//     of 64 keys stream through a 3-stage LDS ring (buffer-to-LDS loads).
+//     S^T = K Q^T and dP^T = V dO^T come out one query per lane, so lse and
+//     delta are one value per lane; dQ^T += K^T dS^T reads K^T with the
+//     transposing LDS read from the same tile.
+//   * bwd_dkdv: the roles swapped.  A workgroup of 4 waves (one per SIMD, so
+//     K, V and both accumulators fit in registers) owns 128 keys of one kv head
+//     (32 per wave, K and V register-resident B operands) and streams the Q,
+//     dO, lse/delta tiles of every q head of the group, so the group's
+//     gradients add up in registers.  S = Q K^T and dP = dO V^T come out one
+//     key per lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with
+//     the transposing LDS read.
+//   The 16-bit P (and dS) B operands take the key (query) order of the fp32
+//   accumulator registers, matched by the transposing reads' addresses, as in
+//   the forward.  Causal: the dq loop stops at its block's diagonal, the dkdv
+//   loop starts at its block's first visible query; only tiles crossing the
+//   diagonal are masked.  Ragged tails read as zeros and contribute nothing.
+#include <type_traits>
+
+#include "kernel_common.hpp"
+#include "launch.hpp"
+#include "lds_tile.hpp"
+
+namespace attn {
+
+namespace {
+
+constexpr int kDqW = 8;           // waves per dq workgroup (two per SIMD)
+constexpr int kDqRows = 32 * kDqW; // query rows per dq workgroup
+constexpr int kKvW = 4;           // waves per dkdv workgroup (one per SIMD: K, V and two
+                                  // accumulators stay in registers)
+constexpr int kKvRows = 32 * kKvW; // keys per dkdv workgroup
+constexpr int kBT = 64;           // streamed rows per LDS tile
+constexpr int kBStages = 3;      // LDS ring depth
+
+// ---- lse * log2(e) and delta = rowsum(dO * O) per query row, fp32 pairs
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a) {
+  constexpr int C = D / 8;  // 16-byte chunks per row = lanes per row
+  const int64_t total = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t r = (int64_t)blockIdx.x * (256 / C) + threadIdx.x / C;
+  const int c = threadIdx.x % C;
+  float s = 0.f;
+  if (r < total) {
+    const int i = (int)(r % a.Nq);
+    const int64_t bh = r / a.Nq;
+    const int h = (int)(bh % a.Hq);
+    const int64_t b = bh / a.Hq;
+    const u32x4 o = load16(a.o + b * a.sob + h * a.soh + (int64_t)i * a.son + 8 * c);
+    const u32x4 g = load16(a.dout + b * a.sdob + h * a.sdoh + (int64_t)i * a.sdon + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s += to_f32<BF16>(o[j] & 0xffff) * to_f32<BF16>(g[j] & 0xffff);
+      s += to_f32<BF16>(o[j] >> 16) * to_f32<BF16>(g[j] >> 16);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < C; m <<= 1) s += __shfl_xor(s, m);
+  if (r < total && c == 0) {
+    float2* out = reinterpret_cast<float2*>(a.ld) + r;
+    *out = make_float2(a.lse[r] * kLog2e, s);
+  }
+}
+
+// LDS ring of the dq kernel: V tiles of all stages, then K tiles
+template <int D>
+struct DqLds {
+  static constexpr int TILE = kBT * D;
+  static constexpr int V0 = 0;
+  static constexpr int K0 = kBStages * TILE;
+  static constexpr int ELEMS = 2 * kBStages * TILE;
+};
+
+// LDS ring of the dkdv kernel: dO tiles, Q tiles, then the (lse2, delta) rows
+template <int D>
+struct DkvLds {
+  static constexpr int TILE = kBT * D;
+  static constexpr int DO0 = 0;
+  static constexpr int Q0 = kBStages * TILE;
+  static constexpr int LD0 = 2 * kBStages * TILE;  // in 16-bit elements; 2 * kBT floats per stage
+  static constexpr int ELEMS = LD0 + kBStages * 4 * kBT;
+};
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0; expcnt, lgkmcnt at
+// their maxima, i.e. unconstrained)
+constexpr int kWaitCnt(int vm) { return 0x0F70 | vm; }
+
+// transposing-read addresses (byte, within stage 0 of a region at `base`) of
+// the A operand X^T for an MFMA whose k runs over 16 rows of a row-major tile:
+// lane (g = lane/16, i = lane%16) reads row 8u + 4(g/2) + i/4 of the 16-row
+// chunk, columns 32dt + 16(g%2) + 4(i%4) .. +3; reads u = 0 / 1 give k-slots
+// 0-3 / 4-7, the order in which pack_pt below lays out the B operand
+template <int D>
+__device__ __forceinline__ void tr_addrs(uint32_t base, int lane, uint32_t (&ad)[D / 32][2]) {
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 8 * u + 4 * (g >> 1) + (i >> 2);
+      const int d = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+      ad[dt][u] = opaque_lds(base + 2 * (row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7))));
+    }
+}
+
+// plain-read addresses of the A operand X (rows of the tile, k over columns):
+// lane (n = lane%32, hh = lane/32) reads row n, 16-byte chunk 2 ks + hh
+template <int D>
+__device__ __forceinline__ void row_addrs(uint32_t base, int lane, uint32_t (&ad)[D / 16]) {
+  const int n = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) ad[ks] = opaque_lds(base + 2 * (n * D + (((2 * ks + hh) ^ swz<D>(n)) << 3)));
+}
+
+// fp32 accumulator x (32x32 tile, element e of lane (n, hh) at row 8(e/4) +
+// 4hh + e%4) -> the 16-bit B operands of two MFMA k-steps over those rows:
+// pf[kk] holds rows 16kk + 8u + 4hh + t in k-slot 4u + t
+template <bool BF16>
+__device__ __forceinline__ void pack_pt(const f32x16& x, u32x4* pf) {
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) pf[e >> 3][(e & 7) >> 1] = pack2<BF16>(x[e], x[e + 1]);
+}
+
+// ---- dQ: one workgroup per (batch, q head, 256 query rows)
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
+  using L = DqLds<D>;
+  constexpr int KS = D / 16, DT = D / 32, C = D / 8;
+  constexpr int NB = L::TILE * 2 / 1024 / kDqW;  // 1 KiB DMA blocks per wave per tile
+  constexpr int RPB = 64 / C;                   // rows per 1 KiB block
+  static_assert(NB >= 1, "every wave loads at least one block");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
+
+  const int per_unit = a.group * a.nqb;
+  const int unit = blockIdx.x / per_unit;
+  const int rem = blockIdx.x - unit * per_unit;
+  int qb = rem / a.group;
+  const int hg = rem - qb * a.group;
+  if (CAUSAL) qb = a.nqb - 1 - qb;  // longest blocks first
+  const int b = unit / a.Hkv;
+  const int kvh = unit - b * a.Hkv;
+  const int h = kvh * a.group + hg;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int q0 = qb * kDqRows;
+  const int qrow = q0 + 32 * w + n;
+
+  // stationary B operands: Q and dO rows (zeros past Nq); lse2 and delta
+  u32x4 qf[KS], gf[KS];
+  {
+    const int64_t qo = (int64_t)q0 * a.sqn, go = (int64_t)q0 * a.sdon;
+    const auto rq = make_rsrc(a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh + qo, clamp_bytes(a.q_bytes - 2 * qo));
+    const auto rg = make_rsrc(a.dout + (int64_t)b * a.sdob + (int64_t)h * a.sdoh + go,
+                              clamp_bytes(a.do_bytes - 2 * go));
+    const int32_t oq = (32 * w + n) * (int32_t)a.sqn * 2 + 16 * hh;
+    const int32_t og = (32 * w + n) * (int32_t)a.sdon * 2 + 16 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = bload16(rq, oq + 32 * ks);
+      gf[ks] = bload16(rg, og + 32 * ks);
+    }
+  }
+  float lse2 = 0.f, delta = 0.f;
+  if (qrow < a.Nq) {
+    const float2 ld = reinterpret_cast<const float2*>(a.ld)[((int64_t)b * a.Hq + h) * a.Nq + qrow];
+    lse2 = ld.x;
+    delta = ld.y;
+  }
+
+  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
+  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
+  const int off = CAUSAL ? a.causal_off : 0;
+  const int kv_end = CAUSAL ? max(0, min(a.Nkv, q0 + kDqRows + off)) : a.Nkv;
+  const int ntiles = (kv_end + kBT - 1) / kBT;
+  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, a.Nkv)) / kBT : a.Nkv / kBT;
+
+  // DMA geometry (as the forward): wave w fills 1 KiB blocks NB w .. NB w + NB - 1
+  int32_t dk[NB], dv[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = RPB * (NB * w + i) + lane / C;
+    const int chunk = (lane % C) ^ swz<D>(row);
+    dk[i] = row * (int32_t)a.skn * 2 + 16 * chunk;
+    dv[i] = row * (int32_t)a.svn * 2 + 16 * chunk;
+  }
+  const uint32_t lds_k = lds_addr(smem + L::K0) + 1024 * NB * w;
+  const uint32_t lds_v = lds_addr(smem + L::V0) + 1024 * NB * w;
+  auto dma_tile = [&](int t, int stage) __attribute__((always_inline)) {
+    const int64_t ko = (int64_t)t * kBT * a.skn, vo = (int64_t)t * kBT * a.svn;
+    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
+    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dma16(rk, lds_k + 2 * stage * L::TILE + 1024 * i, dk[i]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dma16(rv, lds_v + 2 * stage * L::TILE + 1024 * i, dv[i]);
+  };
+
+  uint32_t ka[KS], va[KS], kt[DT][2];
+  row_addrs<D>(lds_addr(smem + L::K0), lane, ka);
+  row_addrs<D>(lds_addr(smem + L::V0), lane, va);
+  tr_addrs<D>(lds_addr(smem + L::K0), lane, kt);
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  const float c = a.c;
+  const int wq_hi = q0 + 32 * w + 31 + off;
+
+  auto compute = [&](int stage, int t, bool masked) __attribute__((always_inline)) {
+    const int kb = t * kBT;
+    bool act1 = true;
+    if (masked) {
+      if (kb >= a.Nkv || (CAUSAL && kb > wq_hi)) return;
+      act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi);
+    }
+    // per 32-key subtile u: S^T = K Q^T, dP^T = V dO^T, then dS^T = P^T (dP^T -
+    // delta) with P^T = exp2(S^T c - lse2); element e of lane (n, hh) is key
+    // kb + 32u + 8(e/4) + 4hh + e%4
+    u32x4 pf[4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !act1) break;
+      const uint32_t so = 2 * stage * L::TILE + 2 * 32 * u * D;
+      f32x16 sx = f32x16{}, px = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sx = mfma_32x32x16<BF16>(lds_load16(ka[ks] + so), qf[ks], sx);
+        px = mfma_32x32x16<BF16>(lds_load16(va[ks] + so), gf[ks], px);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pv = fast_exp2(__builtin_fmaf(sx[e], c, -lse2));
+        if (masked) {
+          const int key = kb + 32 * u + 8 * (e >> 2) + 4 * hh + (e & 3);
+          pv = (key < a.Nkv && (!CAUSAL || key <= qrow + off)) ? pv : 0.f;
+        }
+        sx[e] = pv * (px[e] - delta);
+      }
+      pack_pt<BF16>(sx, pf + 2 * u);
+    }
+    const uint32_t so = 2 * stage * L::TILE;
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 2 || act1) {
+        const uint32_t o = so + 2 * 16 * kk * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x2 lo = lds_read_tr16(kt[dt][0] + o);
+          const u32x2 hi = lds_read_tr16(kt[dt][1] + o);
+          acc[dt] = mfma_32x32x16<BF16>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[kk], acc[dt]);
+        }
+      }
+    }
+  };
+
+  // 3-stage ring: the loads of tile t + 2 go out before tile t is computed
+  constexpr int NDMA = 2 * NB;
+  static_assert(NDMA < 16, "vmcnt field");
+  if (ntiles > 0) dma_tile(0, 0);
+  if (ntiles > 1) dma_tile(1, 1);
+  if (ntiles > 1)
+    __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
+  barrier_nofence();
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t % 3;
+    const bool pre = t + 2 < ntiles;
+    if (pre) dma_tile(t + 2, (stage + 2) % 3);
+    compute(stage, t, t >= n_full);
+    if (pre)
+      __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
+    barrier_nofence();
+  }
+
+  // ---- dQ = scale (dQ^T)^T, cast, store
+  if (qrow < a.Nq) {
+    uint16_t* op = a.dq + (int64_t)b * a.sdqb + (int64_t)h * a.sdqh + (int64_t)qrow * a.sdqn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hh;
+        *reinterpret_cast<u32x2*>(op + d) =
+            u32x2{pack2<BF16>(acc[dt][4 * g] * a.scale, acc[dt][4 * g + 1] * a.scale),
+                  pack2<BF16>(acc[dt][4 * g + 2] * a.scale, acc[dt][4 * g + 3] * a.scale)};
+      }
+  }
+}
+
+// ---- dK, dV: one workgroup per (batch, kv head, 128 keys)
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(64 * kKvW, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+  using L = DkvLds<D>;
+  constexpr int KS = D / 16, DT = D / 32, C = D / 8;
+  constexpr int NB = L::TILE * 2 / 1024 / kKvW;
+  constexpr int RPB = 64 / C;
+  static_assert(NB >= 1, "every wave loads at least one block");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
+
+  const int unit = blockIdx.x / a.nkb;
+  const int kbk = blockIdx.x - unit * a.nkb;  // ascending: under a causal mask the first blocks see the most queries
+  const int b = unit / a.Hkv;
+  const int kvh = unit - b * a.Hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int k0 = kbk * kKvRows;
+  const int key = k0 + 32 * w + n;
+
+  // stationary B operands: K and V rows (zeros past Nkv)
+  u32x4 kf[KS], vf[KS];
+  {
+    const int64_t ko = (int64_t)k0 * a.skn, vo = (int64_t)k0 * a.svn;
+    const auto rk = make_rsrc(a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh + ko, clamp_bytes(a.k_bytes - 2 * ko));
+    const auto rv = make_rsrc(a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh + vo, clamp_bytes(a.v_bytes - 2 * vo));
+    const int32_t ok = (32 * w + n) * (int32_t)a.skn * 2 + 16 * hh;
+    const int32_t ov = (32 * w + n) * (int32_t)a.svn * 2 + 16 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = bload16(rk, ok + 32 * ks);
+      vf[ks] = bload16(rv, ov + 32 * ks);
+    }
+  }
+
+  // query tiles: from the first that sees key k0 to the end, for every q head
+  // of the group; tiles from full_from on see all 256 keys of the block
+  const int off = CAUSAL ? a.causal_off : 0;
+  const int ntq = (a.Nq + kBT - 1) / kBT;
+  const int tq0 = CAUSAL ? min(max(0, k0 - off) / kBT, ntq) : 0;
+  const int full_from = CAUSAL ? min(ntq, (max(0, k0 + kKvRows - 1 - off) + kBT - 1) / kBT) : 0;
+  const int nt = ntq - tq0;
+  const int total = nt * a.group;
+
+  int32_t dq_[NB], dg_[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = RPB * (NB * w + i) + lane / C;
+    const int chunk = (lane % C) ^ swz<D>(row);
+    dq_[i] = row * (int32_t)a.sqn * 2 + 16 * chunk;
+    dg_[i] = row * (int32_t)a.sdon * 2 + 16 * chunk;
+  }
+  const uint32_t lds_q = lds_addr(smem + L::Q0) + 1024 * NB * w;
+  const uint32_t lds_g = lds_addr(smem + L::DO0) + 1024 * NB * w;
+  // (lse2, delta) rows: 8 bytes each, 512 bytes per tile; every wave loads
+  // LDW of them with LDW / 16 lanes (the other lanes stay inactive: a
+  // buffer-to-LDS load writes for every active lane)
+  constexpr int LDW = kBT * 8 / kKvW;
+  const uint32_t lds_ld = lds_addr(smem + L::LD0) + LDW * w;
+  const float* ldb = a.ld + 2 * ((int64_t)b * a.Hq) * a.Nq;
+  auto dma_tile = [&](int it, int stage) __attribute__((always_inline)) {
+    const int hgi = it / nt;
+    const int t = tq0 + (it - hgi * nt);
+    const int h = kvh * a.group + hgi;
+    const int64_t qo = (int64_t)t * kBT * a.sqn, go = (int64_t)t * kBT * a.sdon;
+    const i32x4 rq = rsrc_words(a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh + qo, clamp_bytes(a.q_bytes - 2 * qo));
+    const i32x4 rg = rsrc_words(a.dout + (int64_t)b * a.sdob + (int64_t)h * a.sdoh + go,
+                                clamp_bytes(a.do_bytes - 2 * go));
+    const int64_t lo = ((int64_t)h * a.Nq + (int64_t)t * kBT) * 2;
+    const i32x4 rl = rsrc_words(ldb + lo, clamp_bytes(((int64_t)a.Nq - (int64_t)t * kBT) * 8));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dma16(rq, lds_q + 2 * stage * L::TILE + 1024 * i, dq_[i]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dma16(rg, lds_g + 2 * stage * L::TILE + 1024 * i, dg_[i]);
+    if (lane < LDW / 16) dma16(rl, lds_ld + stage * 4 * kBT * 2, LDW * w + 16 * lane);
+  };
+
+  uint32_t qa[KS], ga[KS], qt[DT][2], gt[DT][2];
+  row_addrs<D>(lds_addr(smem + L::Q0), lane, qa);
+  row_addrs<D>(lds_addr(smem + L::DO0), lane, ga);
+  tr_addrs<D>(lds_addr(smem + L::Q0), lane, qt);
+  tr_addrs<D>(lds_addr(smem + L::DO0), lane, gt);
+  const uint32_t ldr = opaque_lds(lds_addr(smem + L::LD0) + 32 * hh);  // + (32u + 8g) * 8 per read
+
+  f32x16 adv[DT], adk[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    adv[dt] = f32x16{};
+    adk[dt] = f32x16{};
+  }
+  const float c = a.c;
+  const int wk_lo = k0 + 32 * w;  // this wave's first key
+
+  auto compute = [&](int stage, int it, bool masked) __attribute__((always_inline)) {
+    const int hgi = it / nt;
+    const int tq = (tq0 + (it - hgi * nt)) * kBT;
+    u32x4 pp[4], dp[4];
+    bool act[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // a subtile of 32 queries wholly before this wave's keys sees none of them
+      act[u] = !masked || !CAUSAL || wk_lo <= tq + 32 * u + 31 + off;
+      if (!act[u]) continue;
+      const uint32_t so = 2 * stage * L::TILE + 2 * 32 * u * D;
+      f32x16 s = f32x16{}, p = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma_32x32x16<BF16>(lds_load16(qa[ks] + so), kf[ks], s);
+        p = mfma_32x32x16<BF16>(lds_load16(ga[ks] + so), vf[ks], p);
+      }
+      // element e of lane (n, hh) is query tq + 32u + 8(e/4) + 4hh + e%4, key `key`
+      f32x16 pr, ds;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = ldr + stage * 4 * kBT * 2 + (32 * u + 8 * g) * 8;
+        const f32x4 a0 = __builtin_bit_cast(f32x4, lds_load16(lo));
+        const f32x4 a1 = __builtin_bit_cast(f32x4, lds_load16(lo + 16));
+        const float l2[4] = {a0[0], a0[2], a1[0], a1[2]};
+        const float dl[4] = {a0[1], a0[3], a1[1], a1[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * g + j;
+          float pv = fast_exp2(__builtin_fmaf(s[e], c, -l2[j]));
+          if (masked && CAUSAL) {
+            const int qry = tq + 32 * u + 8 * g + 4 * hh + j;
+            pv = (key <= qry + off) ? pv : 0.f;
+          }
+          pr[e] = pv;
+          ds[e] = pv * (p[e] - dl[j]);
+        }
+      }
+      pack_pt<BF16>(pr, pp + 2 * u);
+      pack_pt<BF16>(ds, dp + 2 * u);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's queries
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (!act[kk >> 1]) continue;
+      const uint32_t o = 2 * stage * L::TILE + 2 * 16 * kk * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x2 glo = lds_read_tr16(gt[dt][0] + o);
+        const u32x2 ghi = lds_read_tr16(gt[dt][1] + o);
+        adv[dt] = mfma_32x32x16<BF16>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pp[kk], adv[dt]);
+        const u32x2 qlo = lds_read_tr16(qt[dt][0] + o);
+        const u32x2 qhi = lds_read_tr16(qt[dt][1] + o);
+        adk[dt] = mfma_32x32x16<BF16>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dp[kk], adk[dt]);
+      }
+    }
+  };
+
+  constexpr int NDMA = 2 * NB + 1;
+  static_assert(NDMA < 16, "vmcnt field");
+  if (total > 0) dma_tile(0, 0);
+  if (total > 1) dma_tile(1, 1);
+  if (total > 1)
+    __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
+  barrier_nofence();
+  for (int it = 0; it < total; ++it) {
+    const int stage = it % 3;
+    const bool pre = it + 2 < total;
+    if (pre) dma_tile(it + 2, (stage + 2) % 3);
+    const int t = tq0 + it % nt;
+    compute(stage, it, CAUSAL && t < full_from);
+    if (pre)
+      __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
+    barrier_nofence();
+  }
+
+  // ---- dV = (dV^T)^T, dK = scale (dK^T)^T, cast, store
+  if (key < a.Nkv) {
+    uint16_t* vp = a.dv + (int64_t)b * a.sdvb + (int64_t)kvh * a.sdvh + (int64_t)key * a.sdvn;
+    uint16_t* kp = a.dk + (int64_t)b * a.sdkb + (int64_t)kvh * a.sdkh + (int64_t)key * a.sdkn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * hh;
+        *reinterpret_cast<u32x2*>(vp + d) = u32x2{pack2<BF16>(adv[dt][4 * g], adv[dt][4 * g + 1]),
+                                                  pack2<BF16>(adv[dt][4 * g + 2], adv[dt][4 * g + 3])};
+        *reinterpret_cast<u32x2*>(kp + d) =
+            u32x2{pack2<BF16>(adk[dt][4 * g] * a.scale, adk[dt][4 * g + 1] * a.scale),
+                  pack2<BF16>(adk[dt][4 * g + 2] * a.scale, adk[dt][4 * g + 3] * a.scale)};
+      }
+  }
+}
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t prep_blocks = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
+  hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL>), dim3(a.dq_blocks), dim3(64 * kDqW), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL>), dim3(a.dkv_blocks), dim3(64 * kKvW), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.causal ? launch_bwd_t<D, true, true>(a, stream) : launch_bwd_t<D, true, false>(a, stream);
+  return a.causal ? launch_bwd_t<D, false, true>(a, stream) : launch_bwd_t<D, false, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream) {
+  return D == 64 ? launch_bwd_d<64>(a, stream) : launch_bwd_d<128>(a, stream);
+}
+
+}  // namespace attn

@@ -94,6 +94,38 @@ struct CacheWritePagedArgs {
 
 hipError_t launch_cache_write_paged(const CacheWritePagedArgs& a, hipStream_t stream);
 
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;  // contiguous (B, Hq, Nq), natural log, from the forward
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* ld;  // workspace: (lse * log2 e, delta) per query row, (B, Hq, Nq, 2)
+  int64_t sqb, sqh, sqn;
+  int64_t skb, skh, skn;
+  int64_t svb, svh, svn;
+  int64_t sob, soh, son;
+  int64_t sdob, sdoh, sdon;
+  int64_t sdqb, sdqh, sdqn;
+  int64_t sdkb, sdkh, sdkn;
+  int64_t sdvb, sdvh, sdvn;
+  int B, Hq, Hkv, Nq, Nkv, group;
+  int nqb, nkb;                // query blocks (dq), key blocks (dkdv) per (batch, head)
+  unsigned dq_blocks, dkv_blocks;
+  int causal, causal_off;      // query i sees keys j <= i + causal_off when causal
+  int bf16;
+  float c;                     // scale * log2(e)
+  float scale;
+  // bytes from a (batch, head) slice's first element to the end of its last row
+  int64_t q_bytes, k_bytes, v_bytes, do_bytes;
+};
+
+hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream);
+
 struct CacheWriteArgs {
   uint16_t* kc;
   uint16_t* vc;

@@ -170,6 +170,40 @@ attn_status attn_fwd_varlen_masked(const void* q, const void* k, const void* v, 
                                    float scale, attn_mask mask, attn_dtype dtype, void* stream);
 
 /*
+ * attn_bwd_workspace_bytes -- scratch attn_bwd needs: B * Hq * Nq * 8 bytes
+ * (one (lse * log2 e, delta) pair of floats per query row).  0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+/*
+ * attn_bwd -- gradients of attn_fwd's O with respect to Q, K and V for an
+ * upstream gradient dO: the backward the pages name as a separate, later
+ * kernel pair that recomputes the attention weights from the forward's
+ * logsumexp ([P1] "Do not use this when" and "Correctness requirements",
+ * lse bullet; [P3] Phase 1: separate dq and dk/dv kernels with masked loads;
+ * [P3] deferred scope: GQA backward accumulates every q head of a group into
+ * the shared dK, dV).
+ *
+ *   P  = exp(scale q_i . k_j - lse_i) on visible (i, j), else 0
+ *   dV = P^T dO;  dP = dO V^T;  dS = P (dP - delta_i), delta_i = sum_d dO_i,d O_i,d
+ *   dQ = scale dS K;  dK = scale dS^T Q;  a kv head's dK, dV sum its group's q heads
+ *
+ *   q, o, dout, dq (B, Hq, Nq, D) and k, v, dk, dv (B, Hkv, Nkv, D) via their
+ *   strides (rules as attn_fwd); dq, dk, dv are written (same dtype as q).
+ *   lse: contiguous fp32 (B, Hq, Nq), as attn_fwd returns it for the same
+ *   inputs, causal argument and scale.  causal: as attn_fwd (sliding windows
+ *   are not supported here).  workspace: attn_bwd_workspace_bytes(B, Hq, Nq)
+ *   bytes, 16-byte aligned, contents irrelevant.  Three kernels run in order on
+ *   `stream` (row statistics, dQ, dK/dV); no atomics, so the result does not
+ *   depend on scheduling.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
+                     attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale, int causal,
+                     attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode needs
  * for a cache of S_max slots (covers every cache_len <= S_max and every split
  * count): U * min(64, ceil(S_max/128)) * ceil(G/ceil(G/16)) * (D + 4) * 4

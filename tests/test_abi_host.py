@@ -44,7 +44,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_varlen_masked", "attn_decode",
                           "attn_decode_varlen", "attn_decode_paged", "attn_decode_ex", "attn_decode_workspace_bytes",
-                          "kv_cache_write", "kv_cache_write_paged", "attn_status_string"}
+                          "kv_cache_write", "kv_cache_write_paged", "attn_bwd", "attn_bwd_workspace_bytes",
+                          "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -128,6 +129,34 @@ def decx(lib, opts, **kw):
 ])
 def test_decode_ex_rejects(lib, opts, kw, code):
     assert decx(lib, opts, **kw) == code
+
+
+def bwd(lib, **kw):
+    B, Hq, Hkv, N, D = 1, 4, 2, 300, 128
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=B, Hq=Hq, Hkv=Hkv,
+             Nq=N, Nkv=N, D=D, sq=c4(D, N, Hq), sk=c4(D, N, Hkv), sv=c4(D, N, Hkv), so=c4(D, N, Hq),
+             sdo=c4(D, N, Hq), sdq=c4(D, N, Hq), sdk=c4(D, N, Hkv), sdv=c4(D, N, Hkv), scale=0.088, causal=1,
+             dtype=0, ws=FAKE, ws_bytes=lib.attn_bwd_workspace_bytes(B, Hq, N), stream=None)
+    a.update(kw)
+    return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["Hq"],
+                        a["Hkv"], a["Nq"], a["Nkv"], a["D"], a["sq"], a["sk"], a["sv"], a["so"], a["sdo"], a["sdq"],
+                        a["sdk"], a["sdv"], a["scale"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), NULL), (dict(lse=None), NULL), (dict(dk=None), NULL),
+    (dict(Nq=0), SHAPE), (dict(Hq=3), SHAPE), (dict(B=0), SHAPE),
+    (dict(D=96), UNSUP), (dict(causal=3), UNSUP), (dict(dtype=7), UNSUP), (dict(scale=float("nan")), UNSUP),
+    (dict(lse=FAKE + 2), UNSUP), (dict(dv=FAKE + 8), UNSUP), (dict(sdo=S(0, 128, 130, 1)), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 32, 8192) == 2 * 32 * 8192 * 8
+    assert lib.attn_bwd_workspace_bytes(0, 1, 1) == 0
 
 
 def fwdv(lib, **kw):
