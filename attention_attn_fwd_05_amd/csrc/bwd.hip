@@ -18,13 +18,13 @@
 //     S^T = K Q^T and dP^T = V dO^T come out one query per lane, so lse and
 //     delta are one value per lane; dQ^T += K^T dS^T reads K^T with the
 //     transposing LDS read from the same tile.
-//   * bwd_dkdv: the roles swapped.  A workgroup of 4 waves (one per SIMD, so
-//     K, V and both accumulators fit in registers) owns 128 keys of one kv head
-//     (32 per wave, K and V register-resident B operands) and streams the Q,
-//     dO, lse/delta tiles of every q head of the group, so the group's
-//     gradients add up in registers.  S = Q K^T and dP = dO V^T come out one
-//     key per lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with
-//     the transposing LDS read.
+//   * bwd_dkdv: the roles swapped.  A workgroup of 8 waves owns 128 keys of
+//     one kv head, held in LDS with their V rows; each wave pair shares 32 keys
+//     and splits every 64-query tile.  It streams the Q, dO, lse/delta tiles of
+//     every q head of the group (2-stage ring), so the group's gradients add
+//     up in registers.  S = Q K^T and dP = dO V^T come out one key per lane;
+//     dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with the transposing
+//     LDS read; the pair's partial sums are added through LDS at the end.
 //   The 16-bit P (and dS) B operands take the key (query) order of the fp32
 //   accumulator registers, matched by the transposing reads' addresses, as in
 //   the forward.  Causal: the dq loop stops at its block's diagonal, the dkdv
@@ -42,9 +42,8 @@ namespace {
 
 constexpr int kDqW = 8;           // waves per dq workgroup (two per SIMD)
 constexpr int kDqRows = 32 * kDqW; // query rows per dq workgroup
-constexpr int kKvW = 4;           // waves per dkdv workgroup (one per SIMD: K, V and two
-                                  // accumulators stay in registers)
-constexpr int kKvRows = 32 * kKvW; // keys per dkdv workgroup
+constexpr int kKvW = 8;           // waves per dkdv workgroup (two per SIMD)
+constexpr int kKvRows = 128;      // keys per dkdv workgroup (32 per wave pair)
 constexpr int kBT = 64;           // streamed rows per LDS tile
 constexpr int kBStages = 3;      // LDS ring depth
 
@@ -86,14 +85,18 @@ struct DqLds {
   static constexpr int ELEMS = 2 * kBStages * TILE;
 };
 
-// LDS ring of the dkdv kernel: dO tiles, Q tiles, then the (lse2, delta) rows
+// LDS of the dkdv kernel: the block's K and V rows, a 2-stage ring of (Q, dO)
+// tile pairs, and the (lse2, delta) rows of each stage
 template <int D>
 struct DkvLds {
-  static constexpr int TILE = kBT * D;
-  static constexpr int DO0 = 0;
-  static constexpr int Q0 = kBStages * TILE;
-  static constexpr int LD0 = 2 * kBStages * TILE;  // in 16-bit elements; 2 * kBT floats per stage
-  static constexpr int ELEMS = LD0 + kBStages * 4 * kBT;
+  static constexpr int TILE = kBT * D;        // one Q (or dO) tile
+  static constexpr int KB = kKvRows * D;      // the block's K (or V) rows
+  static constexpr int K0 = 0;
+  static constexpr int V0 = KB;
+  static constexpr int Q0 = 2 * KB;           // stage s: Q at Q0 + 2 s TILE, dO right after
+  static constexpr int LD0 = 2 * KB + 2 * 2 * TILE;  // in 16-bit elements; 2 kBT floats per stage
+  static constexpr int ELEMS = LD0 + 2 * 4 * kBT;
+  static_assert(2 * (2 * 2 * TILE) <= 65536, "Q/dO read offsets fit the 16-bit DS offset");
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0; expcnt, lgkmcnt at
@@ -146,15 +149,15 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   static_assert(NB >= 1, "every wave loads at least one block");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
 
-  const int per_unit = a.group * a.nqb;
-  const int unit = blockIdx.x / per_unit;
-  const int rem = blockIdx.x - unit * per_unit;
-  int qb = rem / a.group;
-  const int hg = rem - qb * a.group;
-  if (CAUSAL) qb = a.nqb - 1 - qb;  // longest blocks first
-  const int b = unit / a.Hkv;
-  const int kvh = unit - b * a.Hkv;
-  const int h = kvh * a.group + hg;
+  // the query block runs slowest: under a causal mask the last blocks see the
+  // most keys, so every head's costliest blocks start first
+  const int heads = a.B * a.Hq;
+  int qb = blockIdx.x / heads;
+  const int bh = blockIdx.x - qb * heads;
+  if (CAUSAL) qb = a.nqb - 1 - qb;
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int kvh = h / a.group;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,44 +311,42 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   }
 }
 
-// ---- dK, dV: one workgroup per (batch, kv head, 128 keys)
+// ---- dK, dV: one workgroup per (batch, kv head, 128 keys).  Wave w owns keys
+//      32 (w % 4) .. +31 and, of every 64-query tile, the 32 queries
+//      32 (w / 4) .. +31; the two waves of a key group add their partial dK,
+//      dV through LDS at the end.  The block's K and V rows sit in LDS (B
+//      operands read with plain 16-byte reads), so only the two accumulators
+//      are register-resident and two waves fit on each SIMD.
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(64 * kKvW, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   using L = DkvLds<D>;
   constexpr int KS = D / 16, DT = D / 32, C = D / 8;
-  constexpr int NB = L::TILE * 2 / 1024 / kKvW;
+  constexpr int NB = L::TILE * 2 / 1024 / kKvW;   // 1 KiB DMA blocks per wave per Q (dO) tile
+  constexpr int NBK = L::KB * 2 / 1024 / kKvW;    // ... per K (V) block
   constexpr int RPB = 64 / C;
-  static_assert(NB >= 1, "every wave loads at least one block");
+  static_assert(NB >= 1 && NBK >= 1, "every wave loads at least one block");
+  // the partial sums of the kKvW / 2 second-half waves (2 accumulators x DT x
+  // 16 floats x 64 lanes) fit in the LDS they reuse
+  static_assert((kKvW / 2) * 2 * DT * 16 * 64 * 4 <= L::ELEMS * 2, "partial sums fit in LDS");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
 
-  const int unit = blockIdx.x / a.nkb;
-  const int kbk = blockIdx.x - unit * a.nkb;  // ascending: under a causal mask the first blocks see the most queries
+  // the key block runs slowest: under a causal mask the first blocks see the
+  // most queries, so every (batch, kv head)'s costliest blocks start first
+  const int units = a.B * a.Hkv;
+  const int kbk = blockIdx.x / units;
+  const int unit = blockIdx.x - kbk * units;
   const int b = unit / a.Hkv;
   const int kvh = unit - b * a.Hkv;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w & 3, qh = w >> 2;  // key group, query half
   const int n = lane & 31, hh = lane >> 5;
   const int k0 = kbk * kKvRows;
-  const int key = k0 + 32 * w + n;
-
-  // stationary B operands: K and V rows (zeros past Nkv)
-  u32x4 kf[KS], vf[KS];
-  {
-    const int64_t ko = (int64_t)k0 * a.skn, vo = (int64_t)k0 * a.svn;
-    const auto rk = make_rsrc(a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh + ko, clamp_bytes(a.k_bytes - 2 * ko));
-    const auto rv = make_rsrc(a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh + vo, clamp_bytes(a.v_bytes - 2 * vo));
-    const int32_t ok = (32 * w + n) * (int32_t)a.skn * 2 + 16 * hh;
-    const int32_t ov = (32 * w + n) * (int32_t)a.svn * 2 + 16 * hh;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = bload16(rk, ok + 32 * ks);
-      vf[ks] = bload16(rv, ov + 32 * ks);
-    }
-  }
+  const int key = k0 + 32 * kg + n;
 
   // query tiles: from the first that sees key k0 to the end, for every q head
-  // of the group; tiles from full_from on see all 256 keys of the block
+  // of the group; tiles from full_from on see all keys of the block
   const int off = CAUSAL ? a.causal_off : 0;
   const int ntq = (a.Nq + kBT - 1) / kBT;
   const int tq0 = CAUSAL ? min(max(0, k0 - off) / kBT, ntq) : 0;
@@ -353,6 +354,28 @@ __global__ __launch_bounds__(64 * kKvW, 1) void bwd_dkdv_kernel(const BwdArgs a)
   const int nt = ntq - tq0;
   const int total = nt * a.group;
 
+  // DMA: the block's K and V rows once, then per tile the Q and dO rows and
+  // the (lse2, delta) pairs (8 bytes a row, 64 bytes a wave, 4 lanes: a
+  // buffer-to-LDS load writes for every active lane)
+  auto dma_rows = [&](int32_t (&o)[NBK], int64_t stride) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) {
+      const int row = RPB * (NBK * w + i) + lane / C;
+      o[i] = row * (int32_t)stride * 2 + 16 * ((lane % C) ^ swz<D>(row));
+    }
+  };
+  {
+    int32_t ok[NBK], ov[NBK];
+    dma_rows(ok, a.skn);
+    dma_rows(ov, a.svn);
+    const int64_t ko = (int64_t)k0 * a.skn, vo = (int64_t)k0 * a.svn;
+    const i32x4 rk = rsrc_words(a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh + ko, clamp_bytes(a.k_bytes - 2 * ko));
+    const i32x4 rv = rsrc_words(a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh + vo, clamp_bytes(a.v_bytes - 2 * vo));
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) dma16(rk, lds_addr(smem + L::K0) + 1024 * (NBK * w + i), ok[i]);
+#pragma unroll
+    for (int i = 0; i < NBK; ++i) dma16(rv, lds_addr(smem + L::V0) + 1024 * (NBK * w + i), ov[i]);
+  }
   int32_t dq_[NB], dg_[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -361,12 +384,8 @@ __global__ __launch_bounds__(64 * kKvW, 1) void bwd_dkdv_kernel(const BwdArgs a)
     dq_[i] = row * (int32_t)a.sqn * 2 + 16 * chunk;
     dg_[i] = row * (int32_t)a.sdon * 2 + 16 * chunk;
   }
+  constexpr int LDW = kBT * 8 / kKvW;  // (lse2, delta) bytes per wave per tile
   const uint32_t lds_q = lds_addr(smem + L::Q0) + 1024 * NB * w;
-  const uint32_t lds_g = lds_addr(smem + L::DO0) + 1024 * NB * w;
-  // (lse2, delta) rows: 8 bytes each, 512 bytes per tile; every wave loads
-  // LDW of them with LDW / 16 lanes (the other lanes stay inactive: a
-  // buffer-to-LDS load writes for every active lane)
-  constexpr int LDW = kBT * 8 / kKvW;
   const uint32_t lds_ld = lds_addr(smem + L::LD0) + LDW * w;
   const float* ldb = a.ld + 2 * ((int64_t)b * a.Hq) * a.Nq;
   auto dma_tile = [&](int it, int stage) __attribute__((always_inline)) {
@@ -379,19 +398,22 @@ __global__ __launch_bounds__(64 * kKvW, 1) void bwd_dkdv_kernel(const BwdArgs a)
                                 clamp_bytes(a.do_bytes - 2 * go));
     const int64_t lo = ((int64_t)h * a.Nq + (int64_t)t * kBT) * 2;
     const i32x4 rl = rsrc_words(ldb + lo, clamp_bytes(((int64_t)a.Nq - (int64_t)t * kBT) * 8));
+    const uint32_t sq = lds_q + stage * 2 * L::TILE * 2;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rq, lds_q + 2 * stage * L::TILE + 1024 * i, dq_[i]);
+    for (int i = 0; i < NB; ++i) dma16(rq, sq + 1024 * i, dq_[i]);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rg, lds_g + 2 * stage * L::TILE + 1024 * i, dg_[i]);
+    for (int i = 0; i < NB; ++i) dma16(rg, sq + 2 * L::TILE + 1024 * i, dg_[i]);
     if (lane < LDW / 16) dma16(rl, lds_ld + stage * 4 * kBT * 2, LDW * w + 16 * lane);
   };
 
-  uint32_t qa[KS], ga[KS], qt[DT][2], gt[DT][2];
-  row_addrs<D>(lds_addr(smem + L::Q0), lane, qa);
-  row_addrs<D>(lds_addr(smem + L::DO0), lane, ga);
-  tr_addrs<D>(lds_addr(smem + L::Q0), lane, qt);
-  tr_addrs<D>(lds_addr(smem + L::DO0), lane, gt);
-  const uint32_t ldr = opaque_lds(lds_addr(smem + L::LD0) + 32 * hh);  // + (32u + 8g) * 8 per read
+  // LDS operand addresses; Q-tile addresses reach the dO tile, the other
+  // stage and the subtiles through immediate offsets (< 64 KiB), and the K
+  // addresses reach V the same way
+  uint32_t qa[KS], qt[DT][2], kva[KS];
+  row_addrs<D>(lds_addr(smem + L::Q0) + 2 * 32 * qh * D, lane, qa);
+  tr_addrs<D>(lds_addr(smem + L::Q0) + 2 * 32 * qh * D, lane, qt);
+  row_addrs<D>(lds_addr(smem + L::K0) + 2 * 32 * kg * D, lane, kva);
+  const uint32_t ldr = opaque_lds(lds_addr(smem + L::LD0) + 32 * qh * 8 + 32 * hh);  // + 8g * 8 per read
 
   f32x16 adv[DT], adk[DT];
 #pragma unroll
@@ -400,58 +422,48 @@ __global__ __launch_bounds__(64 * kKvW, 1) void bwd_dkdv_kernel(const BwdArgs a)
     adk[dt] = f32x16{};
   }
   const float c = a.c;
-  const int wk_lo = k0 + 32 * w;  // this wave's first key
+  const int kmin = k0 + 32 * kg;  // this wave's first key
 
   auto compute = [&](int stage, int it, bool masked) __attribute__((always_inline)) {
     const int hgi = it / nt;
-    const int tq = (tq0 + (it - hgi * nt)) * kBT;
-    u32x4 pp[4], dp[4];
-    bool act[2];
+    const int tq = (tq0 + (it - hgi * nt)) * kBT + 32 * qh;  // this wave's first query
+    // 32 queries wholly before this wave's keys see none of them
+    if (masked && CAUSAL && kmin > tq + 31 + off) return;
+    const uint32_t sq = stage * 2 * L::TILE * 2, sg = sq + 2 * L::TILE;
+    f32x16 sx = f32x16{}, px = f32x16{};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // a subtile of 32 queries wholly before this wave's keys sees none of them
-      act[u] = !masked || !CAUSAL || wk_lo <= tq + 32 * u + 31 + off;
-      if (!act[u]) continue;
-      const uint32_t so = 2 * stage * L::TILE + 2 * 32 * u * D;
-      f32x16 s = f32x16{}, p = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma_32x32x16<BF16>(lds_load16(qa[ks] + so), kf[ks], s);
-        p = mfma_32x32x16<BF16>(lds_load16(ga[ks] + so), vf[ks], p);
-      }
-      // element e of lane (n, hh) is query tq + 32u + 8(e/4) + 4hh + e%4, key `key`
-      f32x16 pr, ds;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t lo = ldr + stage * 4 * kBT * 2 + (32 * u + 8 * g) * 8;
-        const f32x4 a0 = __builtin_bit_cast(f32x4, lds_load16(lo));
-        const f32x4 a1 = __builtin_bit_cast(f32x4, lds_load16(lo + 16));
-        const float l2[4] = {a0[0], a0[2], a1[0], a1[2]};
-        const float dl[4] = {a0[1], a0[3], a1[1], a1[3]};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * g + j;
-          float pv = fast_exp2(__builtin_fmaf(s[e], c, -l2[j]));
-          if (masked && CAUSAL) {
-            const int qry = tq + 32 * u + 8 * g + 4 * hh + j;
-            pv = (key <= qry + off) ? pv : 0.f;
-          }
-          pr[e] = pv;
-          ds[e] = pv * (p[e] - dl[j]);
-        }
-      }
-      pack_pt<BF16>(pr, pp + 2 * u);
-      pack_pt<BF16>(ds, dp + 2 * u);
+    for (int ks = 0; ks < KS; ++ks) {
+      sx = mfma_32x32x16<BF16>(lds_load16(qa[ks] + sq), lds_load16(kva[ks]), sx);
+      px = mfma_32x32x16<BF16>(lds_load16(qa[ks] + sg), lds_load16(kva[ks] + 2 * L::KB), px);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's queries
+    // element e of lane (n, hh) is query tq + 8(e/4) + 4hh + e%4, key `key`
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (!act[kk >> 1]) continue;
-      const uint32_t o = 2 * stage * L::TILE + 2 * 16 * kk * D;
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t lo = ldr + stage * 4 * kBT * 2 + 8 * g * 8;
+      const f32x4 a0 = __builtin_bit_cast(f32x4, lds_load16(lo));
+      const f32x4 a1 = __builtin_bit_cast(f32x4, lds_load16(lo + 16));
+      const float l2[4] = {a0[0], a0[2], a1[0], a1[2]};
+      const float dl[4] = {a0[1], a0[3], a1[1], a1[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * g + j;
+        float pv = fast_exp2(__builtin_fmaf(sx[e], c, -l2[j]));
+        if (masked && CAUSAL) pv = (key <= tq + 8 * g + 4 * hh + j + off) ? pv : 0.f;
+        sx[e] = pv;
+        px[e] = pv * (px[e] - dl[j]);
+      }
+    }
+    u32x4 pp[2], dp[2];
+    pack_pt<BF16>(sx, pp);
+    pack_pt<BF16>(px, dp);
+    // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t o = sq + 2 * 16 * kk * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x2 glo = lds_read_tr16(gt[dt][0] + o);
-        const u32x2 ghi = lds_read_tr16(gt[dt][1] + o);
+        const u32x2 glo = lds_read_tr16(qt[dt][0] + o + 2 * L::TILE);
+        const u32x2 ghi = lds_read_tr16(qt[dt][1] + o + 2 * L::TILE);
         adv[dt] = mfma_32x32x16<BF16>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pp[kk], adv[dt]);
         const u32x2 qlo = lds_read_tr16(qt[dt][0] + o);
         const u32x2 qhi = lds_read_tr16(qt[dt][1] + o);
@@ -460,44 +472,53 @@ __global__ __launch_bounds__(64 * kKvW, 1) void bwd_dkdv_kernel(const BwdArgs a)
     }
   };
 
-  constexpr int NDMA = 2 * NB + 1;
-  static_assert(NDMA < 16, "vmcnt field");
+  // 2-stage ring: the loads of tile it + 1 go out before tile it is computed
   if (total > 0) dma_tile(0, 0);
-  if (total > 1) dma_tile(1, 1);
-  if (total > 1)
-    __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
-  else
-    __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
+  __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
   barrier_nofence();
   for (int it = 0; it < total; ++it) {
-    const int stage = it % 3;
-    const bool pre = it + 2 < total;
-    if (pre) dma_tile(it + 2, (stage + 2) % 3);
+    const int stage = it & 1;
+    if (it + 1 < total) dma_tile(it + 1, stage ^ 1);
     const int t = tq0 + it % nt;
     compute(stage, it, CAUSAL && t < full_from);
-    if (pre)
-      __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
+    __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
     barrier_nofence();
   }
 
-  // ---- dV = (dV^T)^T, dK = scale (dK^T)^T, cast, store
-  if (key < a.Nkv) {
-    uint16_t* vp = a.dv + (int64_t)b * a.sdvb + (int64_t)kvh * a.sdvh + (int64_t)key * a.sdvn;
-    uint16_t* kp = a.dk + (int64_t)b * a.sdkb + (int64_t)kvh * a.sdkh + (int64_t)key * a.sdkn;
+  // ---- add the two query halves' partial sums (through LDS), then
+  //      dV = (dV^T)^T, dK = scale (dK^T)^T, cast, store
+  float* red = reinterpret_cast<float*>(smem);  // [key group][dV, dK][dt][e][lane]
+  if (qh == 1) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hh;
-        *reinterpret_cast<u32x2*>(vp + d) = u32x2{pack2<BF16>(adv[dt][4 * g], adv[dt][4 * g + 1]),
-                                                  pack2<BF16>(adv[dt][4 * g + 2], adv[dt][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(kp + d) =
-            u32x2{pack2<BF16>(adk[dt][4 * g] * a.scale, adk[dt][4 * g + 1] * a.scale),
-                  pack2<BF16>(adk[dt][4 * g + 2] * a.scale, adk[dt][4 * g + 3] * a.scale)};
+      for (int e = 0; e < 16; ++e) {
+        red[(((kg * 2 + 0) * DT + dt) * 16 + e) * 64 + lane] = adv[dt][e];
+        red[(((kg * 2 + 1) * DT + dt) * 16 + e) * 64 + lane] = adk[dt][e];
       }
   }
+  __syncthreads();
+  if (qh == 1 || key >= a.Nkv) return;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      adv[dt][e] += red[(((kg * 2 + 0) * DT + dt) * 16 + e) * 64 + lane];
+      adk[dt][e] += red[(((kg * 2 + 1) * DT + dt) * 16 + e) * 64 + lane];
+    }
+  uint16_t* vp = a.dv + (int64_t)b * a.sdvb + (int64_t)kvh * a.sdvh + (int64_t)key * a.sdvn;
+  uint16_t* kp = a.dk + (int64_t)b * a.sdkb + (int64_t)kvh * a.sdkh + (int64_t)key * a.sdkn;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * hh;
+      *reinterpret_cast<u32x2*>(vp + d) = u32x2{pack2<BF16>(adv[dt][4 * g], adv[dt][4 * g + 1]),
+                                                pack2<BF16>(adv[dt][4 * g + 2], adv[dt][4 * g + 3])};
+      *reinterpret_cast<u32x2*>(kp + d) =
+          u32x2{pack2<BF16>(adk[dt][4 * g] * a.scale, adk[dt][4 * g + 1] * a.scale),
+                pack2<BF16>(adk[dt][4 * g + 2] * a.scale, adk[dt][4 * g + 3] * a.scale)};
+    }
 }
 
 template <int D, bool BF16, bool CAUSAL>

@@ -26,13 +26,14 @@ FETCH_SIZE and WRITE_SIZE counters measured (scaled by a plain copy's reading),
 taken from the committed summaries under profiles/; null once the kernel
 sources differ from the ones those counters were taken with.
 
-The default run also times five widened workloads (not the headline):
+The default run also times six widened workloads (not the headline):
 decode with per-sequence cache lengths over a 16-sequence batch, the same
 batch over a paged cache (16-slot pages in a shuffled pool), a chunked
 prefill (1024 queries at the end of an 8192-token context, causal aligned
 bottom-right), a packed prefill of 16 sequences of seeded lengths up to
-4096, and a causal sliding window of 4096 keys on the 8192-token serving
-shape; they are printed under "widened".
+4096, a causal sliding window of 4096 keys on the 8192-token serving
+shape, and the backward (dQ, dK, dV) of the headline prefill; they are
+printed under "widened".
 
 Flags: --only prefill|decode|copy runs just that launch (for rocprofv3 runs),
 --no-cpu skips the oracle baseline.  Prints one JSON line.
@@ -56,7 +57,7 @@ if ROOT not in sys.path:
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 CSRC = os.path.join(ROOT, "attention_attn_fwd_05_amd", "csrc")
-PREFILL_SOURCES = ["prefill_fwd.hip", "kernel_common.hpp", "launch.hpp", "attn_api.cpp"]
+PREFILL_SOURCES = ["prefill_fwd.hip", "lds_tile.hpp", "kernel_common.hpp", "launch.hpp", "attn_api.cpp"]
 DECODE_SOURCES = ["decode.hip", "kernel_common.hpp", "launch.hpp", "attn_api.cpp"]
 
 
@@ -370,6 +371,33 @@ def main():
             "tflops": round(wflops / (wt * 1e-3) / 1e12, 1),
             "frac_of_2500_tflops": round(wflops / (wt * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
         del wq, wk, wv, wo
+        # backward of the headline prefill (dQ, dK, dV from the forward's O, lse)
+        bc = W.serving(8192, True)
+        bq, bk, bv = (t.to(dev) for t in W.prefill_inputs(bc))
+        bdo = torch.randn(bq.shape, generator=torch.Generator().manual_seed(W.BASE_SEED + 60)).to(bq.dtype).to(dev)
+        bo, blse = A.attn_fwd(bq, bk, bv, causal=True, scale=bc.softmax_scale, return_lse=True)
+        bdq, bdk, bdv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+        bws = torch.empty(A.load_library().attn_bwd_workspace_bytes(bc.B, bc.Hq, bc.Nq), dtype=torch.uint8,
+                          device=dev)
+        run_bwd = lambda: A.attn_bwd(bq, bk, bv, bo, bdo, blse, causal=True, scale=bc.softmax_scale, dq=bdq,
+                                     dk=bdk, dv=bdv, workspace=bws)
+        for _ in range(2):
+            run_bwd()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0.record(stream)
+        for _ in range(5):
+            run_bwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bt = e0.elapsed_time(e1) / 5
+        bflops = int(2.5 * bc.flops())  # 5 GEMMs against the forward's 2
+        widened["backward"] = {
+            "workload": bc.name + "_backward", "B": bc.B, "Hq": bc.Hq, "Hkv": bc.Hkv, "N": bc.Nq, "D": bc.D,
+            "flops_per_launch": bflops, "flop_count": "5 GEMMs (2.5x the forward's causal count); the kernels issue 7",
+            "ms_per_launch": round(bt, 4), "tflops": round(bflops / (bt * 1e-3) / 1e12, 1),
+            "frac_of_2500_tflops": round(bflops / (bt * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+        del bq, bk, bv, bdo, bo, blse, bdq, bdk, bdv, bws
 
     # context: achievable HBM rate of a plain 256 MiB device copy (read + write)
     copy_gbs = None
