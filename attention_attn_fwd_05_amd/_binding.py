@@ -91,6 +91,9 @@ def load_library():
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, S, S, S, S,
                              f32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, S, S,
+                                    S, S, f32, Mask, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd_masked.restype = i32
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, i32, vp]
     lib.kv_cache_write.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -475,11 +478,12 @@ def kv_cache_write_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, k_new: to
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
              lse: torch.Tensor, *, causal: bool, scale: float | None = None, causal_align: str = "top_left",
              dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
-             workspace: torch.Tensor | None = None):
+             workspace: torch.Tensor | None = None, window=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for an upstream gradient ``dout``.
 
     q, o, dout (B,Hq,Nq,D); k, v (B,Hkv,Nkv,D); lse fp32 (B,Hq,Nq) from attn_fwd
     with the same inputs, mask and scale.  A kv head's dk, dv sum its group's q heads.
+    ``window=(left, right)`` as in ``attn_fwd`` (calls attn_bwd_masked).
     """
     if causal_align not in _CAUSAL_ALIGN:
         raise ValueError("causal_align must be 'top_left' or 'bottom_right'")
@@ -503,12 +507,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     _on_gpu(q, k, v, o, dout, lse, dq, dk, dv, workspace)
     code = _dtype_code(q, k, v, o, dout, dq, dk, dv)
     s = _default_scale(D) if scale is None else float(scale)
-    st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D,
-                      _strides4(q), _strides4(k), _strides4(v), _strides4(o), _strides4(dout),
-                      _strides4(dq), _strides4(dk), _strides4(dv), s,
-                      _CAUSAL_ALIGN[causal_align] if causal else 0, code, workspace.data_ptr(),
-                      workspace.numel(), _stream(q))
-    _check(st, "attn_bwd")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D,
+            _strides4(q), _strides4(k), _strides4(v), _strides4(o), _strides4(dout),
+            _strides4(dq), _strides4(dk), _strides4(dv), s)
+    tail = (code, workspace.data_ptr(), workspace.numel(), _stream(q))
+    if window is not None:
+        _check(lib.attn_bwd_masked(*args, _mask(causal, causal_align, window), *tail), "attn_bwd_masked")
+    else:
+        _check(lib.attn_bwd(*args, _CAUSAL_ALIGN[causal_align] if causal else 0, *tail), "attn_bwd")
     return dq, dk, dv
 

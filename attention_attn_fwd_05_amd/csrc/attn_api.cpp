@@ -469,17 +469,17 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
   return (size_t)B * Hq * Nq * 8;
 }
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
-                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
-                     attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale, int causal,
-                     attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+static attn_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv,
+                            int D, attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            attn_strides sdo, attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale,
+                            MaskSpec mk, attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nkv <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
-  if (causal < ATTN_CAUSAL_NONE || causal > ATTN_CAUSAL_BOTTOM_RIGHT) return ATTN_ERR_UNSUPPORTED;
+  if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
   for (const attn_strides* st : {&sq, &sk, &sv, &so, &sdo, &sdq, &sdk, &sdv})
     if (!strides_ok(*st) || st->n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
   for (const void* p : {q, k, v, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
@@ -517,8 +517,10 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   a.nkb = (int)nkb;
   a.dq_blocks = (unsigned)dq_blocks;
   a.dkv_blocks = (unsigned)dkv_blocks;
-  a.causal = causal != ATTN_CAUSAL_NONE;
-  a.causal_off = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? Nkv - Nq : 0;
+  a.mask = mk.mode;
+  a.causal_off = mk.bottom_right ? Nkv - Nq : 0;
+  a.win_left = mk.left;
+  a.win_right = mk.right;
   a.bf16 = dtype == ATTN_BF16;
   a.c = scale * kLog2e;
   a.scale = scale;
@@ -528,6 +530,24 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   a.do_bytes = slice_bytes(Nq, sdo.n, D);
   const hipError_t e = attn::launch_bwd(a, D, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
+                     attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
+                     attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale, int causal,
+                     attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, sq, sk, sv, so, sdo, sdq, sdk, sdv,
+                  scale, mask_of_causal(causal), dtype, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv,
+                            int D, attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            attn_strides sdo, attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale,
+                            attn_mask mask, attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, sq, sk, sv, so, sdo, sdq, sdk, sdv,
+                  scale, mask_of(mask), dtype, workspace, workspace_bytes, stream);
 }
 
 attn_status kv_cache_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

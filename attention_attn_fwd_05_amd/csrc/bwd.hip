@@ -139,9 +139,14 @@ __device__ __forceinline__ void pack_pt(const f32x16& x, u32x4* pf) {
   for (int e = 0; e < 16; e += 2) pf[e >> 3][(e & 7) >> 1] = pack2<BF16>(x[e], x[e + 1]);
 }
 
-// ---- dQ: one workgroup per (batch, q head, 256 query rows)
-template <int D, bool BF16, bool CAUSAL>
+// open side of a band: a bound no key or query reaches
+constexpr int kOpen = 1 << 30;
+
+// ---- dQ: one workgroup per (batch, q head, 256 query rows).  MASK 0: none;
+//      1: causal (j <= i + off); 2: band i + off - win_left <= j <= i + off + win_right
+template <int D, bool BF16, int MASK>
 __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
+  constexpr bool CAUSAL = MASK == 1, BAND = MASK == 2;
   using L = DqLds<D>;
   constexpr int KS = D / 16, DT = D / 32, C = D / 8;
   constexpr int NB = L::TILE * 2 / 1024 / kDqW;  // 1 KiB DMA blocks per wave per tile
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   const int heads = a.B * a.Hq;
   int qb = blockIdx.x / heads;
   const int bh = blockIdx.x - qb * heads;
-  if (CAUSAL) qb = a.nqb - 1 - qb;
+  if (MASK != 0) qb = a.nqb - 1 - qb;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int kvh = h / a.group;
@@ -189,10 +194,18 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
 
   const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
   const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
-  const int off = CAUSAL ? a.causal_off : 0;
-  const int kv_end = CAUSAL ? max(0, min(a.Nkv, q0 + kDqRows + off)) : a.Nkv;
+  const int off = MASK != 0 ? a.causal_off : 0;
+  const int WL = BAND ? (a.win_left < 0 ? kOpen : a.win_left) : 0;
+  const int WR = BAND ? (a.win_right < 0 ? kOpen : a.win_right) : 0;
+  // keys this block's rows see: up to the diagonal (causal), within the band
+  const int kv_end = CAUSAL ? max(0, min(a.Nkv, q0 + kDqRows + off))
+                            : (BAND ? max(0, min(a.Nkv, q0 + kDqRows + off + WR)) : a.Nkv);
   const int ntiles = (kv_end + kBT - 1) / kBT;
-  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, a.Nkv)) / kBT : a.Nkv / kBT;
+  const int t_begin = BAND ? min(max(0, q0 + off - WL) / kBT, ntiles) : 0;
+  // tiles every row sees in full: [full_lo, n_full)
+  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, a.Nkv)) / kBT
+                            : (BAND ? max(0, min(a.Nkv, q0 + off + WR + 1)) / kBT : a.Nkv / kBT);
+  const int full_lo = BAND ? (max(0, q0 + kDqRows - 1 + off - WL) + kBT - 1) / kBT : 0;
 
   // DMA geometry (as the forward): wave w fills 1 KiB blocks NB w .. NB w + NB - 1
   int32_t dk[NB], dv[NB];
@@ -225,13 +238,15 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   const float c = a.c;
   const int wq_hi = q0 + 32 * w + 31 + off;
+  const int wq_lo = q0 + 32 * w + off;
 
   auto compute = [&](int stage, int t, bool masked) __attribute__((always_inline)) {
     const int kb = t * kBT;
     bool act1 = true;
     if (masked) {
       if (kb >= a.Nkv || (CAUSAL && kb > wq_hi)) return;
-      act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi);
+      if (BAND && (kb > wq_hi + WR || kb + kBT - 1 < wq_lo - WL)) return;  // outside this wave's band
+      act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi) && (!BAND || kb + 32 <= wq_hi + WR);
     }
     // per 32-key subtile u: S^T = K Q^T, dP^T = V dO^T, then dS^T = P^T (dP^T -
     // delta) with P^T = exp2(S^T c - lse2); element e of lane (n, hh) is key
@@ -252,7 +267,8 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
         float pv = fast_exp2(__builtin_fmaf(sx[e], c, -lse2));
         if (masked) {
           const int key = kb + 32 * u + 8 * (e >> 2) + 4 * hh + (e & 3);
-          pv = (key < a.Nkv && (!CAUSAL || key <= qrow + off)) ? pv : 0.f;
+          pv = (key < a.Nkv && (!CAUSAL || key <= qrow + off) &&
+                (!BAND || (key >= qrow + off - WL && key <= qrow + off + WR))) ? pv : 0.f;
         }
         sx[e] = pv * (px[e] - delta);
       }
@@ -277,18 +293,18 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   // 3-stage ring: the loads of tile t + 2 go out before tile t is computed
   constexpr int NDMA = 2 * NB;
   static_assert(NDMA < 16, "vmcnt field");
-  if (ntiles > 0) dma_tile(0, 0);
-  if (ntiles > 1) dma_tile(1, 1);
-  if (ntiles > 1)
+  if (t_begin < ntiles) dma_tile(t_begin, 0);
+  if (t_begin + 1 < ntiles) dma_tile(t_begin + 1, 1);
+  if (t_begin + 1 < ntiles)
     __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
   else
     __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
   barrier_nofence();
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t % 3;
+  for (int t = t_begin; t < ntiles; ++t) {
+    const int stage = (t - t_begin) % 3;
     const bool pre = t + 2 < ntiles;
     if (pre) dma_tile(t + 2, (stage + 2) % 3);
-    compute(stage, t, t >= n_full);
+    compute(stage, t, t >= n_full || t < full_lo);
     if (pre)
       __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
     else
@@ -317,8 +333,9 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
 //      dV through LDS at the end.  The block's K and V rows sit in LDS (B
 //      operands read with plain 16-byte reads), so only the two accumulators
 //      are register-resident and two waves fit on each SIMD.
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, int MASK>
 __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr bool CAUSAL = MASK == 1, BAND = MASK == 2;
   using L = DkvLds<D>;
   constexpr int KS = D / 16, DT = D / 32, C = D / 8;
   constexpr int NB = L::TILE * 2 / 1024 / kKvW;   // 1 KiB DMA blocks per wave per Q (dO) tile
@@ -345,12 +362,19 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   const int k0 = kbk * kKvRows;
   const int key = k0 + 32 * kg + n;
 
-  // query tiles: from the first that sees key k0 to the end, for every q head
-  // of the group; tiles from full_from on see all keys of the block
-  const int off = CAUSAL ? a.causal_off : 0;
-  const int ntq = (a.Nq + kBT - 1) / kBT;
-  const int tq0 = CAUSAL ? min(max(0, k0 - off) / kBT, ntq) : 0;
-  const int full_from = CAUSAL ? min(ntq, (max(0, k0 + kKvRows - 1 - off) + kBT - 1) / kBT) : 0;
+  // query tiles that see some key of the block, for every q head of the
+  // group: query i sees key j iff j <= i + off (causal), iff i + off - WL <=
+  // j <= i + off + WR (band); tiles in [full_lo, full_hi) see every key of it
+  const int off = MASK != 0 ? a.causal_off : 0;
+  const int WL = BAND ? (a.win_left < 0 ? kOpen : a.win_left) : 0;
+  const int WR = BAND ? (a.win_right < 0 ? kOpen : a.win_right) : 0;
+  const int ntq0 = (a.Nq + kBT - 1) / kBT;
+  const int ntq = BAND ? min(ntq0, (max(0, min(a.Nq, k0 + kKvRows - off + WL)) + kBT - 1) / kBT) : ntq0;
+  const int tq0 = CAUSAL ? min(max(0, k0 - off) / kBT, ntq)
+                         : (BAND ? min(max(0, k0 - off - WR) / kBT, ntq) : 0);
+  const int full_lo = CAUSAL ? min(ntq, (max(0, k0 + kKvRows - 1 - off) + kBT - 1) / kBT)
+                             : (BAND ? (max(0, k0 + kKvRows - 1 - off - WR) + kBT - 1) / kBT : 0);
+  const int full_hi = BAND ? max(0, k0 - off + WL + 1) / kBT : ntq;
   const int nt = ntq - tq0;
   const int total = nt * a.group;
 
@@ -427,8 +451,9 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   auto compute = [&](int stage, int it, bool masked) __attribute__((always_inline)) {
     const int hgi = it / nt;
     const int tq = (tq0 + (it - hgi * nt)) * kBT + 32 * qh;  // this wave's first query
-    // 32 queries wholly before this wave's keys see none of them
+    // 32 queries that see none of this wave's keys
     if (masked && CAUSAL && kmin > tq + 31 + off) return;
+    if (masked && BAND && (kmin > tq + 31 + off + WR || kmin + 31 < tq + off - WL)) return;
     const uint32_t sq = stage * 2 * L::TILE * 2, sg = sq + 2 * L::TILE;
     f32x16 sx = f32x16{}, px = f32x16{};
 #pragma unroll
@@ -449,6 +474,10 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
         const int e = 4 * g + j;
         float pv = fast_exp2(__builtin_fmaf(sx[e], c, -l2[j]));
         if (masked && CAUSAL) pv = (key <= tq + 8 * g + 4 * hh + j + off) ? pv : 0.f;
+        if (masked && BAND) {
+          const int p = tq + 8 * g + 4 * hh + j + off;
+          pv = (key >= p - WL && key <= p + WR) ? pv : 0.f;
+        }
         sx[e] = pv;
         px[e] = pv * (px[e] - dl[j]);
       }
@@ -480,7 +509,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     const int stage = it & 1;
     if (it + 1 < total) dma_tile(it + 1, stage ^ 1);
     const int t = tq0 + it % nt;
-    compute(stage, it, CAUSAL && t < full_from);
+    compute(stage, it, (MASK != 0) && (t < full_lo || t >= full_hi));
     __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
     barrier_nofence();
   }
@@ -521,20 +550,25 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     }
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, int MASK>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
   const int64_t prep_blocks = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
   hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL>), dim3(a.dq_blocks), dim3(64 * kDqW), 0, stream, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL>), dim3(a.dkv_blocks), dim3(64 * kKvW), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, MASK>), dim3(a.dq_blocks), dim3(64 * kDqW), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, MASK>), dim3(a.dkv_blocks), dim3(64 * kKvW), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_m(const BwdArgs& a, hipStream_t stream) {
+  if (a.mask == 2) return launch_bwd_t<D, BF16, 2>(a, stream);
+  return a.mask == 1 ? launch_bwd_t<D, BF16, 1>(a, stream) : launch_bwd_t<D, BF16, 0>(a, stream);
 }
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.causal ? launch_bwd_t<D, true, true>(a, stream) : launch_bwd_t<D, true, false>(a, stream);
-  return a.causal ? launch_bwd_t<D, false, true>(a, stream) : launch_bwd_t<D, false, false>(a, stream);
+  return a.bf16 ? launch_bwd_m<D, true>(a, stream) : launch_bwd_m<D, false>(a, stream);
 }
 
 }  // namespace

@@ -116,7 +116,9 @@ struct BwdArgs {
   int B, Hq, Hkv, Nq, Nkv, group;
   int nqb, nkb;                // query blocks (dq), key blocks (dkdv) per (batch, head)
   unsigned dq_blocks, dkv_blocks;
-  int causal, causal_off;      // query i sees keys j <= i + causal_off when causal
+  int mask;                    // 0 none, 1 causal, 2 band
+  int causal_off;              // query i sits at key position i + causal_off
+  int win_left, win_right;     // band bounds around that position (-1: open)
   int bf16;
   float c;                     // scale * log2(e)
   float scale;

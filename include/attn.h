@@ -191,8 +191,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *   q, o, dout, dq (B, Hq, Nq, D) and k, v, dk, dv (B, Hkv, Nkv, D) via their
  *   strides (rules as attn_fwd); dq, dk, dv are written (same dtype as q).
  *   lse: contiguous fp32 (B, Hq, Nq), as attn_fwd returns it for the same
- *   inputs, causal argument and scale.  causal: as attn_fwd (sliding windows
- *   are not supported here).  workspace: attn_bwd_workspace_bytes(B, Hq, Nq)
+ *   inputs, causal argument and scale.  causal: as attn_fwd (attn_bwd_masked
+ *   takes a band mask).  workspace: attn_bwd_workspace_bytes(B, Hq, Nq)
  *   bytes, 16-byte aligned, contents irrelevant.  Three kernels run in order on
  *   `stream` (row statistics, dQ, dK/dV); no atomics, so the result does not
  *   depend on scheduling.
@@ -202,6 +202,18 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
                      attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale, int causal,
                      attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_masked -- attn_bwd with a band mask (attn_mask) in place of the
+ * causal argument, the backward of attn_fwd_masked with the same mask: the
+ * dQ pass visits only the key tiles inside its rows' band and the dK/dV pass
+ * only the query tiles whose band reaches its keys.  Otherwise as attn_bwd.
+ */
+attn_status attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv,
+                            int D, attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
+                            attn_strides sdo, attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale,
+                            attn_mask mask, attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode needs

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_varlen_masked", "attn_decode",
                           "attn_decode_varlen", "attn_decode_paged", "attn_decode_ex", "attn_decode_workspace_bytes",
-                          "kv_cache_write", "kv_cache_write_paged", "attn_bwd", "attn_bwd_workspace_bytes",
+                          "kv_cache_write", "kv_cache_write_paged", "attn_bwd", "attn_bwd_masked", "attn_bwd_workspace_bytes",
                           "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n

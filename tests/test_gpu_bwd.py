@@ -51,19 +51,22 @@ def _check(name, got, ref, dtype, floor=0.0):
     assert err <= tol, f"{name}: max|err| {err:.3e} > {tol:.3e}"
 
 
-def run_bwd(name, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, align="top_left", seed=0):
+def run_bwd(name, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, align="top_left", seed=0, window=None):
     case = W.PrefillCase(name, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed=W.BASE_SEED + 120 + seed)
     q, k, v = W.prefill_inputs(case)
     g = torch.Generator().manual_seed(W.BASE_SEED + 220 + seed)
     do = torch.randn(B, Hq, Nq, D, generator=g).to(case.torch_dtype)
-    _say(f"{name} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} causal={causal} align={align}")
+    _say(f"{name} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} causal={causal} align={align} "
+         f"window={window}")
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
-    o, lse = A.attn_fwd(qd, kd, vd, causal=causal, causal_align=align, scale=case.softmax_scale, return_lse=True)
-    dq, dk, dv = A.attn_bwd(qd, kd, vd, o, dod, lse, causal=causal, causal_align=align, scale=case.softmax_scale)
+    o, lse = A.attn_fwd(qd, kd, vd, causal=causal, causal_align=align, scale=case.softmax_scale, return_lse=True,
+                        window=window)
+    dq, dk, dv = A.attn_bwd(qd, kd, vd, o, dod, lse, causal=causal, causal_align=align, scale=case.softmax_scale,
+                            window=window)
     torch.cuda.synchronize()
-    off = Nkv - Nq if (causal and align == "bottom_right") else 0
+    off = Nkv - Nq if ((causal or window is not None) and align == "bottom_right") else 0
     rq, rk, rv = oracle.attention_backward(_np(q), _np(k), _np(v), _np(do), case.softmax_scale, causal,
-                                           causal_offset=off)
+                                           causal_offset=off, window=window or (-1, -1))
     sc = case.softmax_scale
     _check("dQ", dq, rq, case.torch_dtype, _floor(D, Nkv, do, v.float(), sc, k.float()))
     _check("dK", dk, rk, case.torch_dtype, _floor(D, Nq, do, v.float(), sc, q.float()))
@@ -86,6 +89,36 @@ def test_bwd_heads_dtypes(Hq, Hkv, D, dtype):
 @pytest.mark.parametrize("Nq,Nkv", [(300, 1000), (700, 300), (1, 777)])
 def test_bwd_bottom_right(Nq, Nkv):
     run_bwd(f"bwd_br_{Nq}_{Nkv}", 1, 4, 2, Nq, Nkv, 128, "fp16", True, align="bottom_right", seed=Nq)
+
+
+BWD_BANDS = [
+    # name, Nq, Nkv, D, dtype, causal, align, window
+    ("causal_window256", 1000, 1000, 128, "fp16", True, "top_left", (255, -1)),
+    ("two_sided", 777, 777, 64, "bf16", False, "top_left", (100, 37)),
+    ("zero_width", 300, 300, 128, "fp16", False, "top_left", (0, 0)),
+    ("chunk_window", 300, 1500, 128, "fp16", True, "bottom_right", (511, -1)),
+    ("left_only_br", 400, 900, 64, "fp16", False, "bottom_right", (200, -1)),
+    ("right_only", 500, 500, 128, "bf16", False, "top_left", (-1, 64)),
+]
+
+
+@pytest.mark.parametrize("band", BWD_BANDS, ids=[b[0] for b in BWD_BANDS])
+def test_bwd_band(band):
+    name, Nq, Nkv, D, dtype, causal, align, window = band
+    run_bwd(f"bwd_{name}", 1, 4, 2, Nq, Nkv, D, dtype, causal, align=align, seed=Nq + Nkv, window=window)
+
+
+def test_bwd_band_wider_than_sequence_is_causal_bitwise():
+    case = W.PrefillCase("bwd_wide", 2, 8, 2, 1000, 1000, 128, "fp16", True, seed=W.BASE_SEED + 132)
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(case))
+    do = torch.randn_like(q)
+    _say(case.name)
+    o, lse = A.attn_fwd(q, k, v, causal=True, return_lse=True)
+    g1 = A.attn_bwd(q, k, v, o, do, lse, causal=True)
+    g2 = A.attn_bwd(q, k, v, o, do, lse, causal=True, window=(5000, -1))
+    torch.cuda.synchronize()
+    for a_, b_ in zip(g1, g2):
+        assert torch.equal(a_, b_)
 
 
 def test_bwd_cross_lengths_full():
