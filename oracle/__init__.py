@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward,
     attention_probs,
+    attention_varlen_backward,
     attention_varlen,
     decode,
     decode_paged,

@@ -91,6 +91,7 @@ __all__ = [
     "attention_varlen",
     "kv_cache_write",
     "attention_backward",
+    "attention_varlen_backward",
     "page_slot",
     "gather_pages",
     "decode_paged",
@@ -354,6 +355,35 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         O[pick] = Ob[0].transpose(1, 0, 2)
         lse[:, pick] = lb[0]
     return O, lse
+
+
+def attention_varlen_backward(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
+                              bottom_right: bool = False, window=(-1, -1)):
+    """Gradients of ``attention_varlen``'s O: ``attention_backward`` on each
+    sequence's own rows (no gradient crosses sequences).
+
+    q, do: (T_q, Hq, D); k, v: (T_k, Hkv, D); offsets as ``attention_varlen``.
+    Returns (dQ, dK, dV) float64 with the shapes of q, k, v; rows of a sequence
+    with no keys, and keys of a sequence with no queries, get zero gradients.
+    """
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64).reshape(-1)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64).reshape(-1)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(cq.shape[0] - 1):
+        q0, q1 = sequence_bounds(cq, b)
+        k0, k1 = sequence_bounds(ck, b)
+        if q1 == q0 or k1 == k0:
+            continue
+        masked = causal or window != (-1, -1)
+        off = varlen_causal_offset(q1 - q0, k1 - k0, bottom_right) if masked else 0
+        tq = lambda x, a, z: x[a:z].transpose(1, 0, 2)[None]
+        gq, gk, gv = attention_backward(tq(q, q0, q1), tq(k, k0, k1), tq(v, k0, k1), tq(do, q0, q1), scale, causal,
+                                        causal_offset=off, window=window)
+        dq[q0:q1] = gq[0].transpose(1, 0, 2)
+        dk[k0:k1] = gk[0].transpose(1, 0, 2)
+        dv[k0:k1] = gv[0].transpose(1, 0, 2)
+    return dq, dk, dv
 
 
 def kv_cache_write(k_cache, v_cache, k_new, v_new, pos: int):

@@ -448,6 +448,35 @@ def pin_backward_gqa_is_group_sum():
     np.testing.assert_allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-12)
 
 
+def pin_varlen_backward_finite_differences():
+    """P11d: the packed backward equals central finite differences of the
+    packed forward (L = sum(O * G)) for every element, with an empty query set,
+    a sequence without keys, L_q != L_k, bottom-right causal and a window."""
+    rng = np.random.default_rng(114)
+    Hq, Hkv, D, sc = 2, 1, 3, 0.7
+    lens = [(3, 4), (0, 2), (2, 0), (2, 3)]
+    cq = np.concatenate([[0], np.cumsum([a for a, _ in lens])])
+    ck = np.concatenate([[0], np.cumsum([b for _, b in lens])])
+    q, k, v = _rand(rng, int(cq[-1]), Hq, D), _rand(rng, int(ck[-1]), Hkv, D), _rand(rng, int(ck[-1]), Hkv, D)
+    g = _rand(rng, int(cq[-1]), Hq, D)
+    eps = 1e-6
+    for causal, br, win in ((True, True, (-1, -1)), (False, False, (1, 1))):
+        def loss(qq, kk, vv):
+            O, _ = OA.attention_varlen(qq, kk, vv, cq, ck, sc, causal, bottom_right=br, window=win)
+            return float((O * g).sum())
+        dq, dk, dv = OA.attention_varlen_backward(q, k, v, g, cq, ck, sc, causal, bottom_right=br, window=win)
+        for x, dx, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                ap, am = [q, k, v], [q, k, v]
+                ap[which], am[which] = xp, xm
+                num[idx] = (loss(*ap) - loss(*am)) / (2 * eps)
+            np.testing.assert_allclose(dx, num, rtol=0, atol=2e-8)
+
+
 def _scatter_to_pages(cache, perm, page_size):
     """Independent scatter of contiguous (B, Hkv, S, D) caches into a page pool:
     page perm[b * (S // page_size) + j] holds slots [j * ps, (j + 1) * ps) of sequence b."""
@@ -587,6 +616,7 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_matches_torch_autograd,
     pin_backward_gqa_is_group_sum,
+    pin_varlen_backward_finite_differences,
     pin_sliding_window_rows_are_slices,
     pin_zero_width_window_is_the_diagonal_key,
     pin_decode_window_is_the_last_slots,
