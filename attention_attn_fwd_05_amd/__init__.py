@@ -23,6 +23,8 @@ Entry points (same names as the C ABI):
 * ``kv_cache_write(k_cache, v_cache, k_new, v_new, pos)``
 * ``attn_bwd(q, k, v, o, dout, lse, *, causal, ...)`` -> (dq, dk, dv), the
   backward of attn_fwd (GQA gradients summed over each group)
+* ``attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, ...)``
+  -> (dq, dk, dv), the backward of attn_fwd_varlen
 * ``attn_decode_paged(q, k_pages, v_pages, block_table, cache_lens, ...)`` and
   ``kv_cache_write_paged(k_pages, v_pages, k_new, v_new, block_table, pos)``
   (a paged KV cache addressed through a device block table)
@@ -32,6 +34,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     Status,
     attn_bwd,
+    attn_bwd_varlen,
     attn_decode,
     attn_decode_paged,
     attn_decode_varlen,
@@ -50,6 +53,7 @@ __all__ = [
     "Status",
     "attn_fwd",
     "attn_bwd",
+    "attn_bwd_varlen",
     "attn_fwd_varlen",
     "attn_decode",
     "attn_decode_varlen",

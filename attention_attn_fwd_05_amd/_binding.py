@@ -94,6 +94,12 @@ def load_library():
     lib.attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, S, S,
                                     S, S, f32, Mask, i32, vp, ctypes.c_size_t, vp]
     lib.attn_bwd_masked.restype = i32
+    lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    i32, S, S, S, S, S, S, S, S, f32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd_varlen.restype = i32
+    lib.attn_bwd_varlen_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           i32, i32, S, S, S, S, S, S, S, S, f32, Mask, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd_varlen_masked.restype = i32
     lib.kv_cache_write.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, i32, vp]
     lib.kv_cache_write.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -518,3 +524,63 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         _check(lib.attn_bwd(*args, _CAUSAL_ALIGN[causal_align] if causal else 0, *tail), "attn_bwd")
     return dq, dk, dv
 
+
+def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+                    lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                    max_seqlen_q: int | None = None, max_seqlen_k: int | None = None, *, causal: bool,
+                    scale: float | None = None, causal_align: str = "top_left", dq: torch.Tensor | None = None,
+                    dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, window=None):
+    """Gradients (dq, dk, dv) of attn_fwd_varlen's output over packed sequences.
+
+    q, o, dout (total_q, Hq, D); k, v (total_k, Hkv, D); lse fp32 (Hq, total_q)
+    from attn_fwd_varlen with the same offsets, mask, scale and max_seqlen_q.
+    ``max_seqlen_k`` bounds every sequence's key count; either bound, when
+    None, is read from its offsets (a device-to-host copy).
+    """
+    if causal_align not in _CAUSAL_ALIGN:
+        raise ValueError("causal_align must be 'top_left' or 'bottom_right'")
+    lib = load_library()
+    Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or k.shape[2] != D:
+        raise ValueError("shape mismatch between q, k, v, o and dout")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors")
+    if cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    if lse.shape != (Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape (Hq, total_q)")
+    B = cu_seqlens_q.shape[0] - 1
+
+    def _bound(cu):
+        return max(int((cu[1:] - cu[:-1]).max().item()) if B > 0 else 0, 1)
+
+    max_seqlen_q = _bound(cu_seqlens_q) if max_seqlen_q is None else int(max_seqlen_q)
+    max_seqlen_k = _bound(cu_seqlens_k) if max_seqlen_k is None else int(max_seqlen_k)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient buffers must have the shapes of q, k, v")
+    if workspace is None:
+        n = int(lib.attn_bwd_workspace_bytes(1, Hq, Tq))
+        if n == 0:
+            raise ValueError("invalid sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _on_gpu(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, workspace)
+    code = _dtype_code(q, k, v, o, dout, dq, dk, dv)
+    s = _default_scale(D) if scale is None else float(scale)
+    P = _strides_packed
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+            B, max_seqlen_q, max_seqlen_k, Tq, Tk, Hq, Hkv, D,
+            P(q), P(k), P(v), P(o), P(dout), P(dq), P(dk), P(dv), s)
+    tail = (code, workspace.data_ptr(), workspace.numel(), _stream(q))
+    if window is not None:
+        _check(lib.attn_bwd_varlen_masked(*args, _mask(causal, causal_align, window), *tail),
+               "attn_bwd_varlen_masked")
+    else:
+        _check(lib.attn_bwd_varlen(*args, _CAUSAL_ALIGN[causal_align] if causal else 0, *tail), "attn_bwd_varlen")
+    return dq, dk, dv

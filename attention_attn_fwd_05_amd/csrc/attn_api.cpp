@@ -532,6 +532,106 @@ static attn_status bwd_impl(const void* q, const void* k, const void* v, const v
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+static attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k,
+                                   int total_q, int total_k, int Hq, int Hkv, int D, attn_strides sq,
+                                   attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
+                                   attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale, MaskSpec mk,
+                                   attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+    return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 || total_q <= 0 || total_k < 0 ||
+      D <= 0)
+    return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
+  // packed (token, head, dim) views: the batch stride is unused and not checked
+  for (attn_strides* st : {&sq, &sk, &sv, &so, &sdo, &sdq, &sdk, &sdv}) {
+    st->b = 0;
+    if (!strides_ok(*st) || st->n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
+  }
+  for (const void* p : {q, k, v, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv)})
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(1, Hq, total_q);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  const int64_t nqb = ((int64_t)max_seqlen_q + 255) / 256;
+  const int64_t nkb = ((int64_t)max_seqlen_k + 127) / 128;
+  const int64_t dq_blocks = nqb * Hq * B, dkv_blocks = nkb * Hkv * B;
+  if (dq_blocks > INT_MAX || dkv_blocks > INT_MAX || (int64_t)Hq * total_q > INT_MAX) return ATTN_ERR_SHAPE;
+
+  attn::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.ld = static_cast<float*>(workspace);
+  a.sqh = sq.h; a.sqn = sq.n;
+  a.skh = sk.h; a.skn = sk.n;
+  a.svh = sv.h; a.svn = sv.n;
+  a.soh = so.h; a.son = so.n;
+  a.sdoh = sdo.h; a.sdon = sdo.n;
+  a.sdqh = sdq.h; a.sdqn = sdq.n;
+  a.sdkh = sdk.h; a.sdkn = sdk.n;
+  a.sdvh = sdv.h; a.sdvn = sdv.n;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.group = Hq / Hkv;
+  a.Nq = max_seqlen_q;   // per-sequence rows are capped at these bounds
+  a.Nkv = max_seqlen_k;
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  a.dq_blocks = (unsigned)dq_blocks;
+  a.dkv_blocks = (unsigned)dkv_blocks;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.causal_br = mk.bottom_right;
+  a.mask = mk.mode;
+  a.win_left = mk.left;
+  a.win_right = mk.right;
+  a.bf16 = dtype == ATTN_BF16;
+  a.c = scale * kLog2e;
+  a.scale = scale;
+  const hipError_t e = attn::launch_bwd(a, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k, int total_q,
+                            int total_k, int Hq, int Hkv, int D, attn_strides sq, attn_strides sk, attn_strides sv,
+                            attn_strides so, attn_strides sdo, attn_strides sdq, attn_strides sdk, attn_strides sdv,
+                            float scale, int causal, attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return bwd_varlen_impl(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q,
+                         max_seqlen_k, total_q, total_k, Hq, Hkv, D, sq, sk, sv, so, sdo, sdq, sdk, sdv, scale,
+                         mask_of_causal(causal), dtype, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_bwd_varlen_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k,
+                                   int total_q, int total_k, int Hq, int Hkv, int D, attn_strides sq,
+                                   attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
+                                   attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale,
+                                   attn_mask mask, attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return bwd_varlen_impl(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q,
+                         max_seqlen_k, total_q, total_k, Hq, Hkv, D, sq, sk, sv, so, sdo, sdq, sdk, sdv, scale,
+                         mask_of(mask), dtype, workspace, workspace_bytes, stream);
+}
+
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                      attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,

@@ -144,7 +144,7 @@ constexpr int kOpen = 1 << 30;
 
 // ---- dQ: one workgroup per (batch, q head, 256 query rows).  MASK 0: none;
 //      1: causal (j <= i + off); 2: band i + off - win_left <= j <= i + off + win_right
-template <int D, bool BF16, int MASK>
+template <int D, bool BF16, int MASK, bool VARLEN>
 __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   constexpr bool CAUSAL = MASK == 1, BAND = MASK == 2;
   using L = DqLds<D>;
@@ -170,13 +170,40 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   const int q0 = qb * kDqRows;
   const int qrow = q0 + 32 * w + n;
 
+  // ---- this (sequence, head): row counts, first elements, valid bytes.  A
+  //      packed sequence's offsets are clamped into the packed tensors; its
+  //      query rows are capped at the max_seqlen_q bound (a.Nq)
+  int Nq = a.Nq, Nkv = a.Nkv;
+  int off = MASK != 0 ? a.causal_off : 0;
+  int64_t t0 = 0, s0 = 0;
+  int64_t q_bytes = a.q_bytes, do_bytes = a.do_bytes, k_bytes = a.k_bytes, v_bytes = a.v_bytes;
+  if constexpr (VARLEN) {
+    t0 = min(max(a.cu_q[b], 0), a.total_q);
+    const int t1 = min(max(a.cu_q[b + 1], (int)t0), a.total_q);
+    s0 = min(max(a.cu_k[b], 0), a.total_k);
+    const int s1 = min(max(a.cu_k[b + 1], (int)s0), a.total_k);
+    Nq = t1 - (int)t0;
+    Nkv = s1 - (int)s0;
+    if (MASK != 0) off = a.causal_br ? Nkv - Nq : 0;  // from the sequence's own lengths
+    Nq = min(Nq, a.Nq);
+    if (q0 >= Nq) return;  // whole workgroup
+    q_bytes = ((int64_t)(Nq - 1) * a.sqn + D) * 2;
+    do_bytes = ((int64_t)(Nq - 1) * a.sdon + D) * 2;
+    k_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.skn + D) * 2 : 0;
+    v_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.svn + D) * 2 : 0;
+  }
+  const int64_t bq = VARLEN ? t0 : 0, bk = VARLEN ? s0 : 0;  // packed: first row of the sequence
+  const uint16_t* qbase = a.q + (VARLEN ? bq * a.sqn : (int64_t)b * a.sqb) + (int64_t)h * a.sqh;
+  const uint16_t* gbase = a.dout + (VARLEN ? bq * a.sdon : (int64_t)b * a.sdob) + (int64_t)h * a.sdoh;
+  const float2* ldrow = reinterpret_cast<const float2*>(a.ld) +
+                        (VARLEN ? (int64_t)h * a.total_q + bq : ((int64_t)b * a.Hq + h) * a.Nq);
+
   // stationary B operands: Q and dO rows (zeros past Nq); lse2 and delta
   u32x4 qf[KS], gf[KS];
   {
     const int64_t qo = (int64_t)q0 * a.sqn, go = (int64_t)q0 * a.sdon;
-    const auto rq = make_rsrc(a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh + qo, clamp_bytes(a.q_bytes - 2 * qo));
-    const auto rg = make_rsrc(a.dout + (int64_t)b * a.sdob + (int64_t)h * a.sdoh + go,
-                              clamp_bytes(a.do_bytes - 2 * go));
+    const auto rq = make_rsrc(qbase + qo, clamp_bytes(q_bytes - 2 * qo));
+    const auto rg = make_rsrc(gbase + go, clamp_bytes(do_bytes - 2 * go));
     const int32_t oq = (32 * w + n) * (int32_t)a.sqn * 2 + 16 * hh;
     const int32_t og = (32 * w + n) * (int32_t)a.sdon * 2 + 16 * hh;
 #pragma unroll
@@ -186,25 +213,24 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
   }
   float lse2 = 0.f, delta = 0.f;
-  if (qrow < a.Nq) {
-    const float2 ld = reinterpret_cast<const float2*>(a.ld)[((int64_t)b * a.Hq + h) * a.Nq + qrow];
+  if (qrow < Nq) {
+    const float2 ld = ldrow[qrow];
     lse2 = ld.x;
     delta = ld.y;
   }
 
-  const uint16_t* kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
-  const uint16_t* vbase = a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh;
-  const int off = MASK != 0 ? a.causal_off : 0;
+  const uint16_t* kbase = a.k + (VARLEN ? bk * a.skn : (int64_t)b * a.skb) + (int64_t)kvh * a.skh;
+  const uint16_t* vbase = a.v + (VARLEN ? bk * a.svn : (int64_t)b * a.svb) + (int64_t)kvh * a.svh;
   const int WL = BAND ? (a.win_left < 0 ? kOpen : a.win_left) : 0;
   const int WR = BAND ? (a.win_right < 0 ? kOpen : a.win_right) : 0;
   // keys this block's rows see: up to the diagonal (causal), within the band
-  const int kv_end = CAUSAL ? max(0, min(a.Nkv, q0 + kDqRows + off))
-                            : (BAND ? max(0, min(a.Nkv, q0 + kDqRows + off + WR)) : a.Nkv);
+  const int kv_end = CAUSAL ? max(0, min(Nkv, q0 + kDqRows + off))
+                            : (BAND ? max(0, min(Nkv, q0 + kDqRows + off + WR)) : Nkv);
   const int ntiles = (kv_end + kBT - 1) / kBT;
   const int t_begin = BAND ? min(max(0, q0 + off - WL) / kBT, ntiles) : 0;
   // tiles every row sees in full: [full_lo, n_full)
-  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, a.Nkv)) / kBT
-                            : (BAND ? max(0, min(a.Nkv, q0 + off + WR + 1)) / kBT : a.Nkv / kBT);
+  const int n_full = CAUSAL ? max(0, min(q0 + off + 1, Nkv)) / kBT
+                            : (BAND ? max(0, min(Nkv, q0 + off + WR + 1)) / kBT : Nkv / kBT);
   const int full_lo = BAND ? (max(0, q0 + kDqRows - 1 + off - WL) + kBT - 1) / kBT : 0;
 
   // DMA geometry (as the forward): wave w fills 1 KiB blocks NB w .. NB w + NB - 1
@@ -220,8 +246,8 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   const uint32_t lds_v = lds_addr(smem + L::V0) + 1024 * NB * w;
   auto dma_tile = [&](int t, int stage) __attribute__((always_inline)) {
     const int64_t ko = (int64_t)t * kBT * a.skn, vo = (int64_t)t * kBT * a.svn;
-    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(a.k_bytes - 2 * ko));
-    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(a.v_bytes - 2 * vo));
+    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(k_bytes - 2 * ko));
+    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(v_bytes - 2 * vo));
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma16(rk, lds_k + 2 * stage * L::TILE + 1024 * i, dk[i]);
 #pragma unroll
@@ -244,9 +270,9 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
     const int kb = t * kBT;
     bool act1 = true;
     if (masked) {
-      if (kb >= a.Nkv || (CAUSAL && kb > wq_hi)) return;
+      if (kb >= Nkv || (CAUSAL && kb > wq_hi)) return;
       if (BAND && (kb > wq_hi + WR || kb + kBT - 1 < wq_lo - WL)) return;  // outside this wave's band
-      act1 = kb + 32 < a.Nkv && (!CAUSAL || kb + 32 <= wq_hi) && (!BAND || kb + 32 <= wq_hi + WR);
+      act1 = kb + 32 < Nkv && (!CAUSAL || kb + 32 <= wq_hi) && (!BAND || kb + 32 <= wq_hi + WR);
     }
     // per 32-key subtile u: S^T = K Q^T, dP^T = V dO^T, then dS^T = P^T (dP^T -
     // delta) with P^T = exp2(S^T c - lse2); element e of lane (n, hh) is key
@@ -267,7 +293,7 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
         float pv = fast_exp2(__builtin_fmaf(sx[e], c, -lse2));
         if (masked) {
           const int key = kb + 32 * u + 8 * (e >> 2) + 4 * hh + (e & 3);
-          pv = (key < a.Nkv && (!CAUSAL || key <= qrow + off) &&
+          pv = (key < Nkv && (!CAUSAL || key <= qrow + off) &&
                 (!BAND || (key >= qrow + off - WL && key <= qrow + off + WR))) ? pv : 0.f;
         }
         sx[e] = pv * (px[e] - delta);
@@ -313,8 +339,8 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   }
 
   // ---- dQ = scale (dQ^T)^T, cast, store
-  if (qrow < a.Nq) {
-    uint16_t* op = a.dq + (int64_t)b * a.sdqb + (int64_t)h * a.sdqh + (int64_t)qrow * a.sdqn;
+  if (qrow < Nq) {
+    uint16_t* op = a.dq + (VARLEN ? bq * a.sdqn : (int64_t)b * a.sdqb) + (int64_t)h * a.sdqh + (int64_t)qrow * a.sdqn;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -333,7 +359,7 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
 //      dV through LDS at the end.  The block's K and V rows sit in LDS (B
 //      operands read with plain 16-byte reads), so only the two accumulators
 //      are register-resident and two waves fit on each SIMD.
-template <int D, bool BF16, int MASK>
+template <int D, bool BF16, int MASK, bool VARLEN>
 __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr bool CAUSAL = MASK == 1, BAND = MASK == 2;
   using L = DkvLds<D>;
@@ -362,14 +388,37 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   const int k0 = kbk * kKvRows;
   const int key = k0 + 32 * kg + n;
 
+  // ---- this (sequence, kv head): row counts, first rows, valid bytes (as in
+  //      the dQ pass; a.Nq, a.Nkv are the max_seqlen bounds when packed)
+  int Nq = a.Nq, Nkv = a.Nkv;
+  int off = MASK != 0 ? a.causal_off : 0;
+  int64_t bq = 0, bk = 0;
+  int64_t q_bytes = a.q_bytes, do_bytes = a.do_bytes, k_bytes = a.k_bytes, v_bytes = a.v_bytes;
+  if constexpr (VARLEN) {
+    bq = min(max(a.cu_q[b], 0), a.total_q);
+    const int t1 = min(max(a.cu_q[b + 1], (int)bq), a.total_q);
+    bk = min(max(a.cu_k[b], 0), a.total_k);
+    const int s1 = min(max(a.cu_k[b + 1], (int)bk), a.total_k);
+    Nq = t1 - (int)bq;
+    Nkv = s1 - (int)bk;
+    if (MASK != 0) off = a.causal_br ? Nkv - Nq : 0;
+    Nq = min(Nq, a.Nq);
+    if (k0 >= Nkv) return;  // whole workgroup: block past this sequence's keys
+    q_bytes = Nq > 0 ? ((int64_t)(Nq - 1) * a.sqn + D) * 2 : 0;
+    do_bytes = Nq > 0 ? ((int64_t)(Nq - 1) * a.sdon + D) * 2 : 0;
+    k_bytes = ((int64_t)(Nkv - 1) * a.skn + D) * 2;
+    v_bytes = ((int64_t)(Nkv - 1) * a.svn + D) * 2;
+  }
+  const uint16_t* kbase = a.k + (VARLEN ? bk * a.skn : (int64_t)b * a.skb) + (int64_t)kvh * a.skh;
+  const uint16_t* vbase = a.v + (VARLEN ? bk * a.svn : (int64_t)b * a.svb) + (int64_t)kvh * a.svh;
+
   // query tiles that see some key of the block, for every q head of the
   // group: query i sees key j iff j <= i + off (causal), iff i + off - WL <=
   // j <= i + off + WR (band); tiles in [full_lo, full_hi) see every key of it
-  const int off = MASK != 0 ? a.causal_off : 0;
   const int WL = BAND ? (a.win_left < 0 ? kOpen : a.win_left) : 0;
   const int WR = BAND ? (a.win_right < 0 ? kOpen : a.win_right) : 0;
-  const int ntq0 = (a.Nq + kBT - 1) / kBT;
-  const int ntq = BAND ? min(ntq0, (max(0, min(a.Nq, k0 + kKvRows - off + WL)) + kBT - 1) / kBT) : ntq0;
+  const int ntq0 = (Nq + kBT - 1) / kBT;
+  const int ntq = BAND ? min(ntq0, (max(0, min(Nq, k0 + kKvRows - off + WL)) + kBT - 1) / kBT) : ntq0;
   const int tq0 = CAUSAL ? min(max(0, k0 - off) / kBT, ntq)
                          : (BAND ? min(max(0, k0 - off - WR) / kBT, ntq) : 0);
   const int full_lo = CAUSAL ? min(ntq, (max(0, k0 + kKvRows - 1 - off) + kBT - 1) / kBT)
@@ -393,8 +442,8 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     dma_rows(ok, a.skn);
     dma_rows(ov, a.svn);
     const int64_t ko = (int64_t)k0 * a.skn, vo = (int64_t)k0 * a.svn;
-    const i32x4 rk = rsrc_words(a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh + ko, clamp_bytes(a.k_bytes - 2 * ko));
-    const i32x4 rv = rsrc_words(a.v + (int64_t)b * a.svb + (int64_t)kvh * a.svh + vo, clamp_bytes(a.v_bytes - 2 * vo));
+    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(k_bytes - 2 * ko));
+    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(v_bytes - 2 * vo));
 #pragma unroll
     for (int i = 0; i < NBK; ++i) dma16(rk, lds_addr(smem + L::K0) + 1024 * (NBK * w + i), ok[i]);
 #pragma unroll
@@ -411,17 +460,20 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   constexpr int LDW = kBT * 8 / kKvW;  // (lse2, delta) bytes per wave per tile
   const uint32_t lds_q = lds_addr(smem + L::Q0) + 1024 * NB * w;
   const uint32_t lds_ld = lds_addr(smem + L::LD0) + LDW * w;
-  const float* ldb = a.ld + 2 * ((int64_t)b * a.Hq) * a.Nq;
+  // (lse2, delta) row 0 of q head h: (b, h) of (B, Hq, Nq), packed (h, bq) of (Hq, total_q)
+  auto ld_row0 = [&](int h) __attribute__((always_inline)) {
+    return a.ld + 2 * (VARLEN ? (int64_t)h * a.total_q + bq : ((int64_t)b * a.Hq + h) * a.Nq);
+  };
   auto dma_tile = [&](int it, int stage) __attribute__((always_inline)) {
     const int hgi = it / nt;
     const int t = tq0 + (it - hgi * nt);
     const int h = kvh * a.group + hgi;
     const int64_t qo = (int64_t)t * kBT * a.sqn, go = (int64_t)t * kBT * a.sdon;
-    const i32x4 rq = rsrc_words(a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh + qo, clamp_bytes(a.q_bytes - 2 * qo));
-    const i32x4 rg = rsrc_words(a.dout + (int64_t)b * a.sdob + (int64_t)h * a.sdoh + go,
-                                clamp_bytes(a.do_bytes - 2 * go));
-    const int64_t lo = ((int64_t)h * a.Nq + (int64_t)t * kBT) * 2;
-    const i32x4 rl = rsrc_words(ldb + lo, clamp_bytes(((int64_t)a.Nq - (int64_t)t * kBT) * 8));
+    const i32x4 rq = rsrc_words(a.q + (VARLEN ? bq * a.sqn : (int64_t)b * a.sqb) + (int64_t)h * a.sqh + qo,
+                                clamp_bytes(q_bytes - 2 * qo));
+    const i32x4 rg = rsrc_words(a.dout + (VARLEN ? bq * a.sdon : (int64_t)b * a.sdob) + (int64_t)h * a.sdoh + go,
+                                clamp_bytes(do_bytes - 2 * go));
+    const i32x4 rl = rsrc_words(ld_row0(h) + (int64_t)t * kBT * 2, clamp_bytes(((int64_t)Nq - (int64_t)t * kBT) * 8));
     const uint32_t sq = lds_q + stage * 2 * L::TILE * 2;
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma16(rq, sq + 1024 * i, dq_[i]);
@@ -527,7 +579,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
       }
   }
   __syncthreads();
-  if (qh == 1 || key >= a.Nkv) return;
+  if (qh == 1 || key >= Nkv) return;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -535,8 +587,8 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
       adv[dt][e] += red[(((kg * 2 + 0) * DT + dt) * 16 + e) * 64 + lane];
       adk[dt][e] += red[(((kg * 2 + 1) * DT + dt) * 16 + e) * 64 + lane];
     }
-  uint16_t* vp = a.dv + (int64_t)b * a.sdvb + (int64_t)kvh * a.sdvh + (int64_t)key * a.sdvn;
-  uint16_t* kp = a.dk + (int64_t)b * a.sdkb + (int64_t)kvh * a.sdkh + (int64_t)key * a.sdkn;
+  uint16_t* vp = a.dv + (VARLEN ? bk * a.sdvn : (int64_t)b * a.sdvb) + (int64_t)kvh * a.sdvh + (int64_t)key * a.sdvn;
+  uint16_t* kp = a.dk + (VARLEN ? bk * a.sdkn : (int64_t)b * a.sdkb) + (int64_t)kvh * a.sdkh + (int64_t)key * a.sdkn;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -550,20 +602,32 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     }
 }
 
-template <int D, bool BF16, int MASK>
+template <int D, bool BF16, int MASK, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  // the row pass sees a packed batch as one sequence of total_q rows
+  BwdArgs p = a;
+  if (VARLEN) {
+    p.B = 1;
+    p.Nq = a.total_q;
+    p.sob = p.sdob = 0;
+  }
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
   const int64_t prep_blocks = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
-  hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, MASK>), dim3(a.dq_blocks), dim3(64 * kDqW), 0, stream, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, MASK>), dim3(a.dkv_blocks), dim3(64 * kKvW), 0, stream, a);
+  hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, MASK, VARLEN>), dim3(a.dq_blocks), dim3(64 * kDqW), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, MASK, VARLEN>), dim3(a.dkv_blocks), dim3(64 * kKvW), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, bool BF16, bool VARLEN>
+hipError_t launch_bwd_v(const BwdArgs& a, hipStream_t stream) {
+  if (a.mask == 2) return launch_bwd_t<D, BF16, 2, VARLEN>(a, stream);
+  return a.mask == 1 ? launch_bwd_t<D, BF16, 1, VARLEN>(a, stream) : launch_bwd_t<D, BF16, 0, VARLEN>(a, stream);
 }
 
 template <int D, bool BF16>
 hipError_t launch_bwd_m(const BwdArgs& a, hipStream_t stream) {
-  if (a.mask == 2) return launch_bwd_t<D, BF16, 2>(a, stream);
-  return a.mask == 1 ? launch_bwd_t<D, BF16, 1>(a, stream) : launch_bwd_t<D, BF16, 0>(a, stream);
+  return a.cu_q ? launch_bwd_v<D, BF16, true>(a, stream) : launch_bwd_v<D, BF16, false>(a, stream);
 }
 
 template <int D>

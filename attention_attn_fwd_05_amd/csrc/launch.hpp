@@ -116,6 +116,14 @@ struct BwdArgs {
   int B, Hq, Hkv, Nq, Nkv, group;
   int nqb, nkb;                // query blocks (dq), key blocks (dkdv) per (batch, head)
   unsigned dq_blocks, dkv_blocks;
+  // packed variable-length batches (null otherwise): sequence b owns query rows
+  // [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]); B is then the
+  // number of sequences, Nq / Nkv the max_seqlen bounds, and lse and the
+  // workspace rows are (Hq, total_q)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
+  int causal_br;               // packed: causal offset per sequence, 1 = L_k - L_q
   int mask;                    // 0 none, 1 causal, 2 band
   int causal_off;              // query i sits at key position i + causal_off
   int win_left, win_right;     // band bounds around that position (-1: open)

@@ -216,6 +216,36 @@ attn_status attn_bwd_masked(const void* q, const void* k, const void* v, const v
                             attn_mask mask, attn_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_varlen, attn_bwd_varlen_masked -- the backward of attn_fwd_varlen
+ * (attn_fwd_varlen_masked): attn_bwd on each packed sequence's own rows; no
+ * gradient crosses sequences.  Layouts, offsets (clamped on the device) and
+ * the per-sequence mask as the packed forward: q, o, dout, dq (total_q, Hq, D),
+ * k, v, dk, dv (total_k, Hkv, D) via strides (b unused); lse contiguous fp32
+ * (Hq, total_q) as attn_fwd_varlen returns it.  max_seqlen_q, max_seqlen_k:
+ * host bounds on every sequence's query and key rows (they size the grids);
+ * query rows past max_seqlen_q, which the forward does not compute, are
+ * ignored here too (no dq written, no contribution to dk, dv); max_seqlen_k
+ * must bound every key count (dk, dv rows past it are not written).  dq rows of a
+ * sequence with no keys and dk, dv rows of one with no queries are written as
+ * 0.  workspace: attn_bwd_workspace_bytes(1, Hq, total_q) bytes.
+ */
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k, int total_q,
+                            int total_k, int Hq, int Hkv, int D, attn_strides sq, attn_strides sk, attn_strides sv,
+                            attn_strides so, attn_strides sdo, attn_strides sdq, attn_strides sdk, attn_strides sdv,
+                            float scale, int causal, attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+attn_status attn_bwd_varlen_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k,
+                                   int total_q, int total_k, int Hq, int Hkv, int D, attn_strides sq,
+                                   attn_strides sk, attn_strides sv, attn_strides so, attn_strides sdo,
+                                   attn_strides sdq, attn_strides sdk, attn_strides sdv, float scale,
+                                   attn_mask mask, attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * attn_decode_workspace_bytes -- size of the scratch buffer attn_decode needs
  * for a cache of S_max slots (covers every cache_len <= S_max and every split
  * count): U * min(64, ceil(S_max/128)) * ceil(G/ceil(G/16)) * (D + 4) * 4

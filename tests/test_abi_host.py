@@ -44,8 +44,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_varlen_masked", "attn_decode",
                           "attn_decode_varlen", "attn_decode_paged", "attn_decode_ex", "attn_decode_workspace_bytes",
-                          "kv_cache_write", "kv_cache_write_paged", "attn_bwd", "attn_bwd_masked", "attn_bwd_workspace_bytes",
-                          "attn_status_string"}
+                          "kv_cache_write", "kv_cache_write_paged", "attn_bwd", "attn_bwd_masked", "attn_bwd_varlen",
+                          "attn_bwd_varlen_masked", "attn_bwd_workspace_bytes", "attn_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -157,6 +157,40 @@ def test_bwd_rejects(lib, kw, code):
 def test_bwd_workspace_bytes(lib):
     assert lib.attn_bwd_workspace_bytes(2, 32, 8192) == 2 * 32 * 8192 * 8
     assert lib.attn_bwd_workspace_bytes(0, 1, 1) == 0
+
+
+def bwdv(lib, mask=None, **kw):
+    Hq, Hkv, D = 8, 2, 128
+    pk = lambda H: S(0, D, H * D, 1)  # packed (token, head, dim)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cq=FAKE, ck=FAKE, B=3,
+             msq=300, msk=400, tq=700, tk=900, Hq=Hq, Hkv=Hkv, D=D, sq=pk(Hq), sk=pk(Hkv), sv=pk(Hkv), so=pk(Hq),
+             sdo=pk(Hq), sdq=pk(Hq), sdk=pk(Hkv), sdv=pk(Hkv), scale=0.088, causal=2, dtype=0, ws=FAKE,
+             ws_bytes=lib.attn_bwd_workspace_bytes(1, Hq, 700), stream=None)
+    a.update(kw)
+    head = (a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["cq"], a["ck"], a["B"],
+            a["msq"], a["msk"], a["tq"], a["tk"], a["Hq"], a["Hkv"], a["D"], a["sq"], a["sk"], a["sv"], a["so"],
+            a["sdo"], a["sdq"], a["sdk"], a["sdv"], a["scale"])
+    tail = (a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+    if mask is not None:
+        return lib.attn_bwd_varlen_masked(*head, bd.Mask(*mask), *tail)
+    return lib.attn_bwd_varlen(*head, a["causal"], *tail)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), NULL), (dict(lse=None), NULL), (dict(dv=None), NULL), (dict(cq=None), NULL),
+    (dict(ck=None), NULL), (dict(B=0), SHAPE), (dict(msq=0), SHAPE), (dict(msk=0), SHAPE), (dict(tq=0), SHAPE),
+    (dict(tk=-1), SHAPE), (dict(Hq=7), SHAPE), (dict(D=96), UNSUP), (dict(causal=3), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(scale=float("nan")), UNSUP), (dict(cq=FAKE + 2), UNSUP), (dict(lse=FAKE + 1), UNSUP),
+    (dict(dk=FAKE + 8), UNSUP), (dict(sdq=S(0, 128, 1024, 2)), UNSUP), (dict(sv=S(0, 128, 1 << 23, 1)), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=700 * 8 * 8 - 1), WS),
+])
+def test_bwd_varlen_rejects(lib, kw, code):
+    assert bwdv(lib, **kw) == code
+
+
+@pytest.mark.parametrize("mask,code", [((2, -1, 0), UNSUP), ((0, -2, 0), UNSUP), ((1, 5, -3), UNSUP)])
+def test_bwd_varlen_masked_rejects(lib, mask, code):
+    assert bwdv(lib, mask=mask) == code
 
 
 def fwdv(lib, **kw):
