@@ -48,7 +48,11 @@ namespace {
 
 constexpr int kWaves = 8;            // waves per workgroup (32 query rows each)
 constexpr int kBM = 32 * kWaves;     // query rows per workgroup
-constexpr int kStages = 3;           // LDS ring depth (tiles in flight + 1)
+#ifndef ATTN_PF_STAGES
+#define ATTN_PF_STAGES 4
+#endif
+constexpr int kStages = ATTN_PF_STAGES;  // LDS ring depth (tiles in flight + 1)
+static_assert(kStages == 3 || kStages == 4, "the KV loop cycles three or four stages");
 constexpr int kBN = 64;              // key rows per LDS tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 #ifndef ATTN_PF_SCHED
@@ -299,6 +303,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
       }
       schedule_scores();
     }
+
     if constexpr (MASKED) {
       // mask before the row max
 #pragma unroll
@@ -367,59 +372,66 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   using st0 = std::integral_constant<int, 0>;
   using st1 = std::integral_constant<int, 1>;
   using st2 = std::integral_constant<int, 2>;
-  static_assert(kStages == 3, "the loop below cycles three stages");
+  using st3 = std::integral_constant<int, 3>;
 
-  // ---- KV loop over a 3-stage LDS ring filled by DMA: the loads of tile t+2
-  //      are issued before tile t is computed, so every tile's loads have two
-  //      tile computations to land.  After computing tile t a wave waits until
-  //      only its tile-(t+2) loads are outstanding (tile t+1 is in LDS), and
-  //      the barrier publishes it to the workgroup.  Full tiles go in triples
-  //      (stages 0, 1, 2); the rest (diagonal / key tail) take the masked path.
+  // ---- KV loop over a kStages-deep LDS ring filled by DMA: the loads of tile
+  //      t + kStages - 1 are issued before tile t is computed, so every tile's
+  //      loads have kStages - 1 tile computations to land.  After computing
+  //      tile t a wave waits until only the loads of tiles past t+1 are
+  //      outstanding (tile t+1 is in LDS), and the barrier publishes it to the
+  //      workgroup; the stage refilled next was last read before that barrier.
+  //      Full tiles go in groups of kStages (stages 0 .. kStages-1); the rest
+  //      (diagonal / key tail) take the masked path.
   constexpr int NDMA = 2 * NB;  // DMA instructions per wave per tile
-  // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, expcnt and
-  // lgkmcnt left at their maxima, i.e. unconstrained)
-  constexpr int kWaitAllButTile = 0x0F70 | NDMA;
-  constexpr int kWaitAll = 0x0F70;
-  static_assert(NDMA < 16, "vmcnt field");
+  static_assert((kStages - 2) * NDMA < 16, "vmcnt field");
+  // wait until tile tt+1 has landed: the tiles issued after it are
+  // min(kStages - 2, ntiles - tt - 2) (s_waitcnt immediates, gfx9 encoding:
+  // vmcnt in bits 3:0, expcnt and lgkmcnt left at their maxima)
+  auto wait_next = [&](int tt) __attribute__((always_inline)) {
+    const int ahead = min(kStages - 2, max(0, ntiles - tt - 2));
+    if (kStages == 4 && ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (kStages == 4 ? 2 * NDMA : 0));
+    else if (ahead >= 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | NDMA);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
   auto step = [&](int tt, auto stage_tag, auto masked_tag) {
     constexpr int STG = decltype(stage_tag)::value;
-    const bool pre = tt + 2 < ntiles;
-    if (pre) dma_tile(tt + 2, (STG + 2) % 3);
+    if (tt + kStages - 1 < ntiles) dma_tile(tt + kStages - 1, (STG + kStages - 1) % kStages);
     compute(stage_tag, tt, masked_tag);
-    if (pre)
-      __builtin_amdgcn_s_waitcnt(kWaitAllButTile);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    wait_next(tt);
     barrier_nofence();
   };
-  // tile t sits in ring stage (t - t_begin) % 3
-  if (t_begin < ntiles) dma_tile(t_begin, 0);
-  if (t_begin + 1 < ntiles) dma_tile(t_begin + 1, 1);
-  if (t_begin + 1 < ntiles)
-    __builtin_amdgcn_s_waitcnt(kWaitAllButTile);
-  else
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
+  // tile t sits in ring stage (t - t_begin) % kStages
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (t_begin + i < ntiles) dma_tile(t_begin + i, i);
+  wait_next(t_begin - 1);
   barrier_nofence();
   int t = t_begin;
   auto masked_step = [&](int tt) __attribute__((always_inline)) {
-    const int r = (tt - t_begin) % 3;
+    const int r = (tt - t_begin) % kStages;
     if (r == 0)
       step(tt, st0{}, mask_t{});
     else if (r == 1)
       step(tt, st1{}, mask_t{});
-    else
+    else if (kStages == 3 || r == 2)
       step(tt, st2{}, mask_t{});
+    else if constexpr (kStages == 4)
+      step(tt, st3{}, mask_t{});
   };
   if constexpr (BAND) {
     // band: the masked tiles left of the full ones, and as many more as put
-    // the first full triple in stage 0
-    const int f_start = t_begin + 3 * ((max(full_lo - t_begin, 0) + 2) / 3);
+    // the first full group in stage 0
+    const int f_start = t_begin + kStages * ((max(full_lo - t_begin, 0) + kStages - 1) / kStages);
     for (; t < f_start && t < ntiles; ++t) masked_step(t);
   }
-  for (; t + 2 < n_full; t += 3) {
+  for (; t + kStages - 1 < n_full; t += kStages) {
     step(t, st0{}, full_t{});
     step(t + 1, st1{}, full_t{});
     step(t + 2, st2{}, full_t{});
+    if constexpr (kStages == 4) step(t + 3, st3{}, full_t{});
   }
   for (; t < ntiles; ++t) masked_step(t);
 
