@@ -288,6 +288,7 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
   sq3.n = 0;
   so3.n = 0;
   if (!strides_ok(sq3) || !strides_ok(skc) || !strides_ok(svc) || !strides_ok(so3)) return ATTN_ERR_UNSUPPORTED;
+  if (skc.n > kMaxRowStride || svc.n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
   if (lens && (reinterpret_cast<uintptr_t>(lens) & 3u)) return ATTN_ERR_UNSUPPORTED;

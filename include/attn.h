@@ -15,7 +15,11 @@
  *     "Kernel design rules": all strides are arguments, no contiguity assumed).
  *     The innermost (head-dim) stride must be 1, every other stride a multiple
  *     of 8 elements, and every base pointer 16-byte aligned: the kernels move
- *     rows in 16-byte vectors.  Violations return ATTN_ERR_UNSUPPORTED.
+ *     rows in 16-byte vectors.  Row (sequence / cache slot) strides are at
+ *     most 2^22 elements: a tile's rows are addressed with 32-bit offsets from
+ *     its first row (base and row offsets themselves are 64-bit, so tensors
+ *     and offsets beyond 2^31 bytes are fine).  Violations return
+ *     ATTN_ERR_UNSUPPORTED.
  *   - Element types: IEEE fp16 or bf16 for Q/K/V/O; scores, softmax state and
  *     accumulators are fp32 inside the kernels ([P1] "Kernel design rules").
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every

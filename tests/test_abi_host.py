@@ -236,6 +236,7 @@ def dec(lib, **kw):
     (dict(Hq=30), SHAPE), (dict(num_splits=-1), SHAPE),
     (dict(D=80), UNSUP), (dict(dtype=-1), UNSUP), (dict(scale=float("nan")), UNSUP),
     (dict(skc=S(8192 * 128 * 8, 8192 * 128, 128, 2)), UNSUP), (dict(vc=FAKE + 4), UNSUP),
+    (dict(skc=S(8192 * 128 * 8, 128, (1 << 22) + 8, 1)), UNSUP), (dict(svc=S(8192 * 128 * 8, 128, 1 << 23, 1)), UNSUP),
     (dict(ws=None), WS), (dict(ws_bytes=1024), WS), (dict(ws=FAKE + 8), WS),
 ])
 def test_decode_rejects(lib, kw, code):
@@ -282,6 +283,7 @@ def dpg(lib, **kw):
     (dict(Hq=30), SHAPE),
     (dict(ps=24), UNSUP), (dict(ps=8), UNSUP), (dict(ps=1 << 21), UNSUP), (dict(tbl=FAKE + 2), UNSUP),
     (dict(lens=FAKE + 1), UNSUP), (dict(D=96), UNSUP), (dict(skp=S(16 * 128 * 8, 16 * 128, 128, 2)), UNSUP),
+    (dict(svp=S(16 * 128 * 8, 128, (1 << 22) + 8, 1)), UNSUP),
     (dict(ws=None), WS), (dict(ws_bytes=4096), WS),
 ])
 def test_decode_paged_rejects(lib, kw, code):
