@@ -305,15 +305,26 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
     }
 
     if constexpr (MASKED) {
-      // mask before the row max
+      // mask before the row max.  Score register e of this lane holds key
+      // kb + 4 hh + c(e) of the first subtile, c(e) = 8 (e / 4) + e % 4 a
+      // compile-time offset, and c(e) + 32 of the second; the key is visible
+      // iff lo <= c <= hi for this lane's per-tile limits (64-bit, so open
+      // band sides cannot overflow), a compare against an immediate per
+      // register and no branches
+      const int64_t base = (int64_t)kb + 4 * hh, pos = (int64_t)qrow + off;
+      int64_t hi = (int64_t)Nkv - 1 - base;
+      if (CAUSAL) hi = min(hi, pos - base);
+      if (BAND) hi = min(hi, pos + WR - base);
+      const int64_t lo = BAND ? pos - WL - base : 0;
+      const int hi0 = (int)max(min(hi, (int64_t)64), (int64_t)-1);
+      const int lo0 = (int)max(min(lo, (int64_t)64), (int64_t)0);
+      const int hi1 = act1 ? hi0 - 32 : -1;
+      const int lo1 = lo0 - 32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int kv0 = kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const int kv1 = kv0 + 32;
-        const bool vis0 = kv0 < Nkv && (!CAUSAL || kv0 <= qrow + off) &&
-                          (!BAND || (kv0 >= qrow + off - WL && kv0 <= qrow + off + WR));
-        const bool vis1 = act1 && kv1 < Nkv && (!CAUSAL || kv1 <= qrow + off) &&
-                          (!BAND || (kv1 >= qrow + off - WL && kv1 <= qrow + off + WR));
+        const int c = 8 * (e >> 2) + (e & 3);
+        const bool vis0 = (c <= hi0) & (!BAND | (c >= lo0));
+        const bool vis1 = (c <= hi1) & (!BAND | (c >= lo1));
         s0[e] = vis0 ? s0[e] : -INFINITY;
         s1[e] = vis1 ? s1[e] : -INFINITY;
       }
