@@ -272,8 +272,7 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
       }
     }
     float mx = vmax(vmax(vmax(s0[0], s0[1]), vmax(s0[2], s0[3])), vmax(vmax(s1[0], s1[1]), vmax(s1[2], s1[3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    mx = max_xor32(max_xor16(mx)) * c;
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
@@ -313,8 +312,7 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   float* rm = red;       // [4][16]
   float* rl = red + 64;  // [4][16]
   float* ro = red + 128; // [4][16][D]
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = sum_xor32(sum_xor16(l));
   if (rg == 0) {
     rm[w * 16 + col] = m;
     rl[w * 16 + col] = l;

@@ -67,9 +67,30 @@ __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
                                   false);
 }
 
-// max / sum of x over lanes l and l ^ 32 (one ds_bpermute through the LDS crossbar).
-__device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+// max / sum of x over lanes l and l ^ 32 (l ^ 16) with v_permlane32_swap
+// (v_permlane16_swap), gfx950: with x as both operands the two results hold,
+// in every lane, the values of lanes l and l ^ 32 (l ^ 16), so combining them
+// is the exchange; VALU operations, where a shuffle would be an LDS round trip.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
 
 // Buffer resource over [base, base + bytes): 16-byte loads at byte offsets
 // >= bytes return zeros (hardware range check), so ragged tails need no branch.
