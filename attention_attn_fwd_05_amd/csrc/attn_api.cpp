@@ -15,6 +15,7 @@
 namespace {
 
 constexpr int kPrefillRows = 256;  // query rows per prefill workgroup
+constexpr int64_t kSmallGridBlocks = 128;  // 256-row grids this small use 128-row blocks (half the 256 CUs)
 constexpr int kDecodeTile = 128;   // cache rows per decode tile
 constexpr int kDecodeMaxHeads = 16;
 constexpr int kDecodeMaxSplits = 64;     // partials one combine merges
@@ -122,11 +123,16 @@ static attn_status fwd_impl(const void* q, const void* k, const void* v, void* o
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
   if (sq.n > kMaxRowStride || sk.n > kMaxRowStride || sv.n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
-  const int64_t nqb = ((int64_t)Nq + kPrefillRows - 1) / kPrefillRows;
+  // 256 query rows per workgroup (8 waves, two per SIMD), or 128 (4 waves,
+  // one per SIMD) when 256-row blocks would leave at least half the CUs idle
+  const int64_t nqb256 = ((int64_t)Nq + kPrefillRows - 1) / kPrefillRows;
+  const int rows = nqb256 * Hq * B <= kSmallGridBlocks ? kPrefillRows / 2 : kPrefillRows;
+  const int64_t nqb = ((int64_t)Nq + rows - 1) / rows;
   const int64_t nblocks = nqb * Hq * B;
   if (nblocks > INT_MAX) return ATTN_ERR_SHAPE;
 
   attn::FwdArgs a{};
+  a.rows = rows;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -218,6 +224,7 @@ static attn_status fwd_varlen_impl(const void* q, const void* k, const void* v, 
   a.soh = so.h; a.son = so.n;
   a.Hq = Hq; a.Hkv = Hkv; a.group = (int)group;
   a.Nq = max_seqlen_q;  // per-sequence query rows are capped at this bound
+  a.rows = kPrefillRows;
   a.nqb = (int)nqb;
   a.nblocks = (int)nblocks;
   a.cu_q = cu_seqlens_q;

@@ -46,8 +46,6 @@ namespace attn {
 
 namespace {
 
-constexpr int kWaves = 8;            // waves per workgroup (32 query rows each)
-constexpr int kBM = 32 * kWaves;     // query rows per workgroup
 #ifndef ATTN_PF_STAGES
 #define ATTN_PF_STAGES 4
 #endif
@@ -85,8 +83,12 @@ struct PrefillLds {
 
 // MASK 0: every key below Nkv; 1: causal (j <= i + off); 2: a band of keys
 // i + off - win_left <= j <= i + off + win_right (either side may be open)
-template <int D, bool BF16, int MASK, bool VARLEN>
-__global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdArgs a) {
+// WAVES = 8: 256 query rows per workgroup, two waves per SIMD; WAVES = 4: 128
+// rows, for grids too small to fill the chip with 256-row blocks
+template <int D, bool BF16, int MASK, bool VARLEN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArgs a) {
+  constexpr int kWaves = WAVES;       // waves per workgroup (32 query rows each)
+  constexpr int kBM = 32 * kWaves;    // query rows per workgroup
   constexpr bool CAUSAL = MASK == 1;
   constexpr bool BAND = MASK == 2;
   using L = PrefillLds<D>;
@@ -394,16 +396,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
   //      Full tiles go in groups of kStages (stages 0 .. kStages-1); the rest
   //      (diagonal / key tail) take the masked path.
   constexpr int NDMA = 2 * NB;  // DMA instructions per wave per tile
-  static_assert((kStages - 2) * NDMA < 16, "vmcnt field");
+  static_assert((kStages - 2) * NDMA < 64, "vmcnt field");
+  // s_waitcnt immediate for vmcnt <= vm (gfx9 encoding: vmcnt bits 3:0 and
+  // 15:14, expcnt and lgkmcnt left at their maxima, i.e. unconstrained)
+  constexpr int kVm1 = 0x0F70 | (NDMA & 15) | ((NDMA >> 4) << 14);
+  constexpr int kVm2 = 0x0F70 | ((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14);
   // wait until tile tt+1 has landed: the tiles issued after it are
-  // min(kStages - 2, ntiles - tt - 2) (s_waitcnt immediates, gfx9 encoding:
-  // vmcnt in bits 3:0, expcnt and lgkmcnt left at their maxima)
+  // min(kStages - 2, ntiles - tt - 2)
   auto wait_next = [&](int tt) __attribute__((always_inline)) {
     const int ahead = min(kStages - 2, max(0, ntiles - tt - 2));
     if (kStages == 4 && ahead >= 2)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (kStages == 4 ? 2 * NDMA : 0));
+      __builtin_amdgcn_s_waitcnt(kVm2);
     else if (ahead >= 1)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | NDMA);
+      __builtin_amdgcn_s_waitcnt(kVm1);
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);
   };
@@ -467,7 +472,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_fwd_kernel(const FwdAr
 
 template <int D, bool BF16, int MASK, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN>), dim3(a.nblocks), dim3(64 * kWaves), 0, stream, a);
+  if constexpr (!VARLEN) {
+    if (a.rows == 128) {
+      hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4>), dim3(a.nblocks), dim3(64 * 4), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 8>), dim3(a.nblocks), dim3(64 * 8), 0, stream, a);
   return hipGetLastError();
 }
 
