@@ -398,6 +398,54 @@ def main():
             "ms_per_launch": round(bt, 4), "tflops": round(bflops / (bt * 1e-3) / 1e12, 1),
             "frac_of_2500_tflops": round(bflops / (bt * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
         del bq, bk, bv, bdo, bo, blse, bdq, bdk, bdv, bws
+        # backward of the packed 16-sequence batch (as prefill_varlen)
+        vb = W.varlen_serving_case()
+        vq, vk, vv = (t.to(dev) for t in W.varlen_prefill_inputs(vb))
+        vdo = torch.randn(vq.shape, generator=torch.Generator().manual_seed(W.BASE_SEED + 61)).to(vq.dtype).to(dev)
+        vcq = torch.tensor(vb.cu_q, dtype=torch.int32, device=dev)
+        vo, vl = A.attn_fwd_varlen(vq, vk, vv, vcq, vcq, vb.max_q, causal=True, scale=vb.softmax_scale,
+                                   return_lse=True)
+        vdq, vdk, vdv = torch.empty_like(vq), torch.empty_like(vk), torch.empty_like(vv)
+        run_vbwd = lambda: A.attn_bwd_varlen(vq, vk, vv, vo, vdo, vl, vcq, vcq, vb.max_q, vb.max_q, causal=True,
+                                             scale=vb.softmax_scale, dq=vdq, dk=vdk, dv=vdv)
+        for _ in range(2):
+            run_vbwd()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0.record(stream)
+        for _ in range(5):
+            run_vbwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vbt = e0.elapsed_time(e1) / 5
+        vbflops = int(2.5 * vb.flops())
+        widened["backward_varlen"] = {
+            "workload": vb.name + "_backward", "sequences": vb.B, "Hq": vb.Hq, "Hkv": vb.Hkv, "D": vb.D,
+            "flops_per_launch": vbflops, "flop_count": "5 GEMMs (2.5x the forward's causal count)",
+            "ms_per_launch": round(vbt, 4), "tflops": round(vbflops / (vbt * 1e-3) / 1e12, 1),
+            "frac_of_2500_tflops": round(vbflops / (vbt * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+        del vq, vk, vv, vdo, vo, vl, vdq, vdk, vdv
+        # the pages' GQA sweep shape (B=2, Hq=16, N=1023, D=64): a grid small
+        # enough for 128-row blocks
+        gs = {}
+        for gc in (c for c in W.gqa_sweep() if c.Hkv == 4):
+            gq, gk, gv = (t.to(dev) for t in W.prefill_inputs(gc))
+            go = torch.empty_like(gq)
+            for _ in range(5):
+                A.attn_fwd(gq, gk, gv, causal=gc.causal, scale=gc.softmax_scale, out=go)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(2_000_000)
+            e0.record(stream)
+            for _ in range(50):
+                A.attn_fwd(gq, gk, gv, causal=gc.causal, scale=gc.softmax_scale, out=go)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gt = e0.elapsed_time(e1) / 50
+            gs["causal" if gc.causal else "full"] = {
+                "workload": gc.name, "us_per_launch": round(gt * 1e3, 2), "flops_per_launch": gc.flops(),
+                "tflops": round(gc.flops() / (gt * 1e-3) / 1e12, 1)}
+            del gq, gk, gv, go
+        widened["prefill_gqa_sweep"] = gs
 
     # context: achievable HBM rate of a plain 256 MiB device copy (read + write)
     copy_gbs = None
