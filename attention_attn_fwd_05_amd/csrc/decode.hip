@@ -39,9 +39,6 @@ namespace attn {
 namespace {
 
 constexpr int kDT = 128;        // keys per tile (32 per wave)
-#ifndef ATTN_DECODE_VSWZ
-#define ATTN_DECODE_VSWZ 1  // coalesced V loads + XOR-swizzled V^T in LDS
-#endif
 #ifndef ATTN_DECODE_WAVES_PER_SIMD
 #define ATTN_DECODE_WAVES_PER_SIMD 2  // workgroups per CU the register budget is sized for
 #endif
@@ -61,11 +58,7 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
   constexpr bool PAGED = MODE == 2;
   constexpr int KS = D / 32;                 // k-steps of the score MFMA
   constexpr int NDT = D / 16;                // 16-wide head-dim tiles of O
-#if ATTN_DECODE_VSWZ
   constexpr int VLD = kDT;                   // V^T row pitch (elements); 16-byte groups XOR-swizzled
-#else
-  constexpr int VLD = kDT + 8;               // V^T row pitch in LDS (elements)
-#endif
   constexpr int VBLK = (kDT / 4) * (D / 8);  // 4x8 V blocks per tile
   constexpr int VPT = VBLK / 256;            // V blocks per thread
   static_assert(VBLK % 256 == 0, "V blocks divide evenly");
@@ -134,23 +127,14 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int id = tid + 256 * j;
-#if ATTN_DECODE_VSWZ
     vdc[j] = id % (D / 8);
     vkvg[j] = id / (D / 8);
-#else
-    vkvg[j] = id % (kDT / 4);
-    vdc[j] = id / (kDT / 4);
-#endif
 #pragma unroll
     for (int r = 0; r < 4; ++r) voff[j][r] = (4 * vkvg[j] + r) * (int32_t)a.svn * 2 + 16 * vdc[j];
   }
   auto vt_at = [&](int d, int key) {  // element offset of V^T[d][key], key a multiple of 4
-#if ATTN_DECODE_VSWZ
     const int sw = (d ^ (d >> 3)) & 15;
     return d * VLD + 8 * ((key >> 3) ^ sw) + (key & 7);
-#else
-    return d * VLD + key;
-#endif
   };
 
   f32x4 oacc[NDT];
