@@ -453,20 +453,25 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
 
   // ---- epilogue: O = O^T / l, cast, store; lse = (m + log2 l) ln 2
   l = sum_xor32(l);
-  if (qrow < Nq) {
+  // The lane's row and half are re-derived from the lane counter here rather
+  // than kept live across the KV loop (which would cost two spilled registers).
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int hh_e = lane_e >> 5;
+  const int qrow_e = q0 + 32 * w + (lane_e & 31);
+  if (qrow_e < Nq) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    uint16_t* op = obase + (int64_t)qrow * a.son;
+    uint16_t* op = obase + (int64_t)qrow_e * a.son;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hh;
+        const int d = 32 * dt + 8 * g + 4 * hh_e;
         const u32x2 v2{pack2<BF16>(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
                        pack2<BF16>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
         *reinterpret_cast<u32x2*>(op + d) = v2;
       }
     }
-    if (lbase != nullptr && hh == 0) lbase[qrow] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    if (lbase != nullptr && hh_e == 0) lbase[qrow_e] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
