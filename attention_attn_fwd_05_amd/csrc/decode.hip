@@ -365,14 +365,17 @@ __global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel
 // Merge the split partials of one (batch, q head): o = sum_s e^(m_s - M) o_s /
 // sum_s e^(m_s - M) l_s and lse = M + ln(sum_s e^(m_s - M) l_s) (log2 domain
 // inside).  Thread -> (4-wide column of o, group of splits strided by G); all
-// of a thread's partial loads are issued before the (m, l) reduction.
+// of a thread's loads (its splits' o columns and m, and the (m, l) of split
+// `lane`) are issued first.  Lane s of every wave holds split s's (m, l), so M
+// and the denominator come from wave reductions, with no serial loop over the
+// splits.  One barrier: the column sums across the split groups of the 4 waves.
 template <int D, bool BF16, bool VARLEN>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a) {
   constexpr int HP = D + kPartPad;
   constexpr int C4 = D / 4;    // 4-wide columns
   constexpr int G = 256 / C4;  // split groups
   constexpr int PER = (kMaxSplits + G - 1) / G;  // splits per thread at most
-  __shared__ float sm[kMaxSplits], sw[kMaxSplits], sl[kMaxSplits];
+  static_assert(kMaxSplits <= 64 && G * PER <= 64, "one lane per split holds its (m, l)");
   __shared__ __attribute__((aligned(16))) float sacc[G * D];
   const int unit = a.unit_fast ? blockIdx.x : blockIdx.z;  // batch x kv head
   const int hgi = blockIdx.y;
@@ -393,38 +396,35 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a)
   const float* base = a.part + (slot * a.max_splits * a.heads_per_wg + hx) * HP;
   const int64_t sstride = (int64_t)a.heads_per_wg * HP;  // between splits
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int dq = tid % C4, sg = tid / C4;
   f32x4 ov[PER];
+  float mi[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int s = sg + i * G;
     ov[i] = (s < ns) ? *reinterpret_cast<const f32x4*>(base + s * sstride + kPartPad + 4 * dq) : f32x4{};
+    mi[i] = (s < ns) ? base[s * sstride] : -INFINITY;
   }
-  if (tid < ns) {
-    const f32x4 ml = *reinterpret_cast<const f32x4*>(base + tid * sstride);
-    sm[tid] = ml[0];
-    sl[tid] = ml[1];
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < ns) {
+    const f32x4 ml = *reinterpret_cast<const f32x4*>(base + lane * sstride);
+    ms = ml[0];
+    ls = ml[1];
   }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, sm[s]);
+  const float M = wave_max(ms);
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  if (tid < ns) sw[tid] = fast_exp2(sm[tid] - Mu);
-  __syncthreads();
+  const float L = wave_sum((lane < ns) ? fast_exp2(ms - Mu) * ls : 0.f);
   f32x4 o4 = f32x4{};
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int s = sg + i * G;
-    if (s < ns) o4 += sw[s] * ov[i];
-  }
+  for (int i = 0; i < PER; ++i)
+    if (sg + i * G < ns) o4 += fast_exp2(mi[i] - Mu) * ov[i];
   *reinterpret_cast<f32x4*>(sacc + 4 * (sg * C4 + dq)) = o4;
   __syncthreads();
   if (tid < C4) {
     f32x4 t = f32x4{};
 #pragma unroll
     for (int g = 0; g < G; ++g) t += *reinterpret_cast<const f32x4*>(sacc + 4 * (g * C4 + tid));
-    float L = 0.f;
-    for (int s = 0; s < ns; ++s) L += sw[s] * sl[s];
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     uint16_t* op = a.o + (int64_t)b * a.sob + (int64_t)h * a.soh + 4 * tid;
     *reinterpret_cast<u32x2*>(op) = u32x2{pack2<BF16>(t[0] * inv, t[1] * inv), pack2<BF16>(t[2] * inv, t[3] * inv)};

@@ -92,6 +92,32 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// max / sum of x over all 64 lanes, the same value in every lane.  Inside each
+// row of 16 lanes DPP moves combine neighbours (quad_perm [1,0,3,2]), pairs
+// (quad_perm [2,3,0,1]), the two quads of each half-row (row_half_mirror: after
+// the first two steps every lane of a quad holds the quad's result, so lane i
+// meeting lane 7 - i combines the two quads) and the two half-rows (row_mirror,
+// likewise); the permlane swaps above then combine the four rows.  Every step
+// is commutative per lane pair, so all lanes end with bitwise the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  x = fmaxf(x, dpp_mov<0x140>(x));
+  return max_xor32(max_xor16(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return sum_xor32(sum_xor16(x));
+}
+
 // Buffer resource over [base, base + bytes): 16-byte loads at byte offsets
 // >= bytes return zeros (hardware range check), so ragged tails need no branch.
 // `base` and `bytes` must be wave-uniform; readfirstlane makes that explicit to
