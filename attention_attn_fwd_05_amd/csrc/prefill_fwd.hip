@@ -297,11 +297,21 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     {
       constexpr uint32_t off0 = 2 * STG * L::TILE, off1 = off0 + 2 * 32 * D;
+      if constexpr (!MASKED) {
+        // the two subtiles' MFMAs alternate, so the K reads (issued a few
+        // MFMAs ahead) are consumed in the order they were issued
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off0), qf[ks], s0);
-      if (act1) {
+        for (int ks = 0; ks < KS; ++ks) {
+          s0 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off0), qf[ks], s0);
+          s1 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off1), qf[ks], s1);
+        }
+      } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off1), qf[ks], s1);
+        for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off0), qf[ks], s0);
+        if (act1) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off1), qf[ks], s1);
+        }
       }
       schedule_scores();
     }
