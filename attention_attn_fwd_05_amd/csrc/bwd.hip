@@ -46,6 +46,18 @@ constexpr int kKvW = 8;           // waves per dkdv workgroup (two per SIMD)
 constexpr int kKvRows = 128;      // keys per dkdv workgroup (32 per wave pair)
 constexpr int kBT = 64;           // streamed rows per LDS tile
 constexpr int kBStages = 3;      // LDS ring depth
+#ifndef ATTN_BWD_Q_PF
+#define ATTN_BWD_Q_PF 1  // dQ pass: k-steps of K/V reads in flight ahead of its S, dP MFMAs (0: compiler order)
+#endif
+#ifndef ATTN_BWD_Q_GPF
+#define ATTN_BWD_Q_GPF 0  // dQ pass: steps of transposing reads in flight ahead of its dQ MFMAs (0: compiler order)
+#endif
+#ifndef ATTN_BWD_KV_GPF
+#define ATTN_BWD_KV_GPF 1  // steps of transposing reads in flight ahead of its dV, dK MFMAs (0: compiler order)
+#endif
+#ifndef ATTN_BWD_KV_PF
+#define ATTN_BWD_KV_PF 1  // k-steps of operand reads in flight ahead of the dK/dV pass's S, dP MFMAs
+#endif
 
 // ---- lse * log2(e) and delta = rowsum(dO * O) per query row, fp32 pairs
 template <int D, bool BF16>
@@ -283,11 +295,34 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
       if (u == 1 && !act1) break;
       const uint32_t so = 2 * stage * L::TILE + 2 * 32 * u * D;
       f32x16 sx = f32x16{}, px = f32x16{};
+#if ATTN_BWD_Q_PF > 0
+      {
+        // software pipeline: k-step ks + PF's K and V reads go out before
+        // k-step ks's two MFMAs; the fences keep them there
+        constexpr int PF = ATTN_BWD_Q_PF;
+        u32x4 opk[PF + 1], opv[PF + 1];
+        auto issue = [&](int ks) __attribute__((always_inline)) {
+          opk[ks % (PF + 1)] = lds_load16(ka[ks] + so);
+          opv[ks % (PF + 1)] = lds_load16(va[ks] + so);
+        };
+#pragma unroll
+        for (int ks = 0; ks < PF; ++ks) issue(ks);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + PF < KS) issue(ks + PF);
+          __builtin_amdgcn_sched_barrier(0);
+          sx = mfma_32x32x16<BF16>(opk[ks % (PF + 1)], qf[ks], sx);
+          px = mfma_32x32x16<BF16>(opv[ks % (PF + 1)], gf[ks], px);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#else
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sx = mfma_32x32x16<BF16>(lds_load16(ka[ks] + so), qf[ks], sx);
         px = mfma_32x32x16<BF16>(lds_load16(va[ks] + so), gf[ks], px);
       }
+#endif
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float pv = fast_exp2(__builtin_fmaf(sx[e], c, -lse2));
@@ -302,6 +337,36 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
     const uint32_t so = 2 * stage * L::TILE;
     // dQ^T += K^T dS^T
+#if ATTN_BWD_Q_GPF > 0
+    {
+      // the same pipeline over the (kk, dt) steps, two transposing reads a
+      // step; the second subtile's steps run only when it is active
+      constexpr int GP = ATTN_BWD_Q_GPF;
+      u32x4 opk[GP + 1];
+      auto issue = [&](int i) __attribute__((always_inline)) {
+        const int kk = i / DT, dt = i % DT;
+        const uint32_t o = so + 2 * 16 * kk * D;
+        const u32x2 lo = lds_read_tr16(kt[dt][0] + o);
+        const u32x2 hi = lds_read_tr16(kt[dt][1] + o);
+        opk[i % (GP + 1)] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      auto run = [&](int i0, int i1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = i0; i < i0 + GP; ++i) issue(i);
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+          if (i + GP < i1) issue(i + GP);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[i % DT] = mfma_32x32x16<BF16>(opk[i % (GP + 1)], pf[i / DT], acc[i % DT]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (act1)
+        run(0, 4 * DT);
+      else
+        run(0, 2 * DT);
+    }
+#else
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 2 || act1) {
@@ -314,6 +379,7 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
         }
       }
     }
+#endif
   };
 
   // 3-stage ring: the loads of tile t + 2 go out before tile t is computed
@@ -508,17 +574,41 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     if (masked && BAND && (kmin > tq + 31 + off + WR || kmin + 31 < tq + off - WL)) return;
     const uint32_t sq = stage * 2 * L::TILE * 2, sg = sq + 2 * L::TILE;
     f32x16 sx = f32x16{}, px = f32x16{};
+    // software pipeline: the four operand reads of k-step ks + PF go out before
+    // k-step ks's two MFMAs (a loaded LDS read takes some 250 cycles); the
+    // scheduling fences keep the compiler from sinking them next to their use
+    constexpr int PF = ATTN_BWD_KV_PF;
+    u32x4 opq[PF + 1], opk[PF + 1], opg[PF + 1], opv[PF + 1];
+    auto issue = [&](int ks) __attribute__((always_inline)) {
+      const int r = ks % (PF + 1);
+      opq[r] = lds_load16(qa[ks] + sq);
+      opk[r] = lds_load16(kva[ks]);
+      opg[r] = lds_load16(qa[ks] + sg);
+      opv[r] = lds_load16(kva[ks] + 2 * L::KB);
+    };
+    // the (lse2, delta) pairs of this wave's 16 queries per lane, read with the
+    // last k-step's MFMAs in flight
+    f32x4 ldp[8];
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) issue(ks);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sx = mfma_32x32x16<BF16>(lds_load16(qa[ks] + sq), lds_load16(kva[ks]), sx);
-      px = mfma_32x32x16<BF16>(lds_load16(qa[ks] + sg), lds_load16(kva[ks] + 2 * L::KB), px);
+      if (ks + PF < KS) issue(ks + PF);
+      if (ks == KS - 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          ldp[i] = __builtin_bit_cast(f32x4, lds_load16(ldr + stage * 4 * kBT * 2 + 8 * (i >> 1) * 8 + 16 * (i & 1)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int r = ks % (PF + 1);
+      sx = mfma_32x32x16<BF16>(opq[r], opk[r], sx);
+      px = mfma_32x32x16<BF16>(opg[r], opv[r], px);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // element e of lane (n, hh) is query tq + 8(e/4) + 4hh + e%4, key `key`
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t lo = ldr + stage * 4 * kBT * 2 + 8 * g * 8;
-      const f32x4 a0 = __builtin_bit_cast(f32x4, lds_load16(lo));
-      const f32x4 a1 = __builtin_bit_cast(f32x4, lds_load16(lo + 16));
+      const f32x4 a0 = ldp[2 * g], a1 = ldp[2 * g + 1];
       const float l2[4] = {a0[0], a0[2], a1[0], a1[2]};
       const float dl[4] = {a0[1], a0[3], a1[1], a1[3]};
 #pragma unroll
@@ -538,6 +628,35 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     pack_pt<BF16>(sx, pp);
     pack_pt<BF16>(px, dp);
     // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries
+#if ATTN_BWD_KV_GPF > 0
+    {
+      // the same software pipeline over the 2 x DT steps (kk, dt), four
+      // transposing reads a step
+      constexpr int GP = ATTN_BWD_KV_GPF, NS = 2 * DT;
+      u32x4 opg[GP + 1], opq[GP + 1];
+      auto issue = [&](int i) __attribute__((always_inline)) {
+        const int r = i % (GP + 1), kk = i / DT, dt = i % DT;
+        const uint32_t o = sq + 2 * 16 * kk * D;
+        const u32x2 glo = lds_read_tr16(qt[dt][0] + o + 2 * L::TILE);
+        const u32x2 ghi = lds_read_tr16(qt[dt][1] + o + 2 * L::TILE);
+        const u32x2 qlo = lds_read_tr16(qt[dt][0] + o);
+        const u32x2 qhi = lds_read_tr16(qt[dt][1] + o);
+        opg[r] = u32x4{glo[0], glo[1], ghi[0], ghi[1]};
+        opq[r] = u32x4{qlo[0], qlo[1], qhi[0], qhi[1]};
+      };
+#pragma unroll
+      for (int i = 0; i < GP; ++i) issue(i);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (i + GP < NS) issue(i + GP);
+        __builtin_amdgcn_sched_barrier(0);
+        const int r = i % (GP + 1), kk = i / DT, dt = i % DT;
+        adv[dt] = mfma_32x32x16<BF16>(opg[r], pp[kk], adv[dt]);
+        adk[dt] = mfma_32x32x16<BF16>(opq[r], dp[kk], adk[dt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#else
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const uint32_t o = sq + 2 * 16 * kk * D;
@@ -551,6 +670,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
         adk[dt] = mfma_32x32x16<BF16>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dp[kk], adk[dt]);
       }
     }
+#endif
   };
 
   // 2-stage ring: the loads of tile it + 1 go out before tile it is computed
