@@ -297,7 +297,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     {
       constexpr uint32_t off0 = 2 * STG * L::TILE, off1 = off0 + 2 * 32 * D;
-      if constexpr (!MASKED) {
+      if (act1) {
         // the two subtiles' MFMAs alternate, so the K reads (issued a few
         // MFMAs ahead) are consumed in the order they were issued
 #pragma unroll
@@ -305,15 +305,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
           s0 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off0), qf[ks], s0);
           s1 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off1), qf[ks], s1);
         }
+        schedule_scores();
       } else {
+        // (masked tiles only) the second subtile lies wholly outside this
+        // wave's rows
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off0), qf[ks], s0);
-        if (act1) {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) s1 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off1), qf[ks], s1);
-        }
       }
-      schedule_scores();
     }
 
     if constexpr (MASKED) {
