@@ -47,17 +47,15 @@ constexpr int kKvRows = 128;      // keys per dkdv workgroup (32 per wave pair)
 constexpr int kBT = 64;           // streamed rows per LDS tile
 constexpr int kBStages = 3;      // LDS ring depth
 #ifndef ATTN_BWD_Q_PF
-#define ATTN_BWD_Q_PF 1  // dQ pass: k-steps of K/V reads in flight ahead of its S, dP MFMAs (0: compiler order)
-#endif
-#ifndef ATTN_BWD_Q_GPF
-#define ATTN_BWD_Q_GPF 0  // dQ pass: steps of transposing reads in flight ahead of its dQ MFMAs (0: compiler order)
+#define ATTN_BWD_Q_PF 1  // dQ pass: k-steps of K/V reads in flight ahead of its S, dP MFMAs (>= 1)
 #endif
 #ifndef ATTN_BWD_KV_GPF
-#define ATTN_BWD_KV_GPF 1  // steps of transposing reads in flight ahead of its dV, dK MFMAs (0: compiler order)
+#define ATTN_BWD_KV_GPF 1  // dK/dV pass: steps of transposing reads in flight ahead of its dV, dK MFMAs (>= 1)
 #endif
 #ifndef ATTN_BWD_KV_PF
-#define ATTN_BWD_KV_PF 1  // k-steps of operand reads in flight ahead of the dK/dV pass's S, dP MFMAs
+#define ATTN_BWD_KV_PF 1  // dK/dV pass: k-steps of operand reads in flight ahead of its S, dP MFMAs (>= 1)
 #endif
+static_assert(ATTN_BWD_Q_PF >= 1 && ATTN_BWD_KV_PF >= 1 && ATTN_BWD_KV_GPF >= 1, "pipeline depths are at least one step");
 
 // ---- lse * log2(e) and delta = rowsum(dO * O) per query row, fp32 pairs
 template <int D, bool BF16>
@@ -295,7 +293,6 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
       if (u == 1 && !act1) break;
       const uint32_t so = 2 * stage * L::TILE + 2 * 32 * u * D;
       f32x16 sx = f32x16{}, px = f32x16{};
-#if ATTN_BWD_Q_PF > 0
       {
         // software pipeline: k-step ks + PF's K and V reads go out before
         // k-step ks's two MFMAs; the fences keep them there
@@ -316,13 +313,6 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-#else
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sx = mfma_32x32x16<BF16>(lds_load16(ka[ks] + so), qf[ks], sx);
-        px = mfma_32x32x16<BF16>(lds_load16(va[ks] + so), gf[ks], px);
-      }
-#endif
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float pv = fast_exp2(__builtin_fmaf(sx[e], c, -lse2));
@@ -337,36 +327,6 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
     }
     const uint32_t so = 2 * stage * L::TILE;
     // dQ^T += K^T dS^T
-#if ATTN_BWD_Q_GPF > 0
-    {
-      // the same pipeline over the (kk, dt) steps, two transposing reads a
-      // step; the second subtile's steps run only when it is active
-      constexpr int GP = ATTN_BWD_Q_GPF;
-      u32x4 opk[GP + 1];
-      auto issue = [&](int i) __attribute__((always_inline)) {
-        const int kk = i / DT, dt = i % DT;
-        const uint32_t o = so + 2 * 16 * kk * D;
-        const u32x2 lo = lds_read_tr16(kt[dt][0] + o);
-        const u32x2 hi = lds_read_tr16(kt[dt][1] + o);
-        opk[i % (GP + 1)] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      };
-      auto run = [&](int i0, int i1) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = i0; i < i0 + GP; ++i) issue(i);
-#pragma unroll
-        for (int i = i0; i < i1; ++i) {
-          if (i + GP < i1) issue(i + GP);
-          __builtin_amdgcn_sched_barrier(0);
-          acc[i % DT] = mfma_32x32x16<BF16>(opk[i % (GP + 1)], pf[i / DT], acc[i % DT]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      if (act1)
-        run(0, 4 * DT);
-      else
-        run(0, 2 * DT);
-    }
-#else
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 2 || act1) {
@@ -379,7 +339,6 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
         }
       }
     }
-#endif
   };
 
   // 3-stage ring: the loads of tile t + 2 go out before tile t is computed
@@ -628,7 +587,6 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     pack_pt<BF16>(sx, pp);
     pack_pt<BF16>(px, dp);
     // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries
-#if ATTN_BWD_KV_GPF > 0
     {
       // the same software pipeline over the 2 x DT steps (kk, dt), four
       // transposing reads a step
@@ -656,21 +614,6 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#else
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t o = sq + 2 * 16 * kk * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x2 glo = lds_read_tr16(qt[dt][0] + o + 2 * L::TILE);
-        const u32x2 ghi = lds_read_tr16(qt[dt][1] + o + 2 * L::TILE);
-        adv[dt] = mfma_32x32x16<BF16>(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pp[kk], adv[dt]);
-        const u32x2 qlo = lds_read_tr16(qt[dt][0] + o);
-        const u32x2 qhi = lds_read_tr16(qt[dt][1] + o);
-        adk[dt] = mfma_32x32x16<BF16>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dp[kk], adk[dt]);
-      }
-    }
-#endif
   };
 
   // 2-stage ring: the loads of tile it + 1 go out before tile it is computed

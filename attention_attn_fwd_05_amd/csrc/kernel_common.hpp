@@ -56,17 +56,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
 }
 
-// acc + lo + hi of a packed pair of 16-bit values, in fp32 (v_dot2c_f32_{f16,bf16}).
-template <bool BF16>
-__device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-  if constexpr (BF16)
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), (bf16x2){(__bf16)1.0f, (__bf16)1.0f},
-                                           acc, false);
-  else
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), (f16x2){(_Float16)1.0f, (_Float16)1.0f}, acc,
-                                  false);
-}
-
 // max / sum of x over lanes l and l ^ 32 (l ^ 16) with v_permlane32_swap
 // (v_permlane16_swap), gfx950: with x as both operands the two results hold,
 // in every lane, the values of lanes l and l ^ 32 (l ^ 16), so combining them
