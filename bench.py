@@ -12,8 +12,9 @@ beside it).  Decode (a ~20 us call)
 is additionally timed in steady state right after the timed steps: back-to-
 back calls between two events, queued behind a sleep kernel so the events
 measure GPU time only; that figure is the reported decode GB/s.  The same
-measurement on a single cache copy (resident in the Infinity Cache) and a
-plain 256 MiB device copy's rate are printed as context.
+measurement on a single cache copy (resident in the Infinity Cache), a plain
+256 MiB device copy's rate and a large fp16 library GEMM's rate are printed as
+context (achievable HBM and dense-MFMA references on the same box).
 
 `value` is the prefill throughput in TFLOP/s with algorithmic FLOPs counted as
 4 * D per visible (query, key) pair (causal: N(N+1)/2 pairs per head).  Decode
@@ -462,6 +463,27 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = 2 * copy_src.numel() / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
 
+    # context: achievable dense fp16 MFMA rate of a large library GEMM (torch.mm,
+    # 8192^3, contiguous operands) on the same box
+    gemm_tflops = None
+    if args.only == "all":
+        n = 8192
+        ga = torch.randn(n, n, device=dev, dtype=torch.float16)
+        gb = torch.randn(n, n, device=dev, dtype=torch.float16)
+        gcm = torch.empty(n, n, device=dev, dtype=torch.float16)
+        for _ in range(3):
+            torch.mm(ga, gb, out=gcm)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            torch.mm(ga, gb, out=gcm)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gemm_tflops = 2 * n ** 3 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+        del ga, gb, gcm
+
     res = {}
     if do_p:
         pt = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]  # ms
@@ -529,6 +551,11 @@ def main():
         out["context"] = {"hbm_copy_gbs": round(copy_gbs, 1),
                           "note": "plain 256 MiB device copy (read+write bytes) on this box: an achievable HBM rate; "
                                   "decode.achieved / hbm_copy_gbs is the fraction of it"}
+        if gemm_tflops is not None:
+            out["context"]["fp16_gemm_tflops"] = round(gemm_tflops, 1)
+            out["context"]["gemm_note"] = ("torch.mm of two 8192 x 8192 fp16 matrices (a library GEMM) on this box: an "
+                                           "achievable dense-MFMA rate; roofline.achieved / fp16_gemm_tflops is the "
+                                           "fraction of it")
     out["detail"] = res
     if do_p and args.only == "all" and not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(pcase, args.cpu_seconds)
