@@ -339,14 +339,15 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
         s1[e] = vis1 ? s1[e] : -INFINITY;
       }
     }
-    float mx = -INFINITY;
+    float mx = -INFINITY;  // this lane's half of its row
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = vmax(mx, vmax(s0[e], s1[e]));
-    mx = max_xor32(mx) * c;  // this row's max in the log2 domain
 
-    // move the reference max only when some row's max outgrew it by > 2^8
-    if (__any(mx > m + kRescaleLog2)) {
-      const float m_new = fmaxf(m, mx);
+    // move the reference max only when some row's max outgrew it by > 2^8.
+    // With c > 0 a row's max (times c) exceeds that bound iff one of its two
+    // halves does, so the common path needs no exchange between the halves
+    if (__any(mx * c > m + kRescaleLog2)) {
+      const float m_new = fmaxf(m, max_xor32(mx) * c);  // the row's max in the log2 domain
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
