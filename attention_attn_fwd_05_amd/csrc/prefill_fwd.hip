@@ -8,11 +8,13 @@
 //
 // gfx950 design (not the pages' Triton tiling):
 //   * one workgroup = 8 wave64s = 256 query rows of one q head; each wave owns
-//     32 rows for the whole KV loop (two waves per SIMD).
+//     32 rows for the whole KV loop (two waves per SIMD).  When 256-row blocks
+//     would leave at least half the CUs idle, 4 waves = 128 rows (one wave per
+//     SIMD), with bitwise the same per-row arithmetic.
 //   * KV tiles of 64 rows go from HBM/L2 straight into LDS with buffer-to-LDS
-//     loads (no register staging), through a 3-stage ring, row-major with an
+//     loads (no register staging), through a 4-stage ring, row-major with an
 //     XOR swizzle of 16-byte slots that keeps every access pattern free of bank
-//     conflicts.  The loads of tile t+2 are issued before tile t is computed;
+//     conflicts.  The loads of tile t+3 are issued before tile t is computed;
 //     the buffer range check writes zeros past the last key, so ragged tails
 //     need no branches.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
@@ -22,10 +24,11 @@
 //     row-major tile; its key order matches the fp32 score registers, which
 //     therefore are directly the B operand: no shuffles between the two
 //     contractions.
-//   * online softmax in the log2 domain: t = s * scale * log2(e); the row max
-//     needs one cross-lane exchange (lanes l and l+32 share a row); the row
-//     sum l is accumulated from the fp32 P, which then goes to 16 bits (round
-//     to nearest even) right before the P.V MFMA; m, l and O stay fp32.
+//   * online softmax in the log2 domain: t = s * scale * log2(e); lanes l and
+//     l+32 hold the two halves of a row, and their maxima are exchanged only
+//     when the reference max moves (below); the row sum l is accumulated from
+//     the fp32 P, which then goes to 16 bits (round to nearest even) right
+//     before the P.V MFMA; m, l and O stay fp32.
 //   * the reference max used for exp2 moves -- rescaling O and l by alpha --
 //     only when a row's max exceeds it by more than 2^8.  O and l are always
 //     relative to the same reference, so O / l is unchanged (the rescale of
