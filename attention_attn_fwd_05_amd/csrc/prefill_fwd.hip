@@ -342,9 +342,21 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
         s1[e] = vis1 ? s1[e] : -INFINITY;
       }
     }
-    float mx = -INFINITY;  // this lane's half of its row
+    // this lane's half of its row: the 32 scores as a tree of 3-input maxima
+    // (v_maximum3_f32), 16 instructions
+    float t3[11];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = vmax(mx, vmax(s0[e], s1[e]));
+    for (int i = 0; i < 10; ++i) {
+      const int j = 3 * i;
+      const float x0 = j < 16 ? s0[j] : s1[j - 16];
+      const float x1 = j + 1 < 16 ? s0[j + 1] : s1[j + 1 - 16];
+      const float x2 = j + 2 < 16 ? s0[j + 2] : s1[j + 2 - 16];
+      t3[i] = vmax(vmax(x0, x1), x2);
+    }
+    t3[10] = vmax(s1[14], s1[15]);
+    const float u0 = vmax(vmax(t3[0], t3[1]), t3[2]), u1 = vmax(vmax(t3[3], t3[4]), t3[5]);
+    const float u2 = vmax(vmax(t3[6], t3[7]), t3[8]), u3 = vmax(t3[9], t3[10]);
+    const float mx = vmax(vmax(u0, u1), vmax(u2, u3));
 
     // move the reference max only when some row's max outgrew it by > 2^8.
     // With c > 0 a row's max (times c) exceeds that bound iff one of its two
