@@ -60,6 +60,37 @@ def test_serving_sampled(n, causal):
     run_case(case, rows=rows)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,dtype,causal", [
+    (1, 4, 2, "fp16", True),    # 8 blocks: the 128-row (4-wave) path
+    (1, 4, 2, "bf16", False),
+    (2, 32, 8, "fp16", True),   # 256 blocks: the 256-row (8-wave) path
+])
+def test_reference_max_moves_every_tile(B, Hq, Hkv, dtype, causal):
+    """Scores that step up by ~16 log2 units from each 64-key tile to the next,
+    with the largest at a random key of the tile: every tile moves the
+    reference max and rescales the accumulated O and l (random N(0, 1) data
+    almost never does after the first tile), and the new max falls in either
+    lane half of its row."""
+    N = 1000
+    case = W.PrefillCase(f"rising_B{B}_H{Hq}_{dtype}_{'c' if causal else 'nc'}", B, Hq, Hkv, N, N, 128, dtype,
+                         causal, seed=W.BASE_SEED + 170 + B + Hq + (dtype == "bf16"))
+    q, k, v = W.rising_score_inputs(case)
+    _say(f"{case.name} seed={case.seed}")
+    o, lse = A.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=case.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    rows = None if B * Hq <= 4 else sample_rows(N, causal, np.random.default_rng(170))
+    Oref, Lref = oracle.attention_forward(_np(q), _np(k), _np(v), case.softmax_scale, causal, rows=rows)
+    assert torch.isfinite(o.float()).all()
+    og, lg = (o, lse) if rows is None else (o[:, :, torch.as_tensor(rows)], lse[:, :, torch.as_tensor(rows)])
+    check_o(og.cpu(), Oref, case.torch_dtype)
+    check_lse(lg.cpu(), Lref)
+    # the inputs do what they are for: the last row's scores outgrow those of
+    # the first 64-key tile by far more than 2^8
+    _, l_first = oracle.attention_forward(_np(q[:, :, -1:]), _np(k[:, :, :64]), _np(v[:, :, :64]),
+                                          case.softmax_scale, False)
+    assert float((Lref[..., -1] - l_first[..., 0]).min()) > 8 * math.log(2)
+
+
 def test_cross_mqa_bf16_sampled():
     rows = sample_rows(W.CROSS.Nq, False, np.random.default_rng(5))
     run_case(W.CROSS, rows=rows)

@@ -175,6 +175,25 @@ def prefill_inputs(case: PrefillCase):
     return q, k, v
 
 
+def rising_score_inputs(case: PrefillCase, tile: int = 64, rise: float = 128.0, jitter: float = 8.0):
+    """Inputs whose scores step up from one key tile to the next.
+
+    Drawn as ``prefill_inputs``, then query dimension 0 is set to 1 and key
+    dimension 0 to ``rise * (j // tile) + jitter * N(0, 1)``, so every row's
+    largest score grows by about ``rise * scale * log2(e)`` (log2 units) from
+    each tile of ``tile`` keys to the next, at a random key inside the tile.
+    """
+    q, k, v = prefill_inputs(case)
+    g = _gen(case.seed + 1000)
+    j = torch.arange(case.Nkv, dtype=torch.float32)
+    k0 = rise * torch.floor(j / tile) + jitter * torch.randn(case.B, case.Hkv, case.Nkv, generator=g)
+    q = q.clone()
+    k = k.clone()
+    q[..., 0] = 1.0
+    k[..., 0] = k0.to(k.dtype)
+    return q, k, v
+
+
 def decode_inputs(case: DecodeCase):
     """CPU tensors q (B,Hq,D) and full caches (B,Hkv,S_max,D).
 
