@@ -71,6 +71,23 @@ def test_prefill_band(band):
     _compare(o, l, Oref, Lref, case.torch_dtype)
 
 
+@pytest.mark.parametrize("window", [(300, 0), (200, 200)])
+def test_prefill_band_rising_scores(window):
+    """A band over scores that step up from each 64-key tile to the next: the
+    reference max moves on every tile a row sees, on the band kernel's masked
+    and unmasked tiles alike."""
+    causal = window[1] == 0  # a two-sided band goes with no causal mask
+    case = W.PrefillCase(f"band_rising_{window[0]}_{window[1]}", 2, 32, 8, 1000, 1000, 128, "fp16", causal,
+                         seed=W.BASE_SEED + 180 + window[1])
+    q, k, v = W.rising_score_inputs(case)
+    _say(f"{case.name} window={window}")
+    o, l = A.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window, scale=case.softmax_scale,
+                      return_lse=True)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.attention_forward(_np(q), _np(k), _np(v), case.softmax_scale, causal, window=window)
+    _compare(o, l, Oref, Lref, case.torch_dtype)
+
+
 def test_prefill_band_identities_bitwise():
     """(-1, -1) is attn_fwd without a mask, (-1, 0) attn_fwd causal, and a
     causal window wider than the sequence takes the band path to the same bits."""
