@@ -51,9 +51,9 @@ def _check(name, got, ref, dtype, floor=0.0):
     assert err <= tol, f"{name}: max|err| {err:.3e} > {tol:.3e}"
 
 
-def run_bwd(name, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, align="top_left", seed=0, window=None):
+def run_bwd(name, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, align="top_left", seed=0, window=None, rising=False):
     case = W.PrefillCase(name, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, seed=W.BASE_SEED + 120 + seed)
-    q, k, v = W.prefill_inputs(case)
+    q, k, v = W.rising_score_inputs(case) if rising else W.prefill_inputs(case)
     g = torch.Generator().manual_seed(W.BASE_SEED + 220 + seed)
     do = torch.randn(B, Hq, Nq, D, generator=g).to(case.torch_dtype)
     _say(f"{name} B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nkv={Nkv} D={D} {dtype} causal={causal} align={align} "
@@ -72,6 +72,13 @@ def run_bwd(name, B, Hq, Hkv, Nq, Nkv, D, dtype, causal, align="top_left", seed=
     _check("dK", dk, rk, case.torch_dtype, _floor(D, Nq, do, v.float(), sc, q.float()))
     _check("dV", dv, rv, case.torch_dtype)
     return dq, dk, dv
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_bwd_rising_scores(causal):
+    """Scores that step up by ~16 log2 units per 64-key tile (lse up to ~170):
+    P = exp(S scale - lse) spans the whole fp32 range along each row."""
+    run_bwd("bwd_rising", 1, 4, 2, 1000, 1000, 128, "fp16", causal, seed=60 + causal, rising=True)
 
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
