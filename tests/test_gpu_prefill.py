@@ -60,20 +60,21 @@ def test_serving_sampled(n, causal):
     run_case(case, rows=rows)
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,dtype,causal", [
-    (1, 4, 2, "fp16", True),    # 8 blocks: the 128-row (4-wave) path
-    (1, 4, 2, "bf16", False),
-    (2, 32, 8, "fp16", True),   # 256 blocks: the 256-row (8-wave) path
+@pytest.mark.parametrize("B,Hq,Hkv,dtype,causal,D", [
+    (1, 4, 2, "fp16", True, 128),    # 8 blocks: the 128-row (4-wave) path
+    (1, 4, 2, "bf16", False, 128),
+    (2, 32, 8, "fp16", True, 128),   # 256 blocks: the 256-row (8-wave) path
+    (2, 32, 8, "bf16", True, 64),
 ])
-def test_reference_max_moves_every_tile(B, Hq, Hkv, dtype, causal):
+def test_reference_max_moves_every_tile(B, Hq, Hkv, dtype, causal, D):
     """Scores that step up by ~16 log2 units from each 64-key tile to the next,
     with the largest at a random key of the tile: every tile moves the
     reference max and rescales the accumulated O and l (random N(0, 1) data
     almost never does after the first tile), and the new max falls in either
     lane half of its row."""
     N = 1000
-    case = W.PrefillCase(f"rising_B{B}_H{Hq}_{dtype}_{'c' if causal else 'nc'}", B, Hq, Hkv, N, N, 128, dtype,
-                         causal, seed=W.BASE_SEED + 170 + B + Hq + (dtype == "bf16"))
+    case = W.PrefillCase(f"rising_B{B}_H{Hq}_D{D}_{dtype}_{'c' if causal else 'nc'}", B, Hq, Hkv, N, N, D, dtype,
+                         causal, seed=W.BASE_SEED + 170 + B + Hq + D + (dtype == "bf16"))
     q, k, v = W.rising_score_inputs(case)
     _say(f"{case.name} seed={case.seed}")
     o, lse = A.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=case.softmax_scale, return_lse=True)

@@ -89,6 +89,26 @@ def test_varlen_queries_differ_from_keys(causal, br):
     run_varlen(case)
 
 
+@pytest.mark.parametrize("causal,br", MODES, ids=MODE_IDS)
+def test_varlen_rising_scores(causal, br):
+    """Two packed sequences (1000 and 700 rows) of the rising-score inputs: the
+    reference max moves on every tile the packed kernel visits."""
+    case = W.PrefillCase("varlen_rising", 2, 4, 2, 1000, 1000, 128, "fp16", causal, seed=W.BASE_SEED + 190 + causal + br)
+    q, k, v = W.rising_score_inputs(case)
+    lens = [1000, 700]
+    pack = lambda x: torch.cat([x[0].transpose(0, 1), x[1, :, :lens[1]].transpose(0, 1)]).contiguous()  # noqa: E731
+    qp, kp, vp = pack(q), pack(k), pack(v)
+    cu = [0, lens[0], lens[0] + lens[1]]
+    _say(f"varlen rising causal={causal} bottom_right={br}")
+    o, l = A.attn_fwd_varlen(qp.to(DEV), kp.to(DEV), vp.to(DEV), _cu(lens), _cu(lens), max(lens), causal=causal,
+                             scale=case.softmax_scale, return_lse=True,
+                             causal_align="bottom_right" if br else "top_left")
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.attention_varlen(_np(qp), _np(kp), _np(vp), cu, cu, case.softmax_scale, causal,
+                                         bottom_right=br)
+    _compare(o, l, Oref, Lref, case.torch_dtype)
+
+
 def test_varlen_equal_lengths_is_fwd_bitwise():
     """B equal-length sequences packed: identical bits to attn_fwd on the (B, N, H, D) layout."""
     B, N, Hq, Hkv, D = 3, 1000, 8, 2, 128
