@@ -46,6 +46,24 @@ def run_decode(case: W.DecodeCase, num_splits=0, ws=None, check=True):
     return o, l
 
 
+@pytest.mark.parametrize("L,ns", [(4000, 0), (4000, 64), (4000, 7), (8192, 0)])
+def test_decode_rising_scores_split_merge(L, ns):
+    """A cache whose scores step up by ~16 log2 units per 64 slots: the split
+    partials' maxima differ by hundreds of log2 units, so the merge weights
+    e^(m_s - M) range from 1 down to underflow (random caches keep them all
+    near 1)."""
+    case = W.PrefillCase(f"dec_rising_L{L}", 2, 32, 8, 1, L, 128, "fp16", False, seed=W.BASE_SEED + 200 + ns)
+    q, k, v = W.rising_score_inputs(case)
+    q1 = q[:, :, 0].contiguous()  # (B, Hq, D), dimension 0 = 1
+    _say(f"{case.name} splits={ns}")
+    o, l = A.attn_decode(q1.to(DEV), k.to(DEV), v.to(DEV), L, scale=case.softmax_scale, num_splits=ns,
+                         return_lse=True)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.decode(_np(q1), _np(k), _np(v), L, case.softmax_scale)
+    check_o(o, Oref, case.torch_dtype)
+    check_lse(l, Lref)
+
+
 @pytest.mark.parametrize("L", W.DECODE_LENS)
 def test_decode_lengths(L):
     run_decode(W.decode_case(L))
