@@ -138,6 +138,13 @@ def _on_gpu(*ts: torch.Tensor):
             raise ValueError("all tensors must be on the same GPU")
 
 
+def _nbytes(ws: torch.Tensor) -> int:
+    """Size in bytes of a caller's workspace tensor, which must be one contiguous block."""
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    return ws.numel() * ws.element_size()
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -319,14 +326,14 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, c
                                 lse.data_ptr() if lse is not None else None, B, Hq, Hkv, S_max, int(cache_len), D,
                                 _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out), s, code,
                                 int(num_splits), ctypes.byref(opts), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream(q))
+                                _nbytes(workspace), _stream(q))
         _check(st, "attn_decode_ex")
         return (out, lse) if return_lse else out
     st = lib.attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                          lse.data_ptr() if lse is not None else None,
                          B, Hq, Hkv, S_max, int(cache_len), D,
                          _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out),
-                         s, code, int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         s, code, int(num_splits), workspace.data_ptr(), _nbytes(workspace),
                          _stream(q))
     _check(st, "attn_decode")
     return (out, lse) if return_lse else out
@@ -369,7 +376,7 @@ def attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                 lse.data_ptr() if lse is not None else None, B, Hq, Hkv, S_max, mcl, D,
                                 _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out), s, code,
                                 int(num_splits), ctypes.byref(opts), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream(q))
+                                _nbytes(workspace), _stream(q))
         _check(st, "attn_decode_ex")
         return (out, lse) if return_lse else out
     st = lib.attn_decode_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
@@ -377,7 +384,7 @@ def attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                 B, Hq, Hkv, S_max, cache_lens.data_ptr(), mcl, D,
                                 _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out),
                                 s, code, int(num_splits), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream(q))
+                                _nbytes(workspace), _stream(q))
     _check(st, "attn_decode_varlen")
     return (out, lse) if return_lse else out
 
@@ -446,7 +453,7 @@ def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
         st = lib.attn_decode_ex(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
                                 lse.data_ptr() if lse is not None else None, B, Hq, Hkv, 0, int(max_cache_len), D,
                                 _strides3(q), _strides4(k_pages), _strides4(v_pages), _strides3(out), s, code,
-                                int(num_splits), ctypes.byref(opts), workspace.data_ptr(), workspace.numel(),
+                                int(num_splits), ctypes.byref(opts), workspace.data_ptr(), _nbytes(workspace),
                                 _stream(q))
         _check(st, "attn_decode_ex")
         return (out, lse) if return_lse else out
@@ -454,7 +461,7 @@ def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Ten
                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, P, ps,
                                block_table.data_ptr(), mbps, cache_lens.data_ptr(), int(max_cache_len), D,
                                _strides3(q), _strides4(k_pages), _strides4(v_pages), _strides3(out), s, code,
-                               int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(q))
+                               int(num_splits), workspace.data_ptr(), _nbytes(workspace), _stream(q))
     _check(st, "attn_decode_paged")
     return (out, lse) if return_lse else out
 
@@ -517,7 +524,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D,
             _strides4(q), _strides4(k), _strides4(v), _strides4(o), _strides4(dout),
             _strides4(dq), _strides4(dk), _strides4(dv), s)
-    tail = (code, workspace.data_ptr(), workspace.numel(), _stream(q))
+    tail = (code, workspace.data_ptr(), _nbytes(workspace), _stream(q))
     if window is not None:
         _check(lib.attn_bwd_masked(*args, _mask(causal, causal_align, window), *tail), "attn_bwd_masked")
     else:
@@ -577,7 +584,7 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
             B, max_seqlen_q, max_seqlen_k, Tq, Tk, Hq, Hkv, D,
             P(q), P(k), P(v), P(o), P(dout), P(dq), P(dk), P(dv), s)
-    tail = (code, workspace.data_ptr(), workspace.numel(), _stream(q))
+    tail = (code, workspace.data_ptr(), _nbytes(workspace), _stream(q))
     if window is not None:
         _check(lib.attn_bwd_varlen_masked(*args, _mask(causal, causal_align, window), *tail),
                "attn_bwd_varlen_masked")

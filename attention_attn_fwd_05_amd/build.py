@@ -1,4 +1,8 @@
-"""Build libattn.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc."""
+"""Build libattn.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Each source is compiled to an object in its own hipcc process (in parallel),
+then the objects are linked into the shared library.
+"""
 
 from __future__ import annotations
 
@@ -6,6 +10,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -22,22 +28,36 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libattn.so")
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source into attention_attn_fwd_05_amd/libattn.so."""
-    tmp = LIB + ".tmp"
-    cmd = [
-        hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def compile_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-        "-o", tmp,
-    ] + [os.path.join(CSRC, s) for s in SOURCES]
+    ]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+        raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd[-3:])}")
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every HIP source into attention_attn_fwd_05_amd/libattn.so."""
+    hipcc = hipcc_path()
+    flags = compile_flags()
+    with tempfile.TemporaryDirectory(prefix="attn_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hipcc, *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -6,7 +6,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
+#include <initializer_list>
 #include <cmath>
 #include <cstdint>
 
@@ -19,10 +21,7 @@ constexpr int64_t kSmallGridBlocks = 128;  // 256-row grids this small use 128-r
 constexpr int kDecodeTile = 128;   // cache rows per decode tile
 constexpr int kDecodeMaxHeads = 16;
 constexpr int kDecodeMaxSplits = 64;     // partials one combine merges
-#ifndef ATTN_DECODE_TARGET_WGS
-#define ATTN_DECODE_TARGET_WGS 512
-#endif
-constexpr int kDecodeTargetWorkgroups = ATTN_DECODE_TARGET_WGS;  // decode workgroups that fill MI355X (2 per CU)
+constexpr int kDecodeTargetWorkgroups = 512;  // decode workgroups that fill MI355X (2 per CU)
 // with per-sequence lengths, default chunks hold at most this many tiles (768
 // rows): the chunks covering a sequence then number in proportion to its
 // length and the last workgroups to finish hold little work
@@ -35,6 +34,27 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // head-dim stride 1; other strides non-negative multiples of 8 elements (16 bytes)
 inline bool strides_ok(const attn_strides& s) {
   return s.d == 1 && s.b >= 0 && s.h >= 0 && s.n >= 0 && s.b % 8 == 0 && s.h % 8 == 0 && s.n % 8 == 0;
+}
+
+// An output view whose elements are all distinct addresses: taken in order
+// of stride, every dimension of extent > 1 steps at least past the span of
+// the dimensions below it.  Views that alias rows or heads would have several
+// workgroups store to one address, so they are refused rather than raced.
+struct Dim {
+  int64_t extent, stride;
+};
+inline bool writes_once(std::initializer_list<Dim> dims) {
+  Dim d[4];
+  int n = 0;
+  for (const Dim& x : dims)
+    if (x.extent > 1) d[n++] = x;
+  std::sort(d, d + n, [](const Dim& a, const Dim& b) { return a.stride < b.stride; });
+  int64_t span = 1;  // max offset + 1 over the dimensions taken so far
+  for (int i = 0; i < n; ++i) {
+    if (d[i].stride < span) return false;
+    span += (d[i].extent - 1) * d[i].stride;
+  }
+  return true;
 }
 
 inline bool dtype_ok(attn_dtype t) { return t == ATTN_F16 || t == ATTN_BF16; }
@@ -109,6 +129,24 @@ static MaskSpec mask_of(attn_mask m) {
   return MaskSpec{mode, m.align == ATTN_ALIGN_BOTTOM_RIGHT ? 1 : 0, m.window_left, m.window_right};
 }
 
+// Band sides that hide nothing become open (-1), so the mask takes its
+// cheapest mode.  A query's key position p = i + off lies in [Nkv - Nq, Nkv)
+// bottom-right and [0, Nq) top-left, keys in [0, Nkv): with a side of at least
+// reach = max(Nq, Nkv) every key passes that side's test for every query.
+// (Packed batches pass the totals, which bound every sequence's lengths.)
+static MaskSpec open_wide_sides(MaskSpec mk, int64_t reach) {
+  if (mk.mode != 2) return mk;
+  if (mk.left >= reach) mk.left = -1;
+  if (mk.right >= reach) mk.right = -1;
+  mk.mode = (mk.left < 0 && mk.right < 0) ? 0 : (mk.left < 0 && mk.right == 0) ? 1 : 2;
+  return mk;
+}
+
+// The kernels evaluate band bounds as 32-bit sums of a position, a window
+// side (open sides count as 2^30) and a tile offset; sequences up to 2^28 rows
+// keep every such sum inside int32.
+constexpr int64_t kMaxBandRows = int64_t(1) << 28;
+
 static attn_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int Nq, int Nkv, int D,
                             attn_strides sq, attn_strides sk, attn_strides sv, attn_strides so,
@@ -119,7 +157,10 @@ static attn_status fwd_impl(const void* q, const void* k, const void* v, void* o
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
   if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
+  mk = open_wide_sides(mk, Nq > Nkv ? Nq : Nkv);
+  if (mk.mode == 2 && (Nq > kMaxBandRows || Nkv > kMaxBandRows)) return ATTN_ERR_UNSUPPORTED;
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so)) return ATTN_ERR_UNSUPPORTED;
+  if (!writes_once({{B, so.b}, {Hq, so.h}, {Nq, so.n}, {D, 1}})) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
   if (sq.n > kMaxRowStride || sk.n > kMaxRowStride || sv.n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
@@ -196,10 +237,13 @@ static attn_status fwd_varlen_impl(const void* q, const void* k, const void* v, 
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
   if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
+  mk = open_wide_sides(mk, total_q > total_k ? total_q : total_k);
+  if (mk.mode == 2 && (total_q > kMaxBandRows || total_k > kMaxBandRows)) return ATTN_ERR_UNSUPPORTED;
   // packed (token, head, dim) views: the batch stride is unused and not checked
   attn_strides sq3 = sq, sk3 = sk, sv3 = sv, so3 = so;
   sq3.b = sk3.b = sv3.b = so3.b = 0;
   if (!strides_ok(sq3) || !strides_ok(sk3) || !strides_ok(sv3) || !strides_ok(so3)) return ATTN_ERR_UNSUPPORTED;
+  if (!writes_once({{total_q, so.n}, {Hq, so.h}, {D, 1}})) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
@@ -295,6 +339,7 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
   sq3.n = 0;
   so3.n = 0;
   if (!strides_ok(sq3) || !strides_ok(skc) || !strides_ok(svc) || !strides_ok(so3)) return ATTN_ERR_UNSUPPORTED;
+  if (!writes_once({{B, so.b}, {Hq, so.h}, {D, 1}})) return ATTN_ERR_UNSUPPORTED;
   if (skc.n > kMaxRowStride || svc.n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
@@ -449,6 +494,9 @@ attn_status kv_cache_write_paged(void* k_pages, void* v_pages, const void* k_new
   const int lg = page_log2(page_size);
   if (lg < 0 || D % 8 != 0 || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
   if (!strides_ok(skp) || !strides_ok(svp) || !strides_ok(skn) || !strides_ok(svn)) return ATTN_ERR_UNSUPPORTED;
+  if (!writes_once({{num_pages, skp.b}, {Hkv, skp.h}, {page_size, skp.n}, {D, 1}}) ||
+      !writes_once({{num_pages, svp.b}, {Hkv, svp.h}, {page_size, svp.n}, {D, 1}}))
+    return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) || !aligned16(v_new))
     return ATTN_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(pos) & 3u))
@@ -488,8 +536,14 @@ static attn_status bwd_impl(const void* q, const void* k, const void* v, const v
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
   if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
+  mk = open_wide_sides(mk, Nq > Nkv ? Nq : Nkv);
+  if (mk.mode == 2 && (Nq > kMaxBandRows || Nkv > kMaxBandRows)) return ATTN_ERR_UNSUPPORTED;
   for (const attn_strides* st : {&sq, &sk, &sv, &so, &sdo, &sdq, &sdk, &sdv})
     if (!strides_ok(*st) || st->n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
+  if (!writes_once({{B, sdq.b}, {Hq, sdq.h}, {Nq, sdq.n}, {D, 1}}) ||
+      !writes_once({{B, sdk.b}, {Hkv, sdk.h}, {Nkv, sdk.n}, {D, 1}}) ||
+      !writes_once({{B, sdv.b}, {Hkv, sdv.h}, {Nkv, sdv.n}, {D, 1}}))
+    return ATTN_ERR_UNSUPPORTED;
   for (const void* p : {q, k, v, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv)})
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
@@ -556,11 +610,16 @@ static attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, 
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (!dtype_ok(dtype) || !std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
   if (mk.mode < 0) return ATTN_ERR_UNSUPPORTED;
+  mk = open_wide_sides(mk, total_q > total_k ? total_q : total_k);
+  if (mk.mode == 2 && (total_q > kMaxBandRows || total_k > kMaxBandRows)) return ATTN_ERR_UNSUPPORTED;
   // packed (token, head, dim) views: the batch stride is unused and not checked
   for (attn_strides* st : {&sq, &sk, &sv, &so, &sdo, &sdq, &sdk, &sdv}) {
     st->b = 0;
     if (!strides_ok(*st) || st->n > kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
   }
+  if (!writes_once({{total_q, sdq.n}, {Hq, sdq.h}, {D, 1}}) || !writes_once({{total_k, sdk.n}, {Hkv, sdk.h}, {D, 1}}) ||
+      !writes_once({{total_k, sdv.n}, {Hkv, sdv.h}, {D, 1}}))
+    return ATTN_ERR_UNSUPPORTED;
   for (const void* p : {q, k, v, o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv)})
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
@@ -667,6 +726,9 @@ attn_status kv_cache_write(void* k_cache, void* v_cache, const void* k_new, cons
   if (pos < 0 || (int64_t)pos + T > S_max) return ATTN_ERR_SHAPE;
   if (D % 8 != 0 || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
   if (!strides_ok(skc) || !strides_ok(svc) || !strides_ok(skn) || !strides_ok(svn)) return ATTN_ERR_UNSUPPORTED;
+  if (!writes_once({{B, skc.b}, {Hkv, skc.h}, {S_max, skc.n}, {D, 1}}) ||
+      !writes_once({{B, svc.b}, {Hkv, svc.h}, {S_max, svc.n}, {D, 1}}))
+    return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return ATTN_ERR_UNSUPPORTED;
 

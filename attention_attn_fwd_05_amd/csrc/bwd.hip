@@ -46,16 +46,10 @@ constexpr int kKvW = 8;           // waves per dkdv workgroup (two per SIMD)
 constexpr int kKvRows = 128;      // keys per dkdv workgroup (32 per wave pair)
 constexpr int kBT = 64;           // streamed rows per LDS tile
 constexpr int kBStages = 3;      // LDS ring depth
-#ifndef ATTN_BWD_Q_PF
-#define ATTN_BWD_Q_PF 1  // dQ pass: k-steps of K/V reads in flight ahead of its S, dP MFMAs (>= 1)
-#endif
-#ifndef ATTN_BWD_KV_GPF
-#define ATTN_BWD_KV_GPF 1  // dK/dV pass: steps of transposing reads in flight ahead of its dV, dK MFMAs (>= 1)
-#endif
-#ifndef ATTN_BWD_KV_PF
-#define ATTN_BWD_KV_PF 1  // dK/dV pass: k-steps of operand reads in flight ahead of its S, dP MFMAs (>= 1)
-#endif
-static_assert(ATTN_BWD_Q_PF >= 1 && ATTN_BWD_KV_PF >= 1 && ATTN_BWD_KV_GPF >= 1, "pipeline depths are at least one step");
+// software-pipeline depths: steps of LDS operand reads in flight ahead of the MFMAs that use them
+constexpr int kDqReadAhead = 1;    // dQ pass: K/V reads ahead of its S, dP MFMAs
+constexpr int kKvReadAhead = 1;    // dK/dV pass: operand reads ahead of its S, dP MFMAs
+constexpr int kKvTrReadAhead = 1;  // dK/dV pass: transposing reads ahead of its dV, dK MFMAs
 
 // ---- lse * log2(e) and delta = rowsum(dO * O) per query row, fp32 pairs
 template <int D, bool BF16>
@@ -296,7 +290,7 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
       {
         // software pipeline: k-step ks + PF's K and V reads go out before
         // k-step ks's two MFMAs; the fences keep them there
-        constexpr int PF = ATTN_BWD_Q_PF;
+        constexpr int PF = kDqReadAhead;
         u32x4 opk[PF + 1], opv[PF + 1];
         auto issue = [&](int ks) __attribute__((always_inline)) {
           opk[ks % (PF + 1)] = lds_load16(ka[ks] + so);
@@ -536,7 +530,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     // software pipeline: the four operand reads of k-step ks + PF go out before
     // k-step ks's two MFMAs (a loaded LDS read takes some 250 cycles); the
     // scheduling fences keep the compiler from sinking them next to their use
-    constexpr int PF = ATTN_BWD_KV_PF;
+    constexpr int PF = kKvReadAhead;
     u32x4 opq[PF + 1], opk[PF + 1], opg[PF + 1], opv[PF + 1];
     auto issue = [&](int ks) __attribute__((always_inline)) {
       const int r = ks % (PF + 1);
@@ -590,7 +584,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     {
       // the same software pipeline over the 2 x DT steps (kk, dt), four
       // transposing reads a step
-      constexpr int GP = ATTN_BWD_KV_GPF, NS = 2 * DT;
+      constexpr int GP = kKvTrReadAhead, NS = 2 * DT;
       u32x4 opg[GP + 1], opq[GP + 1];
       auto issue = [&](int i) __attribute__((always_inline)) {
         const int r = i % (GP + 1), kk = i / DT, dt = i % DT;

@@ -39,9 +39,7 @@ namespace attn {
 namespace {
 
 constexpr int kDT = 128;        // keys per tile (32 per wave)
-#ifndef ATTN_DECODE_WAVES_PER_SIMD
-#define ATTN_DECODE_WAVES_PER_SIMD 2  // workgroups per CU the register budget is sized for
-#endif
+constexpr int kDecodeWgsPerCu = 2;  // workgroups per CU the register budget is sized for
 constexpr int kMaxSplits = 64;  // partials merged by one combine (the host keeps nsplit <= this)
 constexpr int kPartPad = 4;     // per-head partial: m, l, 2 pad, o[D] -> 16-byte aligned o
 
@@ -53,7 +51,7 @@ __device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
 // lengths over a paged cache.  WINDOW: a sliding window hides the slots before
 // len - 1 - window_left (without it none of that code is compiled in)
 template <int D, bool BF16, int MODE, bool WINDOW>
-__global__ __launch_bounds__(256, ATTN_DECODE_WAVES_PER_SIMD) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const DecodeArgs a) {
   constexpr bool VARLEN = MODE >= 1;
   constexpr bool PAGED = MODE == 2;
   constexpr int KS = D / 32;                 // k-steps of the score MFMA

@@ -49,28 +49,14 @@ namespace attn {
 
 namespace {
 
-#ifndef ATTN_PF_STAGES
-#define ATTN_PF_STAGES 4
-#endif
-constexpr int kStages = ATTN_PF_STAGES;  // LDS ring depth (tiles in flight + 1)
-static_assert(kStages == 3 || kStages == 4, "the KV loop cycles three or four stages");
+constexpr int kStages = 4;           // LDS ring depth (tiles in flight + 1)
 constexpr int kBN = 64;              // key rows per LDS tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
-#ifndef ATTN_PF_SCHED
-#define ATTN_PF_SCHED 1   // apply the instruction order hints below
-#endif
-#ifndef ATTN_PF_KLEAD
-#define ATTN_PF_KLEAD 4   // K fragment reads issued before the first score MFMA
-#endif
-#ifndef ATTN_PF_VLEAD
-#define ATTN_PF_VLEAD 2   // V^T fragments (2 reads each) issued before the first P.V MFMA
-#endif
-#ifndef ATTN_PF_VALU0
-#define ATTN_PF_VALU0 40  // softmax vector instructions before the first P.V MFMA
-#endif
-#ifndef ATTN_PF_VALU1
-#define ATTN_PF_VALU1 5   // softmax vector instructions after each P.V MFMA
-#endif
+// instruction order hints of a tile's two MFMA phases
+constexpr int kKLead = 4;   // K fragment reads issued before the first score MFMA
+constexpr int kVLead = 2;   // V^T fragments (2 reads each) issued before the first P.V MFMA
+constexpr int kValu0 = 40;  // softmax vector instructions before the first P.V MFMA
+constexpr int kValu1 = 5;   // softmax vector instructions after each P.V MFMA
 
 // LDS ring: the V tiles of all stages first, then the K tiles, so that every
 // V^T read is its wave's base address plus an immediate below 64 KiB
@@ -263,26 +249,22 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
   // MFMA, 0x100 LDS read, 0x002 VALU): LDS reads run several MFMAs ahead of
   // their use, since a loaded LDS read takes some 250 cycles
   auto schedule_scores = [&]() __attribute__((always_inline)) {
-#if ATTN_PF_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, ATTN_PF_KLEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kKLead, 0);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-#endif
   };
   auto schedule_pv = [&]() __attribute__((always_inline)) {
-#if ATTN_PF_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * ATTN_PF_VLEAD, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, ATTN_PF_VALU0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVLead, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu0, 0);
 #pragma unroll
     for (int i = 0; i < 4 * DT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, ATTN_PF_VALU1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu1, 0);
     }
-#endif
   };
 
   auto compute = [&](auto stage_tag, int t, auto masked_tag) {

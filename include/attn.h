@@ -18,7 +18,11 @@
  *     rows in 16-byte vectors.  Row (sequence / cache slot) strides are at
  *     most 2^22 elements: a tile's rows are addressed with 32-bit offsets from
  *     its first row (base and row offsets themselves are 64-bit, so tensors
- *     and offsets beyond 2^31 bytes are fine).  Violations return
+ *     and offsets beyond 2^31 bytes are fine).  Output views (o, dq, dk, dv,
+ *     the caches and page pools written) must address every element once:
+ *     ordered by stride, each dimension of extent > 1 steps past the whole
+ *     span of the smaller ones (heads or rows that alias would have several
+ *     workgroups race on one address).  Violations return
  *     ATTN_ERR_UNSUPPORTED.
  *   - Element types: IEEE fp16 or bf16 for Q/K/V/O; scores, softmax state and
  *     accumulators are fp32 inside the kernels ([P1] "Kernel design rules").
@@ -76,6 +80,10 @@ enum {
  * open.  {align, -1, 0} is the causal mask ([P1] step 5c with align top-left),
  * {align, -1, -1} no mask, {align, w - 1, 0} a causal sliding window of w keys
  * ([P1] "Use this when": windowed attention; [P3] deferred scope).
+ * A side of max(Nq, Nkv) or more (packed batches: max(total_q, total_k))
+ * hides no key and is treated as open, INT32_MAX included.  A mask that is
+ * still a band after that (neither unmasked nor causal) needs Nq, Nkv (packed:
+ * total_q, total_k) <= 2^28; longer sequences give ATTN_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t align;         /* ATTN_ALIGN_TOP_LEFT or ATTN_ALIGN_BOTTOM_RIGHT */

@@ -44,9 +44,17 @@ def check_lse(gpu: torch.Tensor, ref: np.ndarray, what: str = "lse"):
     return float(ratio.max())
 
 
+WAVE_ROWS = 32  # query rows one prefill wave owns
+
+
 def sample_rows(N: int, causal: bool, rng: np.random.Generator, count: int = 24) -> np.ndarray:
-    """Query rows to compare at full size: both ends, tile edges, and random rows."""
+    """Query rows to compare at full size: both ends, tile edges, random rows,
+    and one random row in every 32-row slice, so that every wave of every
+    query block of the launch is compared element by element."""
     fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
     rnd = rng.integers(0, N, size=max(0, count - len(fixed)))
-    rows = np.unique(np.clip(np.concatenate([fixed, rnd]), 0, N - 1))
+    starts = np.arange(0, N, WAVE_ROWS)
+    per_slice = starts + rng.integers(0, WAVE_ROWS, size=starts.size)
+    rows = np.unique(np.clip(np.concatenate([fixed, rnd, per_slice]), 0, N - 1))
+    assert set((rows // WAVE_ROWS).tolist()) == set(range((N + WAVE_ROWS - 1) // WAVE_ROWS))
     return rows

@@ -107,6 +107,30 @@ def pin_rows_sum_to_one():
             assert (P[..., j <= i] > 0).all()
 
 
+def pin_probs_head_mapping():
+    """attention_probs maps q head h to kv head h // (Hq / Hkv): with every key
+    of kv head 1 equal, the q heads of its group see equal scores, so their
+    rows are uniform over the visible keys (1 / n_visible), while the group of
+    kv head 0 (distinct keys) is not; and P V reproduces attention_forward's O."""
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, N, D = 2, 6, 3, 11, 8
+    q, k, v = _rand(rng, B, Hq, N, D), _rand(rng, B, Hkv, N, D), _rand(rng, B, Hkv, N, D)
+    k[:, 1] = k[:, 1, :1]  # kv head 1: one key repeated
+    for causal in (False, True):
+        P = OA.attention_probs(q, k, 0.41, causal)
+        n_vis = (np.arange(N)[:, None] + 1) if causal else np.full((N, 1), N)
+        vis = (np.arange(N)[None, :] <= np.arange(N)[:, None]) if causal else np.ones((N, N), bool)
+        uniform = np.where(vis, 1.0 / n_vis, 0.0)
+        for h in range(Hq):
+            if h // 2 == 1:
+                np.testing.assert_allclose(P[:, h], np.broadcast_to(uniform, (B, N, N)), rtol=0, atol=1e-14)
+            else:
+                assert np.abs(P[:, h, -1] - uniform[-1]).max() > 1e-3, h
+        O, _ = OA.attention_forward(q, k, v, 0.41, causal)
+        kvh = np.arange(Hq) // (Hq // Hkv)
+        np.testing.assert_allclose(np.einsum("bhij,bhjd->bhid", P, v[:, kvh]), O, rtol=0, atol=1e-12)
+
+
 def pin_causal_row0_is_v0():
     """P2: with top-left causal masking row 0 sees key 0 only: O = V[0] exactly."""
     rng = np.random.default_rng(2)
@@ -598,6 +622,7 @@ ALL_PINS = [
     pin_golden_decode,
     pin_golden_cache_write,
     pin_rows_sum_to_one,
+    pin_probs_head_mapping,
     pin_causal_row0_is_v0,
     pin_equal_scores_give_mean,
     pin_single_key,

@@ -79,7 +79,7 @@ def fwd(lib, **kw):
     (dict(sq=S(8320, 4160, 64, 2)), UNSUP), (dict(sk=S(4160, 4160, 60, 1)), UNSUP),
     (dict(so=S(-8, 4160, 64, 1)), UNSUP),
     (dict(q=FAKE + 2), UNSUP), (dict(o=FAKE + 8), UNSUP), (dict(lse=FAKE + 2), UNSUP),
-    (dict(B=1 << 20, Nq=1 << 30, Hq=64, Hkv=1), SHAPE),
+    (dict(B=1 << 20, Nq=1 << 30, Hq=64, Hkv=1, so=c4(64, 1 << 30, 64)), SHAPE),
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -154,6 +154,19 @@ def test_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
 
 
+def bwdm(lib, mask, **kw):
+    B, Hq, Hkv, N, D = 1, 4, 2, 300, 128
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=B, Hq=Hq, Hkv=Hkv,
+             Nq=N, Nkv=N, D=D, sq=c4(D, N, Hq), sk=c4(D, N, Hkv), sv=c4(D, N, Hkv), so=c4(D, N, Hq),
+             sdo=c4(D, N, Hq), sdq=c4(D, N, Hq), sdk=c4(D, N, Hkv), sdv=c4(D, N, Hkv), scale=0.088,
+             dtype=0, ws=FAKE, ws_bytes=lib.attn_bwd_workspace_bytes(B, Hq, N), stream=None)
+    a.update(kw)
+    return lib.attn_bwd_masked(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                               a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["D"], a["sq"], a["sk"], a["sv"], a["so"],
+                               a["sdo"], a["sdq"], a["sdk"], a["sdv"], a["scale"], bd.Mask(*mask), a["dtype"], a["ws"],
+                               a["ws_bytes"], a["stream"])
+
+
 def test_bwd_workspace_bytes(lib):
     assert lib.attn_bwd_workspace_bytes(2, 32, 8192) == 2 * 32 * 8192 * 8
     assert lib.attn_bwd_workspace_bytes(0, 1, 1) == 0
@@ -212,7 +225,7 @@ def fwdv(lib, **kw):
     (dict(cq=FAKE + 2), UNSUP), (dict(ck=FAKE + 1), UNSUP), (dict(lse=FAKE + 2), UNSUP), (dict(k=FAKE + 8), UNSUP),
     (dict(sq=S(0, 128, 1024, 2)), UNSUP), (dict(sk=S(0, 128, 260, 1)), UNSUP),
     (dict(sv=S(0, 128, 1 << 23, 1)), UNSUP),
-    (dict(B=1 << 30, Hkv=8, Hq=64, msq=1 << 20), SHAPE),
+    (dict(B=1 << 30, Hkv=8, Hq=64, msq=1 << 20, so=S(0, 128, 64 * 128, 1)), SHAPE),
 ])
 def test_fwd_varlen_rejects(lib, kw, code):
     assert fwdv(lib, **kw) == code
@@ -326,6 +339,56 @@ def cw(lib, **kw):
 ])
 def test_cache_write_rejects(lib, kw, code):
     assert cw(lib, **kw) == code
+
+
+INT_MAX = (1 << 31) - 1
+
+
+@pytest.mark.parametrize("call,kw", [
+    # q heads of o alias each other (head stride 0), rows overlap (row stride < D)
+    ("fwd", dict(so=S(8320, 0, 64, 1))), ("fwd", dict(so=S(8320, 4160, 32, 1))),
+    ("fwdm", dict(so=S(8320, 0, 64, 1))),
+    ("fwdv", dict(so=S(0, 128, 512, 1))),             # 8 heads x 128 in a 512-element token row
+    ("dec", dict(so=S(0, 128, 0, 1))),                # two batch elements on one address
+    ("dec", dict(so=S(32 * 128, 64, 0, 1))),          # heads overlap
+    ("bwd", dict(sdq=S(0, 100 * 128, 128, 1))), ("bwd", dict(sdk=S(76800, 128 * 8, 64, 1))),
+    ("bwd", dict(sdv=S(76800, 0, 128, 1))),
+    ("bwdv", dict(sdk=S(0, 0, 128, 1))),
+    ("cw", dict(skc=S(0, 64 * 128, 128, 1))), ("cw", dict(svc=S(8 * 64 * 128, 64 * 128, 64, 1))),
+    ("cwp", dict(skp=S(16 * 128 * 8, 16 * 128, 0, 1))),
+])
+def test_aliasing_outputs_rejected(lib, call, kw):
+    """An output view that maps two elements to one address would have several
+    workgroups race on it: refused before anything is launched."""
+    fn = {"fwd": fwd, "fwdm": fwdm, "fwdv": fwdv, "dec": dec, "bwd": bwd, "bwdv": bwdv, "cw": cw, "cwp": cwp}[call]
+    assert fn(lib, **kw) == UNSUP
+
+
+def test_band_size_limit(lib):
+    """Band masks are evaluated in 32-bit sums of positions and window sides:
+    sequences past 2^28 rows are refused (forward and backward, dense and packed)."""
+    big = (1 << 28) + 1
+    assert fwdm(lib, (0, 100, 3), Nq=big, Nkv=65) == UNSUP
+    assert fwdm(lib, (1, 100, 3), Nq=65, Nkv=big) == UNSUP
+    assert bwdm(lib, (0, 7, 7), Nq=big) == UNSUP
+    assert bwdv(lib, mask=(1, 100, 0), tk=big) == UNSUP
+
+
+def test_wide_window_sides_open(lib):
+    """A window side of max(Nq, Nkv) or more hides no key, so it is opened on
+    the host: with sequences too long for a band, (INT_MAX, INT_MAX) is the
+    unmasked mode and (INT_MAX, 0) the causal one, and the call proceeds to its
+    next check (here the grid-size bound, ERR_SHAPE) instead of being refused
+    as an oversize band."""
+    big = (1 << 28) + 1
+    huge = dict(B=1 << 20, Hq=64, Hkv=1, Nq=big, Nkv=big, sq=c4(64, big, 64), so=c4(64, big, 64),
+                sk=c4(64, big, 1), sv=c4(64, big, 1))
+    assert fwdm(lib, (0, 100, 3), **huge) == UNSUP               # a real band: too long
+    assert fwdm(lib, (0, INT_MAX, INT_MAX), **huge) == SHAPE     # no mask
+    assert fwdm(lib, (1, INT_MAX, 0), **huge) == SHAPE           # causal
+    assert fwdm(lib, (1, -1, INT_MAX), **huge) == SHAPE          # no mask
+    assert fwdm(lib, (0, big, big), **huge) == SHAPE             # exactly the reach
+    assert fwdm(lib, (0, big - 1, big), **huge) == UNSUP         # one short on the left: still a band
 
 
 def test_workspace_bytes(lib):

@@ -1,7 +1,7 @@
 """GPU parity of attn_bwd (dQ, dK, dV) against the fp64 oracle.
 
 The GPU backward takes the GPU forward's O and lse, as a training step would.
-Tolerance, per gradient tensor X: max|X_gpu - X_oracle| <= 16 u max|X_oracle|
+Tolerance, per gradient tensor X: max|X_gpu - X_oracle| <= 4 u max|X_oracle|
 + floor, u = 2^-11 (fp16) or 2^-8 (bf16).  Each gradient element is a sum of
 products in which one factor was rounded once to 16 bits (P for dV, dS for dQ
 and dK), and delta comes from the forward's 16-bit O; the rows of dS sum to
@@ -11,7 +11,8 @@ element.  The floor covers the fp32 rounding of dP - delta (two sums of D
 products, each at most max|dO| max|V|) carried into dQ (dK) by one more
 product with scale K (Q) per key (query): 2^-24 D N max|dO| max|V| |scale|
 max|K| (resp. max|Q|); it matters only where the exact gradient is 0 (one key:
-dS = 0).
+dS = 0).  Under an earlier bound of 16 u the largest error any backward test
+measured was 8 % of it, 1.3 u max|X|; 4 u leaves a factor of about 3.
 """
 
 from __future__ import annotations
@@ -27,6 +28,7 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 U = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+TOL_U = 4  # multiples of u * max|X_oracle|
 
 
 def _say(msg):
@@ -46,7 +48,7 @@ def _check(name, got, ref, dtype, floor=0.0):
     assert np.isfinite(g).all(), f"{name}: non-finite values"
     err = float(np.abs(g - ref).max())
     scale = float(np.abs(ref).max())
-    tol = 16 * U[dtype] * scale + floor
+    tol = TOL_U * U[dtype] * scale + floor
     print(f"    {name}: max|err| = {err:.3e}, max|ref| = {scale:.3e}, err/tol = {err / tol:.3f}", flush=True)
     assert err <= tol, f"{name}: max|err| {err:.3e} > {tol:.3e}"
 
@@ -106,6 +108,10 @@ BWD_BANDS = [
     ("chunk_window", 300, 1500, 128, "fp16", True, "bottom_right", (511, -1)),
     ("left_only_br", 400, 900, 64, "fp16", False, "bottom_right", (200, -1)),
     ("right_only", 500, 500, 128, "bf16", False, "top_left", (-1, 64)),
+    # window sides at INT32_MAX: opened on the host (they reach past every key)
+    ("right_side_int_max", 300, 700, 128, "fp16", False, "top_left", (-1, 2 ** 31 - 1)),
+    ("br_left_int_max_q_longer", 700, 300, 128, "fp16", True, "bottom_right", (2 ** 31 - 1, -1)),
+    ("left_int_max_right_5", 500, 500, 64, "bf16", False, "top_left", (2 ** 31 - 1, 5)),
 ]
 
 

@@ -53,6 +53,11 @@ BANDS = [
     ("left_only_br", 1, 4, 2, 400, 900, 64, "fp16", "bottom_right", False, (200, -1)),
     ("ragged_small_window", 1, 4, 4, 1, 129, 128, "bf16", "bottom_right", True, (3, -1)),
     ("q_longer_than_k", 1, 4, 2, 700, 300, 128, "fp16", "bottom_right", True, (64, -1)),
+    # window sides at INT32_MAX: opened on the host (they reach past every key)
+    ("right_side_int_max", 1, 4, 2, 300, 700, 128, "fp16", "top_left", False, (-1, 2 ** 31 - 1)),
+    ("br_left_int_max_q_longer", 1, 4, 2, 700, 300, 128, "fp16", "bottom_right", True, (2 ** 31 - 1, -1)),
+    ("both_sides_int_max", 1, 4, 4, 257, 513, 64, "bf16", "bottom_right", False, (2 ** 31 - 1, 2 ** 31 - 1)),
+    ("left_int_max_right_5", 1, 4, 2, 500, 500, 128, "fp16", "top_left", False, (2 ** 31 - 1, 5)),
 ]
 
 

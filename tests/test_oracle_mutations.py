@@ -180,6 +180,18 @@ def _write_shifted(k_cache, v_cache, k_new, v_new, pos):
     return kc, vc
 
 
+def _probs_heads_tiled(q, k, scale, causal, causal_offset=0):
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    B, Hq, Nq, _ = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, Nq, Nkv))
+    vis = OA.visibility(np.arange(Nq), Nkv, causal, causal_offset)
+    for b in range(B):
+        for h in range(Hq):
+            out[b, h], _ = OA._masked_softmax(OA._scores(q[b, h], k[b, h % Hkv], scale), vis)
+    return out
+
+
 MUTATIONS = {
     "causal_strict_lt": ("visibility", _vis_strict),
     "causal_ignored": ("visibility", _vis_no_causal),
@@ -190,6 +202,7 @@ MUTATIONS = {
     "window_left_one_short": ("visibility", _vis_window_left_strict),
     "window_sides_swapped": ("visibility", _vis_window_sides_swapped),
     "gqa_tiled_heads": ("kv_head_of", _kv_head_tiled),
+    "probs_heads_tiled": ("attention_probs", _probs_heads_tiled),
     "scale_dropped": ("_scores", _scores_unscaled),
     "scale_twice": ("_scores", _scores_scaled_twice),
     "lse_missing_log_l": ("_masked_softmax", _soft_lse_is_max),
