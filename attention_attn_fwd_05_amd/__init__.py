@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
   form takes ``window_left``, through attn_decode_ex)
 * ``attn_decode_varlen(q, k_cache, v_cache, cache_lens, max_cache_len=None, ...)``
   (one cache length per sequence, read on the device)
+* ``attn_decode_noalloc(q, k_cache, v_cache, cache_len, *, out, lse=None, ...)``
+  (attn_decode with the library's own fixed scratch: allocates nothing)
 * ``attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D)`` /
   ``decode_workspace(...)`` (a uint8 scratch tensor of that size)
 * ``kv_cache_write(k_cache, v_cache, k_new, v_new, pos)``
@@ -36,6 +38,7 @@ from ._binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_varlen,
     attn_decode,
+    attn_decode_noalloc,
     attn_decode_paged,
     attn_decode_varlen,
     attn_decode_workspace_bytes,
@@ -56,6 +59,7 @@ __all__ = [
     "attn_bwd_varlen",
     "attn_fwd_varlen",
     "attn_decode",
+    "attn_decode_noalloc",
     "attn_decode_varlen",
     "attn_decode_paged",
     "kv_cache_write_paged",

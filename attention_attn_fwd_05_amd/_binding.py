@@ -77,6 +77,9 @@ def load_library():
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32,
                                 vp, ctypes.c_size_t, vp]
     lib.attn_decode.restype = i32
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, S, S, S, S, f32, i32, i32,
+                                        vp]
+    lib.attn_decode_noalloc.restype = i32
     lib.attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, i32, S, S, S, S, f32, i32,
                                        i32, vp, ctypes.c_size_t, vp]
     lib.attn_decode_varlen.restype = i32
@@ -337,6 +340,30 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, c
                          _stream(q))
     _check(st, "attn_decode")
     return (out, lse) if return_lse else out
+
+
+def attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: int, *,
+                        scale: float | None = None, num_splits: int = 0, out: torch.Tensor,
+                        lse: torch.Tensor | None = None):
+    """attn_decode without a workspace: the split partials go to the library's
+    own fixed scratch, so the call allocates nothing (``out`` and ``lse`` are
+    the caller's).  Calls that may overlap on one GPU must be serialised."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if lse is not None and (lse.shape != (B, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq)")
+    _on_gpu(q, k_cache, v_cache, out, *([lse] if lse is not None else []))
+    code = _dtype_code(q, k_cache, v_cache, out)
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, caches and out")
+    s = _default_scale(D) if scale is None else float(scale)
+    st = lib.attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None, B, Hq, Hkv, S_max, int(cache_len), D,
+                                 _strides3(q), _strides4(k_cache), _strides4(v_cache), _strides3(out), s, code,
+                                 int(num_splits), _stream(q))
+    _check(st, "attn_decode_noalloc")
+    return out
 
 
 def attn_decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_lens: torch.Tensor,

@@ -328,7 +328,7 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
                         attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
                         float scale, attn_dtype dtype, int num_splits,
                         void* workspace, size_t workspace_bytes, void* stream, const PagedSpec* pg = nullptr,
-                        int window_left = -1) {
+                        int window_left = -1, bool use_scratch = false) {
   if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0 || cache_len < 1 || cache_len > S_max || num_splits < 0) return ATTN_ERR_SHAPE;
@@ -345,7 +345,7 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_UNSUPPORTED;
   if (lens && (reinterpret_cast<uintptr_t>(lens) & 3u)) return ATTN_ERR_UNSUPPORTED;
   const DecodeGeometry g = decode_geometry(B, Hq, Hkv, S_max, D);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < g.part_bytes)
+  if (!use_scratch && (!workspace || !aligned16(workspace) || workspace_bytes < g.part_bytes))
     return ATTN_ERR_WORKSPACE;
   // B * Hkv goes in grid x (limit 2^31 - 1) or z (limit 65535); head groups in y
   if ((int64_t)B * Hkv > 0x7fffffff || g.hgroups > 65535) return ATTN_ERR_SHAPE;
@@ -400,6 +400,18 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
   a.c = score_coef(scale);
   a.qsign = q_sign_mask(scale);
   a.part = static_cast<float*>(workspace);
+  if (use_scratch) {
+    // the library's scratch holds exactly this call's partials: nsplit slots
+    // per (batch, kv head, head group) rather than the workspace's max_splits
+    a.max_splits = nsplit;
+    const size_t need = nsplit > 1 ? (size_t)slots * nsplit * g.heads_per_wg * (size_t)(D + kDecodePartPad) *
+                                         sizeof(float)
+                                   : 0;
+    if (need > ATTN_DECODE_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+    void* p = nullptr;
+    if (attn::decode_scratch_address(static_cast<hipStream_t>(stream), &p) != hipSuccess) return ATTN_ERR_HIP;
+    a.part = static_cast<float*>(p);
+  }
   a.window_left = window_left;
   if (pg) {
     a.block_table = pg->table;
@@ -421,6 +433,14 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, cache_len, nullptr, D, sq, skc, svc, so,
                      scale, dtype, num_splits, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+                                attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
+                                float scale, attn_dtype dtype, int num_splits, void* stream) {
+  return decode_impl(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, cache_len, nullptr, D, sq, skc, svc, so,
+                     scale, dtype, num_splits, nullptr, 0, stream, nullptr, -1, true);
 }
 
 attn_status attn_decode_varlen(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

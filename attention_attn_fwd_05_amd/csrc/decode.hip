@@ -31,6 +31,10 @@
 //     which the last workgroup to finish merges measured slower on MI355X:
 //     device-coherent publication costs every workgroup a store drain and an
 //     atomic, more than the second launch costs.)
+#include <atomic>
+#include <mutex>
+
+#include "attn.h"
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
@@ -507,7 +511,47 @@ __global__ __launch_bounds__(256) void cache_write_paged_kernel(const CacheWrite
   }
 }
 
+// ---- the split partials of attn_decode_noalloc, for callers that cannot
+//      allocate: a fixed array in the library's own device memory, one copy
+//      per GPU, held until the process ends.  Every such call on a GPU uses
+//      that GPU's copy (calls that overlap on one GPU race on it).  Each call
+//      writes every partial its combine reads, so nothing needs clearing.
+static __device__ __align__(256) uint8_t scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;  // devices whose scratch address is remembered
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
+
+hipError_t decode_scratch_address(hipStream_t stream, void** addr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      // the symbol's address on `dev`, looked up with `dev` current (each GPU
+      // holds its own copy of the array at its own address); host code uses
+      // only this address, never the array's name
+      int cur = 0;
+      e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+      if (e != hipSuccess) return e;
+      if (e2 != hipSuccess) return e2;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_cache_write_paged(const CacheWritePagedArgs& a, hipStream_t stream) {
   const int64_t work = 2 * a.rows * (a.D / 8);

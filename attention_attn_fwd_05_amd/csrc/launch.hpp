@@ -78,6 +78,11 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, bool bf16, hipStream_t stream);
 
+// Device address of the library's own decode scratch (ATTN_DECODE_NOALLOC_SCRATCH_BYTES
+// bytes) on the device `stream` runs on (the current device for a null stream),
+// looked up once per device and kept.  Allocates nothing.
+hipError_t decode_scratch_address(hipStream_t stream, void** addr);
+
 struct CacheWritePagedArgs {
   uint16_t* kp;
   uint16_t* vp;

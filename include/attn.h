@@ -294,6 +294,32 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, allocation-free serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, with the split partials
+ * kept in a fixed scratch array inside the library instead of a caller's
+ * workspace.  No allocation happens in this call or in the library.
+ *
+ *   Arguments, layouts, results and errors as attn_decode (no workspace).
+ *   Scratch: ATTN_DECODE_NOALLOC_SCRATCH_BYTES per GPU, in the library's device
+ *   memory, held until the process ends.  A call whose partials, B * Hkv *
+ *   ceil(G/16) * n * ceil(G/ceil(G/16)) * (D + 4) * 4 bytes for its n > 1
+ *   chunks (G = Hq / Hkv; none when n = 1), exceed it returns
+ *   ATTN_ERR_WORKSPACE and launches nothing.  At the default split count
+ *   (num_splits = 0: fewer than 1024 chunks in all) the partials stay below
+ *   8.7 MB and always fit; only a forced num_splits can exceed the scratch.
+ *   Every call on a GPU shares that GPU's scratch: calls that may overlap on
+ *   one GPU (different streams, or host threads) race and must be serialised
+ *   by the caller.  The first call on a device looks up the scratch's address
+ *   there (with that device current) and keeps it.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                int B, int Hq, int Hkv, int S_max, int cache_len, int D,
+                                attn_strides sq, attn_strides skc, attn_strides svc, attn_strides so,
+                                float scale, attn_dtype dtype, int num_splits, void* stream);
+
+/*
  * attn_decode_varlen -- attn_decode with a length per sequence: batch element
  * b attends to its cache slots [0, cache_lens[b]).  Per-sequence lengths are
  * the first item of [P3]'s deferred scope ("Out of scope for now": decode for

@@ -44,6 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_masked", "attn_fwd_varlen", "attn_fwd_varlen_masked", "attn_decode",
                           "attn_decode_varlen", "attn_decode_paged", "attn_decode_ex", "attn_decode_workspace_bytes",
+                          "attn_decode_noalloc",
                           "kv_cache_write", "kv_cache_write_paged", "attn_bwd", "attn_bwd_masked", "attn_bwd_varlen",
                           "attn_bwd_varlen_masked", "attn_bwd_workspace_bytes", "attn_status_string"}
     for n in names:
@@ -254,6 +255,30 @@ def dec(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, code):
     assert dec(lib, **kw) == code
+
+
+def decna(lib, **kw):
+    B, Hq, Hkv, Smax, D = 2, 32, 8, 8192, 128
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, B=B, Hq=Hq, Hkv=Hkv, S_max=Smax, cache_len=100, D=D,
+             sq=S(Hq * D, D, 0, 1), skc=c4(D, Smax, Hkv), svc=c4(D, Smax, Hkv), so=S(Hq * D, D, 0, 1),
+             scale=0.088, dtype=0, num_splits=0, stream=None)
+    a.update(kw)
+    return lib.attn_decode_noalloc(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                   a["S_max"], a["cache_len"], a["D"], a["sq"], a["skc"], a["svc"], a["so"],
+                                   a["scale"], a["dtype"], a["num_splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(cache_len=0), SHAPE), (dict(Hq=30), SHAPE),
+    (dict(num_splits=-1), SHAPE), (dict(D=80), UNSUP), (dict(so=S(0, 128, 0, 1)), UNSUP),
+    # 64 x 64 (batch, kv head) units x 64 forced chunks x 132 floats = 138 MB of partials > 16 MiB
+    (dict(B=64, Hq=64, Hkv=64, sq=S(64 * 128, 128, 0, 1), so=S(64 * 128, 128, 0, 1), skc=c4(128, 8192, 64),
+          svc=c4(128, 8192, 64), cache_len=8192, num_splits=64), WS),
+])
+def test_decode_noalloc_rejects(lib, kw, code):
+    """The allocation-free decode validates like attn_decode, and refuses a
+    call whose partials exceed its fixed scratch before anything is launched."""
+    assert decna(lib, **kw) == code
 
 
 def decv(lib, **kw):
