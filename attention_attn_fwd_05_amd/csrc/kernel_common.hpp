@@ -139,6 +139,13 @@ __device__ __forceinline__ float to_f32(uint32_t bits16) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + (low half + high half) of a dword holding two bf16 values, summed in
+// fp32 (one v_dot2c_f32_bf16 against (1, 1); the products are exact)
+__device__ __forceinline__ float sum2_bf16(uint32_t two, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, two), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
+                                         false);
+}
+
 // NaN-propagating maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no
 // quieting of its inputs, which matters in a row max over many scores.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }

@@ -49,7 +49,6 @@ namespace attn {
 
 namespace {
 
-constexpr int kStages = 4;           // LDS ring depth (tiles in flight + 1)
 constexpr int kBN = 64;              // key rows per LDS tile
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 // instruction order hints of a tile's two MFMA phases
@@ -58,35 +57,51 @@ constexpr int kVLead = 2;   // V^T fragments (2 reads each) issued before the fi
 constexpr int kValu0 = 40;  // softmax vector instructions before the first P.V MFMA
 constexpr int kValu1 = 5;   // softmax vector instructions after each P.V MFMA
 
-// LDS ring: the V tiles of all stages first, then the K tiles, so that every
-// V^T read is its wave's base address plus an immediate below 64 KiB
-template <int D>
+// One LDS ring of STAGES (K, V) tile pairs: the V tiles of all stages first,
+// then the K tiles, so that every V^T read is its wave's base address plus an
+// immediate below 64 KiB
+template <int D, int STAGES>
 struct PrefillLds {
   static constexpr int C = D / 8;        // 16-byte slots per K/V row
   static constexpr int TILE = kBN * D;   // elements of one K (or V) tile
   static constexpr int V0 = 0;           // V tile of stage s at V0 + s * TILE
-  static constexpr int K0 = kStages * TILE;
-  static constexpr int ELEMS = 2 * kStages * TILE;
-  static_assert(2 * (kStages * TILE) <= 65536, "V^T read offsets fit the 16-bit DS offset");
+  static constexpr int K0 = STAGES * TILE;
+  static constexpr int ELEMS = 2 * STAGES * TILE;
+  static_assert(2 * (STAGES * TILE) <= 65536, "V^T read offsets fit the 16-bit DS offset");
 };
 
+// ring depth: four stages (loads of tile t+3 issued before tile t); two when a
+// workgroup holds two rings of D = 128 tiles (four would need 256 KiB of LDS)
+template <int D, int KVS>
+constexpr int prefill_stages() {
+  return (KVS == 2 && D == 128) ? 2 : 4;
+}
+
 // MASK 0: every key below Nkv; 1: causal (j <= i + off); 2: a band of keys
-// i + off - win_left <= j <= i + off + win_right (either side may be open)
-// WAVES = 8: 256 query rows per workgroup, two waves per SIMD; WAVES = 4: 128
-// rows, for grids too small to fill the chip with 256-row blocks
-template <int D, bool BF16, int MASK, bool VARLEN, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArgs a) {
-  constexpr int kWaves = WAVES;       // waves per workgroup (32 query rows each)
-  constexpr int kBM = 32 * kWaves;    // query rows per workgroup
+// i + off - win_left <= j <= i + off + win_right (either side may be open).
+// RW: row waves, 32 query rows each (RW = 8: 256-row blocks).  KVS: key
+// groups.  With KVS = 2 a workgroup of 8 waves owns 128 rows (RW = 4); waves
+// w and w + 4 share a SIMD and the same 32 rows, and each streams every
+// second key tile of the block's range through a ring of its own, so a grid
+// too small to fill the chip with 256-row blocks still runs two waves per
+// SIMD.  The two groups' (m, l, O) meet in LDS at the end and are merged with
+// the rescale identity of the online softmax.
+template <int D, bool BF16, int MASK, bool VARLEN, int RW, int KVS>
+__global__ __launch_bounds__(64 * RW * KVS, 2) void prefill_fwd_kernel(const FwdArgs a) {
+  constexpr int kWaves = RW * KVS;    // waves per workgroup
+  constexpr int kBM = 32 * RW;        // query rows per workgroup
+  constexpr int kStages = prefill_stages<D, KVS>();
+  static_assert(kStages == 2 || kStages == 4, "the KV loop cycles two or four stages");
+  static_assert(KVS == 1 || KVS == 2, "one or two key groups");
   constexpr bool CAUSAL = MASK == 1;
   constexpr bool BAND = MASK == 2;
-  using L = PrefillLds<D>;
+  using L = PrefillLds<D, kStages>;
   constexpr int KS = D / 16;        // k-steps of the score MFMA
   constexpr int DT = D / 32;        // 32-wide head-dim tiles of O
-  constexpr int NB = L::C / kWaves; // 1 KiB DMA blocks per wave per K (or V) tile
+  constexpr int NB = L::C / RW;     // 1 KiB DMA blocks per wave per K (or V) tile
   static_assert(NB >= 1, "every wave loads at least one block");
   constexpr int RPB = 64 / L::C;    // rows per 1 KiB block
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[KVS * L::ELEMS];
 
   // ---- which (batch, q head, query block) this workgroup owns
   const int bid = blockIdx.x;
@@ -118,7 +133,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave 0..kWaves-1 (uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave 0..kWaves-1 (uniform)
+  const int w = KVS == 1 ? wv : wv % RW;   // row wave: rows 32 w .. 32 w + 31 of the block
+  const int grp = KVS == 1 ? 0 : wv / RW;  // key group
   const int n = lane & 31;   // this lane's query column within the wave
   const int hh = lane >> 5;  // which half of the wave
   const int q0 = qb * kBM;
@@ -200,8 +217,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
     dk[i] = row * (int32_t)a.skn * 2 + 16 * chunk;
     dv[i] = row * (int32_t)a.svn * 2 + 16 * chunk;
   }
-  const uint32_t lds_k = lds_addr(smem + L::K0) + 1024 * NB * w;  // this wave's first block, stage 0
-  const uint32_t lds_v = lds_addr(smem + L::V0) + 1024 * NB * w;
+  uint16_t* const ring = KVS == 1 ? smem : smem + grp * L::ELEMS;  // this key group's ring
+  const uint32_t lds_k = lds_addr(ring + L::K0) + 1024 * NB * w;  // this wave's first block, stage 0
+  const uint32_t lds_v = lds_addr(ring + L::V0) + 1024 * NB * w;
   auto dma_tile = [&](int t, int stage) {
     const int64_t ko = (int64_t)t * kBN * a.skn, vo = (int64_t)t * kBN * a.svn;
     const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(k_bytes - 2 * ko));
@@ -217,7 +235,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
   uint32_t ka[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    ka[ks] = opaque_lds(lds_addr(smem + L::K0) + 2 * (n * D + (((2 * ks + hh) ^ swz<D>(n)) << 3)));
+    ka[ks] = opaque_lds(lds_addr(ring + L::K0) + 2 * (n * D + (((2 * ks + hh) ^ swz<D>(n)) << 3)));
   // V^T operand of P.V via transposed reads: lane (group g = lane/16, i = lane%16)
   // addresses row 8u + 4*(g/2) + i/4 of the 16-key chunk, head dims
   // 32*dt + 16*(g%2) + 4*(i%4) .. +3; read u = 0 / 1 give MFMA k-slots 0-3 / 4-7
@@ -230,7 +248,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
       for (int u = 0; u < 2; ++u) {
         const int row = 8 * u + 4 * (g >> 1) + (i >> 2);
         const int d = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
-        va[dt][u] = opaque_lds(lds_addr(smem + L::V0) + 2 * (row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7))));
+        va[dt][u] = opaque_lds(lds_addr(ring + L::V0) + 2 * (row * D + ((((d >> 3) ^ swz<D>(row)) << 3) | (d & 7))));
       }
   }
 
@@ -241,6 +259,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   float m = -INFINITY;
   float l = 0.f;
+  // bf16 only: this lane's share of the row sum of the P values as rounded for
+  // the P.V MFMA (O is normalised by it; lse uses the fp32 sum l)
+  float lt = 0.f;
   const float c = a.c;  // > 0
   const int wq_hi = q0 + 32 * w + 31 + off;  // last key any of this wave's rows sees
   const int wq_lo = q0 + 32 * w + off;       // band: this wave's first row's position
@@ -349,6 +370,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
       l *= alpha;
+      if constexpr (BF16) lt *= alpha;
       m = m_new;
     }
     const float m_use = (m == -INFINITY) ? 0.f : m;  // rows with nothing visible yet get P = 0
@@ -369,6 +391,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
       pf[2 + (e >> 3)][(e & 7) >> 1] = pack2<BF16>(p2, p3);
     }
     l += rs0 + rs1;
+    if constexpr (BF16) {
+      // a bf16 P carries 8 significant bits and, under the lazy rescale, can
+      // reach 2^8: normalising O by the sum of the rounded values makes O a
+      // convex combination of V rows, so the rounding of a dominant P cancels
+      // between O and its normaliser instead of scaling O by up to 2^-9
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lt = sum2_bf16(pf[kk][j], lt);
+    }
 
     // O^T += V^T P^T : A = V^T from transposed LDS reads, B = P^T from registers
 #pragma unroll
@@ -393,24 +425,29 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
   using st2 = std::integral_constant<int, 2>;
   using st3 = std::integral_constant<int, 3>;
 
-  // ---- KV loop over a kStages-deep LDS ring filled by DMA: the loads of tile
-  //      t + kStages - 1 are issued before tile t is computed, so every tile's
-  //      loads have kStages - 1 tile computations to land.  After computing
-  //      tile t a wave waits until only the loads of tiles past t+1 are
-  //      outstanding (tile t+1 is in LDS), and the barrier publishes it to the
-  //      workgroup; the stage refilled next was last read before that barrier.
-  //      Full tiles go in groups of kStages (stages 0 .. kStages-1); the rest
-  //      (diagonal / key tail) take the masked path.
+  // ---- this key group's tiles: first, first + KVS, ... below ntiles (every
+  //      tile of [t_begin, ntiles) when KVS = 1)
+  const int first = t_begin + grp;
+
+  // ---- KV loop over a kStages-deep LDS ring filled by DMA: the loads of the
+  //      group's tile kStages - 1 steps ahead are issued before tile t is
+  //      computed, so every tile's loads have kStages - 1 tile computations to
+  //      land.  After computing tile t a wave waits until only the loads of the
+  //      group's tiles past its next one are outstanding (the next tile is in
+  //      LDS), and the barrier publishes it to the workgroup; the stage
+  //      refilled next was last read before that barrier.  Full tiles go in
+  //      groups of kStages (stages 0 .. kStages-1); the rest (diagonal / key
+  //      tail / band edges) take the masked path.
   constexpr int NDMA = 2 * NB;  // DMA instructions per wave per tile
-  static_assert((kStages - 2) * NDMA < 64, "vmcnt field");
+  static_assert(kStages == 2 || (kStages - 2) * NDMA < 64, "vmcnt field");
   // s_waitcnt immediate for vmcnt <= vm (gfx9 encoding: vmcnt bits 3:0 and
   // 15:14, expcnt and lgkmcnt left at their maxima, i.e. unconstrained)
   constexpr int kVm1 = 0x0F70 | (NDMA & 15) | ((NDMA >> 4) << 14);
   constexpr int kVm2 = 0x0F70 | ((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14);
-  // wait until tile tt+1 has landed: the tiles issued after it are
-  // min(kStages - 2, ntiles - tt - 2)
+  // wait until the group's tile after tt has landed: the tiles issued after
+  // it are the group's tiles from tt + 2 KVS on, at most kStages - 2
   auto wait_next = [&](int tt) __attribute__((always_inline)) {
-    const int ahead = min(kStages - 2, max(0, ntiles - tt - 2));
+    const int ahead = min(kStages - 2, max(0, ntiles - tt - 2 * KVS + KVS - 1) / KVS);
     if (kStages == 4 && ahead >= 2)
       __builtin_amdgcn_s_waitcnt(kVm2);
     else if (ahead >= 1)
@@ -420,52 +457,97 @@ __global__ __launch_bounds__(64 * WAVES, 2) void prefill_fwd_kernel(const FwdArg
   };
   auto step = [&](int tt, auto stage_tag, auto masked_tag) {
     constexpr int STG = decltype(stage_tag)::value;
-    if (tt + kStages - 1 < ntiles) dma_tile(tt + kStages - 1, (STG + kStages - 1) % kStages);
+    if (tt + KVS * (kStages - 1) < ntiles) dma_tile(tt + KVS * (kStages - 1), (STG + kStages - 1) % kStages);
     compute(stage_tag, tt, masked_tag);
     wait_next(tt);
     barrier_nofence();
   };
-  // tile t sits in ring stage (t - t_begin) % kStages
+  // the group's k-th tile sits in ring stage k % kStages
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (t_begin + i < ntiles) dma_tile(t_begin + i, i);
-  wait_next(t_begin - 1);
+    if (first + KVS * i < ntiles) dma_tile(first + KVS * i, i);
+  wait_next(first - KVS);
   barrier_nofence();
-  int t = t_begin;
+  int t = first;
   auto masked_step = [&](int tt) __attribute__((always_inline)) {
-    const int r = (tt - t_begin) % kStages;
+    const int r = ((tt - first) / KVS) % kStages;
     if (r == 0)
       step(tt, st0{}, mask_t{});
     else if (r == 1)
       step(tt, st1{}, mask_t{});
-    else if (kStages == 3 || r == 2)
-      step(tt, st2{}, mask_t{});
-    else if constexpr (kStages == 4)
-      step(tt, st3{}, mask_t{});
+    else if constexpr (kStages == 4) {
+      if (r == 2)
+        step(tt, st2{}, mask_t{});
+      else
+        step(tt, st3{}, mask_t{});
+    }
   };
   if constexpr (BAND) {
     // band: the masked tiles left of the full ones, and as many more as put
     // the first full group in stage 0
-    const int f_start = t_begin + kStages * ((max(full_lo - t_begin, 0) + kStages - 1) / kStages);
-    for (; t < f_start && t < ntiles; ++t) masked_step(t);
+    const int i_lo = (max(full_lo - first, 0) + KVS - 1) / KVS;
+    const int f_start = first + KVS * kStages * ((i_lo + kStages - 1) / kStages);
+    for (; t < f_start && t < ntiles; t += KVS) masked_step(t);
   }
-  for (; t + kStages - 1 < n_full; t += kStages) {
+  for (; t + KVS * (kStages - 1) < n_full; t += KVS * kStages) {
     step(t, st0{}, full_t{});
-    step(t + 1, st1{}, full_t{});
-    step(t + 2, st2{}, full_t{});
-    if constexpr (kStages == 4) step(t + 3, st3{}, full_t{});
+    step(t + KVS, st1{}, full_t{});
+    if constexpr (kStages == 4) {
+      step(t + 2 * KVS, st2{}, full_t{});
+      step(t + 3 * KVS, st3{}, full_t{});
+    }
   }
-  for (; t < ntiles; ++t) masked_step(t);
+  for (; t < ntiles; t += KVS) masked_step(t);
+
+  if constexpr (KVS == 2) {
+    // the shorter group passes the barriers of the longer one's last step
+    const int span = max(ntiles - t_begin, 0);
+    const int count = (max(span - grp, 0) + 1) / 2;  // this group's tiles
+    for (int j = count; j < (span + 1) / 2; ++j) barrier_nofence();
+    // ---- merge: group 1 leaves (m, l, O^T) in LDS (its ring is free: every
+    //      LDS read and load of both rings completed before the last
+    //      barrier), group 0 takes them up with the rescale identity
+    //      O = 2^(m0 - M) O0 + 2^(m1 - M) O1, l likewise, M = max(m0, m1)
+    constexpr int NC = 1 + 4 * DT;  // 16-byte chunks per lane: (m, l), then O^T
+    f32x4* const xch = reinterpret_cast<f32x4*>(smem) + (w * NC) * 64 + lane;
+    if (grp == 1) {
+      xch[0] = f32x4{m, l, lt, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+          xch[(1 + 4 * dt + c4) * 64] =
+              f32x4{oacc[dt][4 * c4], oacc[dt][4 * c4 + 1], oacc[dt][4 * c4 + 2], oacc[dt][4 * c4 + 3]};
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const f32x4 ml = xch[0];
+    const float mx = fmaxf(m, ml[0]);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    const float a0 = fast_exp2(m - mu), a1 = fast_exp2(ml[0] - mu);
+    l = a0 * l + a1 * ml[1];
+    if constexpr (BF16) lt = a0 * lt + a1 * ml[2];
+    m = mx;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 o1 = xch[(1 + 4 * dt + c4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[dt][4 * c4 + e] = a0 * oacc[dt][4 * c4 + e] + a1 * o1[e];
+      }
+  }
 
   // ---- epilogue: O = O^T / l, cast, store; lse = (m + log2 l) ln 2
   l = sum_xor32(l);
+  const float ln = BF16 ? sum_xor32(lt) : l;  // O's normaliser
   // The lane's row and half are re-derived from the lane counter here rather
   // than kept live across the KV loop (which would cost two spilled registers).
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int hh_e = lane_e >> 5;
   const int qrow_e = q0 + 32 * w + (lane_e & 31);
   if (qrow_e < Nq) {
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const float inv = (ln > 0.f) ? 1.f / ln : 0.f;
     uint16_t* op = obase + (int64_t)qrow_e * a.son;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -485,11 +567,12 @@ template <int D, bool BF16, int MASK, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   if constexpr (!VARLEN) {
     if (a.rows == 128) {
-      hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4>), dim3(a.nblocks), dim3(64 * 4), 0, stream, a);
+      hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4, 2>), dim3(a.nblocks), dim3(64 * 8), 0, stream,
+                         a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 8>), dim3(a.nblocks), dim3(64 * 8), 0, stream, a);
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 8, 1>), dim3(a.nblocks), dim3(64 * 8), 0, stream, a);
   return hipGetLastError();
 }
 

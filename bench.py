@@ -36,8 +36,17 @@ bottom-right), a packed prefill of 16 sequences of seeded lengths up to
 shape, and the backward (dQ, dK, dV) of the headline prefill; they are
 printed under "widened".
 
-Flags: --only prefill|decode|copy runs just that launch (for rocprofv3 runs),
---no-cpu skips the oracle baseline.  Prints one JSON line.
+"configs" times every workload of the pages at its own shape: the tiny
+causal prefill, the ten GQA-sweep cases (B=2, Hq=16, Hkv 16..1, N=1023, D=64,
+causal and not), the six serving prefills (B=2, Hq=32, Hkv=8, D=128,
+N 2048/4096/8192, causal and not), the bf16 cross-attention MQA prefill (B=4,
+Hq=32, Hkv=1, Nq=512, Nkv=16384, D=128) and decode at every cache length
+(1 .. 8192), each with its seed, time, throughput and fraction of peak.
+
+Flags: --only prefill|decode|copy|cross|gqa runs just that launch (for
+rocprofv3 runs; cross = the bf16 cross-attention MQA prefill, gqa = the GQA
+sweep at Hkv=4, causal and not), --no-cpu skips the oracle baseline,
+--no-configs the per-workload block.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -92,8 +101,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all")
+    p.add_argument("--only", choices=["all", "prefill", "decode", "copy", "cross", "gqa"], default="all")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-configs", action="store_true", help="skip the per-workload timing block")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--causal", type=int, default=1)
     return p.parse_args()
@@ -152,6 +162,96 @@ def cpu_baseline(case, budget_s: float):
             "cpu_model": cpu_model(), "host_cpu_count": os.cpu_count()}
 
 
+def _back_to_back_ms(fn, reps: int, stream, sleep_cycles: int = 2_000_000) -> float:
+    """Mean ms per call of `reps` back-to-back calls between two HIP events on
+    `stream`, queued behind a sleep kernel so the events time GPU work only."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda._sleep(sleep_cycles)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _per_launch_ms(fn, reps: int, stream):
+    """Median and mean ms of `reps` launches, each bracketed by its own pair of
+    HIP events on `stream`."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in evs]
+    return statistics.median(t), statistics.fmean(t)
+
+
+def time_configs(A, W, dev, stream, kcs, vcs, warmup: int = 10, reps: int = 30):
+    """Every workload of the pages at its own shape, with its seed, time,
+    algorithmic throughput and fraction of the MI355X peak (2.5 PFLOP/s dense
+    fp16/bf16 MFMA for prefill, 8 TB/s HBM for decode).  Prefill launches of
+    100 us or more are timed one by one (median, the pages' statistic); the
+    GQA sweep and the decode calls back to back (mean).  Decode reads rotate
+    over the cache copies in `kcs`/`vcs` (>= 512 MiB), so the Infinity Cache
+    cannot hold them between calls."""
+    import torch
+    out = {}
+
+    def prefill(case, back_to_back):
+        q, k, v = (t.to(dev) for t in W.prefill_inputs(case))
+        o = torch.empty_like(q)
+        lse = torch.empty(case.B, case.Hq, case.Nq, dtype=torch.float32, device=dev)
+        fn = lambda i: A.attn_fwd(q, k, v, causal=case.causal, scale=case.softmax_scale, out=o, lse=lse,  # noqa
+                                  return_lse=True)
+        for i in range(warmup):
+            fn(i)
+        if back_to_back:
+            ms = _back_to_back_ms(fn, max(reps, 50), stream)
+            stat = "mean of back-to-back launches"
+        else:
+            ms, _ = _per_launch_ms(fn, reps, stream)
+            stat = "median of per-launch events"
+        fl = case.flops()
+        r = {"workload": case.name, "seed": case.seed, "B": case.B, "Hq": case.Hq, "Hkv": case.Hkv, "Nq": case.Nq,
+             "Nkv": case.Nkv, "D": case.D, "dtype": case.dtype, "causal": case.causal, "flops_per_launch": fl,
+             "us_per_launch": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+             "frac_of_2500_tflops": round(fl / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4), "timing": stat}
+        del q, k, v, o, lse
+        return r
+
+    out["tiny"] = prefill(W.TINY, True)
+    out["gqa_sweep"] = [prefill(c, True) for c in W.gqa_sweep()]
+    out["serving"] = [prefill(W.serving(n, c), False) for n in (2048, 4096, 8192) for c in (True, False)]
+    out["cross_mqa_bf16"] = prefill(W.CROSS, False)
+
+    dec = []
+    for L in W.DECODE_LENS:
+        dc = W.decode_case(L)
+        qd = W.decode_inputs(dc)[0].to(dev)
+        od = torch.empty_like(qd)
+        ld = torch.empty(dc.B, dc.Hq, dtype=torch.float32, device=dev)
+        ws = A.decode_workspace(dc.B, dc.Hq, dc.Hkv, dc.S_max, dc.D, dev)
+        rot = len(kcs)
+        fn = lambda i: A.attn_decode(qd, kcs[i % rot], vcs[i % rot], L, scale=dc.softmax_scale,  # noqa
+                                     workspace=ws, out=od, lse=ld, return_lse=True)
+        for i in range(warmup):
+            fn(i)
+        ms = _back_to_back_ms(fn, max(reps, 40), stream)
+        nb = dc.kv_bytes()
+        dec.append({"workload": dc.name, "seed": dc.seed, "cache_len": L, "bytes_per_call": nb,
+                    "us_per_call": round(ms * 1e3, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "frac_of_8000_gbs": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "timing": f"mean of back-to-back calls over {rot} rotated cache copies"})
+    out["decode"] = dec
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -171,6 +271,22 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.only in ("cross", "gqa"):
+        # one workload alone, for a profiler run: warm-up launches, then `steps` timed ones
+        cases = [W.CROSS] if args.only == "cross" else [c for c in W.gqa_sweep() if c.Hkv == 4]
+        res = []
+        for case in cases:
+            q, k, v = (t.to(dev) for t in W.prefill_inputs(case))
+            o = torch.empty_like(q)
+            fn = lambda i: A.attn_fwd(q, k, v, causal=case.causal, scale=case.softmax_scale, out=o)  # noqa
+            for i in range(args.warmup):
+                fn(i)
+            ms = _back_to_back_ms(fn, args.steps, stream)
+            res.append({"workload": case.name, "us_per_launch": round(ms * 1e3, 2),
+                        "tflops": round(case.flops() / (ms * 1e-3) / 1e12, 1)})
+        print(json.dumps({"only": args.only, "results": res}), flush=True)
+        return
 
     pcase = W.serving(8192, bool(args.causal))
     dcase = W.decode_case(8192)
@@ -448,6 +564,10 @@ def main():
             del gq, gk, gv, go
         widened["prefill_gqa_sweep"] = gs
 
+    configs = None
+    if args.only == "all" and not args.no_configs:
+        configs = time_configs(A, W, dev, stream, kcs, vcs)
+
     # context: achievable HBM rate of a plain 256 MiB device copy (read + write)
     copy_gbs = None
     if args.only == "all":
@@ -545,6 +665,8 @@ def main():
                          "timing": "back-to-back calls over rotating caches (split kernel + combine kernel)",
                          "kernel": "decode_kernel<128, f16, uniform lengths> + decode_combine_kernel<128, f16, uniform lengths>",
                          "traffic": measured_traffic("decode_L8192_hkv8_d128_fp16.md", DECODE_SOURCES)}
+    if configs:
+        out["configs"] = configs
     if widened:
         out["widened"] = widened
     if copy_gbs is not None:

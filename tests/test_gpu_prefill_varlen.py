@@ -110,8 +110,9 @@ def test_varlen_rising_scores(causal, br):
 
 
 def test_varlen_equal_lengths_is_fwd_bitwise():
-    """B equal-length sequences packed: identical bits to attn_fwd on the (B, N, H, D) layout."""
-    B, N, Hq, Hkv, D = 3, 1000, 8, 2, 128
+    """B equal-length sequences packed: identical bits to attn_fwd on the (B, N, H, D) layout
+    (3 x 32 heads x 4 query blocks: a grid large enough for 256-row blocks on both paths)."""
+    B, N, Hq, Hkv, D = 3, 1000, 32, 8, 128
     _say("varlen vs attn_fwd, equal lengths")
     g = torch.Generator().manual_seed(W.BASE_SEED + 86)
     q = torch.randn(B, N, Hq, D, generator=g).half().to(DEV)
@@ -129,8 +130,9 @@ def test_varlen_equal_lengths_is_fwd_bitwise():
 
 
 def test_varlen_chunk_is_fwd_bottom_right_bitwise():
-    """One packed chunk of 300 queries against 2000 keys equals attn_fwd bottom-right bit for bit."""
-    Lq, Lk, Hq, Hkv, D = 300, 2000, 8, 2, 64
+    """One packed chunk of 300 queries against 2000 keys equals attn_fwd bottom-right bit for bit
+    (72 heads x 2 query blocks: a grid large enough for 256-row blocks on both paths)."""
+    Lq, Lk, Hq, Hkv, D = 300, 2000, 72, 8, 64
     _say("varlen chunk vs attn_fwd bottom_right")
     g = torch.Generator().manual_seed(W.BASE_SEED + 87)
     q = torch.randn(Lq, Hq, D, generator=g).bfloat16().to(DEV)
