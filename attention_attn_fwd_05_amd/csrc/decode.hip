@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const Deco
   constexpr int VBLK = (kDT / 4) * (D / 8);  // 4x8 V blocks per tile
   constexpr int VPT = VBLK / 256;            // V blocks per thread
   static_assert(VBLK % 256 == 0, "V blocks divide evenly");
-  constexpr int RED_FLOATS = 128 + 4 * 16 * D;  // wave merge: m[4][16], l[4][16], o[4][16][D]
+  constexpr int RED_FLOATS = 128 + 4 * 16 * (D + 4);  // wave merge: m[4][16], l[4][16], o[4][16][D + 4]
   constexpr int LDS_BYTES = (RED_FLOATS * 4 > D * VLD * 2) ? RED_FLOATS * 4 : D * VLD * 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];  // V^T stage, then the merges
   uint16_t* const vt = reinterpret_cast<uint16_t*>(lds);
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const Deco
         const int64_t pg = rr >= kw0 + 16 ? kp_hi : kp_lo;
         const uint16_t* kp = kbase + pg * a.skb + (int64_t)(rr & rmask) * a.skn + 8 * rg;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) T.kf[gi][ks] = load16(kp + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks) T.kf[gi][ks] = load16_nt(kp + 32 * ks);
       }
       constexpr int VROWS = 2048 / D;  // V rows one wave loads per j
 #pragma unroll
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const Deco
         const int g0 = kb + 4 * vkvg[j];
         const uint16_t* vb = vbase + (g0 >= vs + 16 ? vp_hi : vp_lo) * a.svb + 8 * vdc[j];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) T.v[j][r] = load16(vb + (int64_t)(row(g0 + r) & rmask) * a.svn);
+        for (int r = 0; r < 4; ++r) T.v[j][r] = load16_nt(vb + (int64_t)(row(g0 + r) & rmask) * a.svn);
       }
       return;
     }
@@ -202,22 +202,22 @@ __global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const Deco
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          T.kf[gi][ks] = bload16(rk, max(krow + 4 * gi, f) * (int32_t)a.skn * 2 + 16 * rg + 64 * ks);
+          T.kf[gi][ks] = bload16_nt(rk, max(krow + 4 * gi, f) * (int32_t)a.skn * 2 + 16 * rg + 64 * ks);
 #pragma unroll
       for (int j = 0; j < VPT; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          T.v[j][r] = bload16(rv, max(4 * vkvg[j] + r, f) * (int32_t)a.svn * 2 + 16 * vdc[j]);
+          T.v[j][r] = bload16_nt(rv, max(4 * vkvg[j] + r, f) * (int32_t)a.svn * 2 + 16 * vdc[j]);
       return;
     }
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) T.kf[gi][ks] = bload16(rk, koff + gi * 4 * (int32_t)a.skn * 2 + 64 * ks);
+      for (int ks = 0; ks < KS; ++ks) T.kf[gi][ks] = bload16_nt(rk, koff + gi * 4 * (int32_t)a.skn * 2 + 64 * ks);
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) T.v[j][r] = bload16(rv, voff[j][r]);
+      for (int r = 0; r < 4; ++r) T.v[j][r] = bload16_nt(rv, voff[j][r]);
   };
   auto compute_tile = [&](const Tile& T, int kb, bool first) {
     if (!first) __syncthreads();  // the previous tile's V^T reads are done
@@ -293,20 +293,24 @@ __global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const Deco
   }
   __syncthreads();  // V^T reads done: the LDS is reused for the merges below
 
-  // ---- merge the 4 waves in LDS: per wave m[16], l[16], o[16][D] (fp32)
+  // ---- merge the 4 waves in LDS: per wave m[16], l[16] and the o rows of the
+  //      group's nh heads (fp32), rows padded to D + 4 floats so that the
+  //      heads of a wave start on different banks
   float* red = reinterpret_cast<float*>(lds);
   float* rm = red;       // [4][16]
   float* rl = red + 64;  // [4][16]
-  float* ro = red + 128; // [4][16][D]
+  constexpr int RP = D + 4;  // padded row of o: heads of one wave start on different banks
+  float* ro = red + 128; // [4][16][RP]
   l = sum_xor32(sum_xor16(l));
   if (rg == 0) {
     rm[w * 16 + col] = m;
     rl[w * 16 + col] = l;
   }
+  if (col < nh) {
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ro[(w * 16 + col) * D + 16 * dt + 4 * rg + e] = oacc[dt][e];
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<f32x4*>(ro + (w * 16 + col) * RP + 16 * dt + 4 * rg) = oacc[dt];
+  }
   __syncthreads();
 
   // thread -> (head hn, SL-wide slice of the head dim)
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const Deco
     const float sc = fast_exp2(rm[ww * 16 + hn] - Mu);
     Ls += sc * rl[ww * 16 + hn];
 #pragma unroll
-    for (int j = 0; j < SL; ++j) acc[j] += sc * ro[(ww * 16 + hn) * D + d0 + j];
+    for (int j = 0; j < SL; ++j) acc[j] += sc * ro[(ww * 16 + hn) * RP + d0 + j];
   }
 
   auto store_lse = [&](int head, float Mx, float Lx) {

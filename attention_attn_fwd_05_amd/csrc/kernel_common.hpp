@@ -121,6 +121,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// the same with the non-temporal hint: data read once (a decode's K/V stream)
+// is not kept in the caches at the expense of other lines
+__device__ __forceinline__ u32x4 bload16_nt(__amdgpu_buffer_rsrc_t r, int32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 
 // Low (SEL = 0x05040100) or high (SEL = 0x07060302) 16-bit halves of two dwords:
 // result = {a.half, b.half} with a's half in the low 16 bits.
@@ -151,6 +156,9 @@ __device__ __forceinline__ float sum2_bf16(uint32_t two, float acc) {
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 load16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void store16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace attn
