@@ -7,11 +7,12 @@ One step = one pass of the whole path over resident synthetic inputs:
 W untimed warm-up steps, then K timed steps between two device synchronisations.
 Each launch is also bracketed by HIP events on the stream it runs on (the
 current torch stream, which the binding launches on); prefill throughput is
-algorithmic work per launch / median event duration (the mean is reported
-beside it).  Decode (a ~20 us call)
-is additionally timed in steady state right after the timed steps: back-to-
-back calls between two events, queued behind a sleep kernel so the events
-measure GPU time only; that figure is the reported decode GB/s.  The same
+algorithmic work per launch / average launch duration, the latter measured
+right after the timed steps as R back-to-back launches between two events on
+that stream, queued behind a sleep kernel so the events measure GPU time only
+(the in-step per-launch event figures are reported beside it: an event pair
+around each launch adds its own cost).  Decode (a ~17 us call) is timed the
+same way; that figure is the reported decode GB/s.  The same
 measurement on a single cache copy (resident in the Infinity Cache), a plain
 256 MiB device copy's rate and a large fp16 library GEMM's rate are printed as
 context (achievable HBM and dense-MFMA references on the same box).
@@ -177,27 +178,12 @@ def _back_to_back_ms(fn, reps: int, stream, sleep_cycles: int = 2_000_000) -> fl
     return e0.elapsed_time(e1) / reps
 
 
-def _per_launch_ms(fn, reps: int, stream):
-    """Median and mean ms of `reps` launches, each bracketed by its own pair of
-    HIP events on `stream`."""
-    import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        fn(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    t = [a.elapsed_time(b) for a, b in evs]
-    return statistics.median(t), statistics.fmean(t)
-
-
 def time_configs(A, W, dev, stream, kcs, vcs, warmup: int = 10, reps: int = 30):
     """Every workload of the pages at its own shape, with its seed, time,
     algorithmic throughput and fraction of the MI355X peak (2.5 PFLOP/s dense
-    fp16/bf16 MFMA for prefill, 8 TB/s HBM for decode).  Prefill launches of
-    100 us or more are timed one by one (median, the pages' statistic); the
-    GQA sweep and the decode calls back to back (mean).  Decode reads rotate
+    fp16/bf16 MFMA for prefill, 8 TB/s HBM for decode), every figure the mean
+    of back-to-back launches between two events (at least 50 for launches
+    under a millisecond, 30 for the longer ones).  Decode reads rotate
     over the cache copies in `kcs`/`vcs` (>= 512 MiB), so the Infinity Cache
     cannot hold them between calls."""
     import torch
@@ -211,12 +197,8 @@ def time_configs(A, W, dev, stream, kcs, vcs, warmup: int = 10, reps: int = 30):
                                   return_lse=True)
         for i in range(warmup):
             fn(i)
-        if back_to_back:
-            ms = _back_to_back_ms(fn, max(reps, 50), stream)
-            stat = "mean of back-to-back launches"
-        else:
-            ms, _ = _per_launch_ms(fn, reps, stream)
-            stat = "median of per-launch events"
+        ms = _back_to_back_ms(fn, max(reps, 50) if back_to_back else reps, stream)
+        stat = "mean of back-to-back launches"
         fl = case.flops()
         r = {"workload": case.name, "seed": case.seed, "B": case.B, "Hq": case.Hq, "Hkv": case.Hkv, "Nq": case.Nq,
              "Nkv": case.Nkv, "D": case.D, "dtype": case.dtype, "causal": case.causal, "flops_per_launch": fl,
@@ -227,7 +209,7 @@ def time_configs(A, W, dev, stream, kcs, vcs, warmup: int = 10, reps: int = 30):
 
     out["tiny"] = prefill(W.TINY, True)
     out["gqa_sweep"] = [prefill(c, True) for c in W.gqa_sweep()]
-    out["serving"] = [prefill(W.serving(n, c), False) for n in (2048, 4096, 8192) for c in (True, False)]
+    out["serving"] = [prefill(W.serving(n, c), n < 8192) for n in (2048, 4096, 8192) for c in (True, False)]
     out["cross_mqa_bf16"] = prefill(W.CROSS, False)
 
     dec = []
@@ -341,6 +323,17 @@ def main():
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # steady-state prefill: R back-to-back launches between two events on the
+    # launching stream, queued behind a sleep kernel so the events time GPU work
+    # only; their mean is the kernel's average launch duration (an event pair
+    # around every launch adds its own cost between launches, shown beside it)
+    pf_ss = None
+    if do_p:
+        R = max(20, args.steps)
+        pf_ss = _back_to_back_ms(
+            lambda i: A.attn_fwd(q, k, v, causal=pcase.causal, scale=pcase.softmax_scale, out=o, lse=lse,
+                                 return_lse=True), R, stream, sleep_cycles=5_000_000)
 
     # steady-state decode: R back-to-back decode calls (rotating caches) between
     # two events, queued behind a sleep kernel so the events time GPU work only
@@ -610,8 +603,10 @@ def main():
         p_mean = statistics.fmean(pt)
         p_med = statistics.median(pt)
         flops = pcase.flops()
-        res["prefill"] = {"ms_mean": p_mean, "ms_median": p_med, "ms_std": statistics.pstdev(pt),
-                          "tflops": flops / (p_med * 1e-3) / 1e12, "tflops_from_mean": flops / (p_mean * 1e-3) / 1e12,
+        res["prefill"] = {"steady_ms_per_launch": pf_ss, "steady_launches": max(20, args.steps),
+                          "tflops": flops / (pf_ss * 1e-3) / 1e12,
+                          "in_step_ms_mean": p_mean, "in_step_ms_median": p_med, "in_step_ms_std": statistics.pstdev(pt),
+                          "in_step_tflops_from_median": flops / (p_med * 1e-3) / 1e12,
                           "flops_per_launch": flops,
                           "flops_per_launch_no_causal_factor": 4 * pcase.B * pcase.Hq * pcase.Nq * pcase.Nkv * pcase.D}
     if do_d:
