@@ -39,7 +39,7 @@ struct FwdArgs {
   // band mask (mask mode 2): query i sees keys i + off - win_left <= j <=
   // i + off + win_right; -1 leaves that side open
   int win_left, win_right;
-  int rows;  // query rows per workgroup: 256, or 128 for grids that 256-row blocks leave half empty
+  int rows;  // query rows per workgroup: 256; 128 for dense grids that 256-row blocks leave half empty and for packed batches of short sequences
 };
 
 // mask: 0 none, 1 causal, 2 band

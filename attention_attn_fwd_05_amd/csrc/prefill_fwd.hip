@@ -8,9 +8,11 @@
 //
 // gfx950 design (not the pages' Triton tiling):
 //   * one workgroup = 8 wave64s = 256 query rows of one q head; each wave owns
-//     32 rows for the whole KV loop (two waves per SIMD).  When 256-row blocks
-//     would leave at least half the CUs idle, 4 waves = 128 rows (one wave per
-//     SIMD), with bitwise the same per-row arithmetic.
+//     32 rows for the whole KV loop (two waves per SIMD).  Dense grids that
+//     256-row blocks would leave at least half empty use 128-row blocks of two
+//     key groups (below).  Packed batches of short sequences use 128-row
+//     blocks of 4 waves and one key group, two workgroups per CU, with
+//     bitwise the same per-row arithmetic as 256-row blocks.
 //   * KV tiles of 64 rows go from HBM/L2 straight into LDS with buffer-to-LDS
 //     loads (no register staging), through a 4-stage ring, row-major with an
 //     XOR swizzle of 16-byte slots that keeps every access pattern free of bank
@@ -70,17 +72,19 @@ struct PrefillLds {
   static_assert(2 * (STAGES * TILE) <= 65536, "V^T read offsets fit the 16-bit DS offset");
 };
 
-// ring depth: four stages (loads of tile t+3 issued before tile t); two when a
-// workgroup holds two rings of D = 128 tiles (four would need 256 KiB of LDS)
-template <int D, int KVS>
+// ring depth: four stages (loads of tile t+3 issued before tile t); two for
+// D = 128 tiles in a 4-row-wave workgroup: with two key groups (two rings;
+// four stages would need 256 KiB of LDS), or with one, whose 64 KiB ring lets
+// two such workgroups share a CU
+template <int D, int KVS, int RW>
 constexpr int prefill_stages() {
-  return (KVS == 2 && D == 128) ? 2 : 4;
+  return (D == 128 && RW == 4) ? 2 : 4;
 }
 
 // MASK 0: every key below Nkv; 1: causal (j <= i + off); 2: a band of keys
 // i + off - win_left <= j <= i + off + win_right (either side may be open).
-// RW: row waves, 32 query rows each (RW = 8: 256-row blocks).  KVS: key
-// groups.  With KVS = 2 a workgroup of 8 waves owns 128 rows (RW = 4); waves
+// RW: row waves, 32 query rows each (RW = 8: 256-row blocks; RW = 4: 128).
+// KVS: key groups.  With KVS = 2 a workgroup of 8 waves owns 128 rows; waves
 // w and w + 4 share a SIMD and the same 32 rows, and each streams every
 // second key tile of the block's range through a ring of its own, so a grid
 // too small to fill the chip with 256-row blocks still runs two waves per
@@ -90,7 +94,7 @@ template <int D, bool BF16, int MASK, bool VARLEN, int RW, int KVS>
 __global__ __launch_bounds__(64 * RW * KVS, 2) void prefill_fwd_kernel(const FwdArgs a) {
   constexpr int kWaves = RW * KVS;    // waves per workgroup
   constexpr int kBM = 32 * RW;        // query rows per workgroup
-  constexpr int kStages = prefill_stages<D, KVS>();
+  constexpr int kStages = prefill_stages<D, KVS, RW>();
   static_assert(kStages == 2 || kStages == 4, "the KV loop cycles two or four stages");
   static_assert(KVS == 1 || KVS == 2, "one or two key groups");
   constexpr bool CAUSAL = MASK == 1;
@@ -563,14 +567,19 @@ __global__ __launch_bounds__(64 * RW * KVS, 2) void prefill_fwd_kernel(const Fwd
   }
 }
 
+// 128-row blocks: dense grids too small for 256-row blocks take two key groups
+// (8 waves); packed batches of short sequences take one (4 waves, two
+// workgroups per CU, so one block's start and end overlap the other's loop)
 template <int D, bool BF16, int MASK, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  if constexpr (!VARLEN) {
-    if (a.rows == 128) {
+  if (a.rows == 128) {
+    if constexpr (VARLEN)
+      hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4, 1>), dim3(a.nblocks), dim3(64 * 4), 0, stream,
+                         a);
+    else
       hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4, 2>), dim3(a.nblocks), dim3(64 * 8), 0, stream,
                          a);
-      return hipGetLastError();
-    }
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 8, 1>), dim3(a.nblocks), dim3(64 * 8), 0, stream, a);
   return hipGetLastError();

@@ -109,11 +109,15 @@ def test_varlen_rising_scores(causal, br):
     _compare(o, l, Oref, Lref, case.torch_dtype)
 
 
-def test_varlen_equal_lengths_is_fwd_bitwise():
-    """B equal-length sequences packed: identical bits to attn_fwd on the (B, N, H, D) layout
-    (3 x 32 heads x 4 query blocks: a grid large enough for 256-row blocks on both paths)."""
-    B, N, Hq, Hkv, D = 3, 1000, 32, 8, 128
-    _say("varlen vs attn_fwd, equal lengths")
+@pytest.mark.parametrize("N", [1000, 6500], ids=["short_128row", "long_256row"])
+def test_varlen_equal_lengths_is_fwd_bitwise(N):
+    """B equal-length sequences packed: identical bits to attn_fwd on the (B, N, H, D) layout.
+    attn_fwd runs 256-row blocks of one key group (a grid of 3 x 32 heads x >= 4 query
+    blocks); the packed path runs 128-row blocks of 4 waves for a mean length of 1000 and
+    256-row blocks for 6500 (above the 6144-row mean where it switches), the same per-row
+    arithmetic either way."""
+    B, Hq, Hkv, D = 3, 32, 8, 128
+    _say(f"varlen vs attn_fwd, equal lengths N={N}")
     g = torch.Generator().manual_seed(W.BASE_SEED + 86)
     q = torch.randn(B, N, Hq, D, generator=g).half().to(DEV)
     k = torch.randn(B, N, Hkv, D, generator=g).half().to(DEV)
@@ -210,6 +214,19 @@ def test_varlen_malformed_offsets_stay_in_bounds():
     case = W.VarlenPrefillCase("after_malformed", (300, 400), (300, 400), Hq, Hkv, D, "fp16", True,
                                seed=W.BASE_SEED + 91)
     run_varlen(case)
+
+
+def test_varlen_long_mixed_sampled():
+    """A packed batch of long sequences (mean 7000 rows: 256-row blocks) against the
+    oracle on the first, last and two inner rows of every sequence, causal and not."""
+    lens = (5000, 9000, 7000)
+    for causal in (True, False):
+        case = W.VarlenPrefillCase(f"long_mixed_{'causal' if causal else 'full'}", lens, lens, 16, 4, 128, "fp16",
+                                   causal, seed=W.BASE_SEED + 192)
+        cq = case.cu_q
+        rows = sorted({r for b in range(case.B)
+                       for r in (cq[b], cq[b] + 255, cq[b] + 256, (cq[b] + cq[b + 1]) // 2, cq[b + 1] - 1)})
+        run_varlen(case, rows=np.array(rows))
 
 
 def test_varlen_serving_batch_sampled():
