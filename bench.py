@@ -44,9 +44,10 @@ N 2048/4096/8192, causal and not), the bf16 cross-attention MQA prefill (B=4,
 Hq=32, Hkv=1, Nq=512, Nkv=16384, D=128) and decode at every cache length
 (1 .. 8192), each with its seed, time, throughput and fraction of peak.
 
-Flags: --only prefill|decode|copy|cross|gqa runs just that launch (for
-rocprofv3 runs; cross = the bf16 cross-attention MQA prefill, gqa = the GQA
-sweep at Hkv=4, causal and not), --no-cpu skips the oracle baseline,
+Flags: --only prefill|decode|copy|cross|gqa|packed|bwd runs just that launch
+(for rocprofv3 runs; cross = the bf16 cross-attention MQA prefill, gqa = the
+GQA sweep at Hkv=4, causal and not, packed = the 16-sequence packed prefill,
+bwd = the headline backward), --no-cpu skips the oracle baseline,
 --no-configs the per-workload block.  Prints one JSON line.
 """
 
@@ -102,7 +103,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--only", choices=["all", "prefill", "decode", "copy", "cross", "gqa"], default="all")
+    p.add_argument("--only", choices=["all", "prefill", "decode", "copy", "cross", "gqa", "packed", "bwd"],
+                   default="all")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-configs", action="store_true", help="skip the per-workload timing block")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -254,19 +256,49 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    if args.only in ("cross", "gqa"):
+    if args.only in ("cross", "gqa", "packed", "bwd"):
         # one workload alone, for a profiler run: warm-up launches, then `steps` timed ones
-        cases = [W.CROSS] if args.only == "cross" else [c for c in W.gqa_sweep() if c.Hkv == 4]
         res = []
-        for case in cases:
-            q, k, v = (t.to(dev) for t in W.prefill_inputs(case))
+        if args.only in ("cross", "gqa"):
+            cases = [W.CROSS] if args.only == "cross" else [c for c in W.gqa_sweep() if c.Hkv == 4]
+            for case in cases:
+                q, k, v = (t.to(dev) for t in W.prefill_inputs(case))
+                o = torch.empty_like(q)
+                fn = lambda i: A.attn_fwd(q, k, v, causal=case.causal, scale=case.softmax_scale, out=o)  # noqa
+                for i in range(args.warmup):
+                    fn(i)
+                ms = _back_to_back_ms(fn, args.steps, stream)
+                res.append({"workload": case.name, "us_per_launch": round(ms * 1e3, 2),
+                            "tflops": round(case.flops() / (ms * 1e-3) / 1e12, 1)})
+        elif args.only == "packed":
+            # the packed 16-sequence serving batch (as widened.prefill_varlen)
+            vp = W.varlen_serving_case()
+            q, k, v = (t.to(dev) for t in W.varlen_prefill_inputs(vp))
+            cq = torch.tensor(vp.cu_q, dtype=torch.int32, device=dev)
             o = torch.empty_like(q)
-            fn = lambda i: A.attn_fwd(q, k, v, causal=case.causal, scale=case.softmax_scale, out=o)  # noqa
+            fn = lambda i: A.attn_fwd_varlen(q, k, v, cq, cq, vp.max_q, causal=True, scale=vp.softmax_scale,  # noqa
+                                             out=o)
             for i in range(args.warmup):
                 fn(i)
             ms = _back_to_back_ms(fn, args.steps, stream)
-            res.append({"workload": case.name, "us_per_launch": round(ms * 1e3, 2),
-                        "tflops": round(case.flops() / (ms * 1e-3) / 1e12, 1)})
+            res.append({"workload": vp.name, "us_per_launch": round(ms * 1e3, 2),
+                        "tflops": round(vp.flops() / (ms * 1e-3) / 1e12, 1)})
+        else:
+            # backward of the headline prefill (as widened.backward): prep, dQ and dK/dV kernels
+            bc = W.serving(8192, True)
+            q, k, v = (t.to(dev) for t in W.prefill_inputs(bc))
+            do = torch.randn(q.shape, generator=torch.Generator().manual_seed(W.BASE_SEED + 60)).to(q.dtype).to(dev)
+            o, lse = A.attn_fwd(q, k, v, causal=True, scale=bc.softmax_scale, return_lse=True)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(A.load_library().attn_bwd_workspace_bytes(bc.B, bc.Hq, bc.Nq), dtype=torch.uint8,
+                             device=dev)
+            fn = lambda i: A.attn_bwd(q, k, v, o, do, lse, causal=True, scale=bc.softmax_scale, dq=dq, dk=dk,  # noqa
+                                      dv=dv, workspace=ws)
+            for i in range(args.warmup):
+                fn(i)
+            ms = _back_to_back_ms(fn, args.steps, stream)
+            res.append({"workload": bc.name + "_backward", "us_per_launch": round(ms * 1e3, 2),
+                        "tflops_5gemm": round(2.5 * bc.flops() / (ms * 1e-3) / 1e12, 1)})
         print(json.dumps({"only": args.only, "results": res}), flush=True)
         return
 
