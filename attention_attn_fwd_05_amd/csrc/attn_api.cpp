@@ -605,6 +605,12 @@ static attn_status bwd_impl(const void* q, const void* k, const void* v, const v
   a.nkb = (int)nkb;
   a.dq_blocks = (unsigned)dq_blocks;
   a.dkv_blocks = (unsigned)dkv_blocks;
+  // XCD-aware block order, as the forward's: workgroup i runs on XCD i % 8,
+  // and the remap gives each XCD a contiguous span of whole (batch, kv head)
+  // units, so the workgroups that stream one kv head's K and V (dQ pass) or
+  // its q heads' Q and dO rows (dK/dV pass) run on one XCD and meet in its L2
+  a.dq_remap = (dq_blocks % 8 == 0) && (dq_blocks / 8) % ((int64_t)a.group * nqb) == 0;
+  a.dkv_remap = (dkv_blocks % 8 == 0) && (dkv_blocks / 8) % nkb == 0;
   a.mask = mk.mode;
   a.causal_off = mk.bottom_right ? Nkv - Nq : 0;
   a.win_left = mk.left;

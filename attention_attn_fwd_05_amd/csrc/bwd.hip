@@ -158,14 +158,29 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   static_assert(NB >= 1, "every wave loads at least one block");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
 
-  // the query block runs slowest: under a causal mask the last blocks see the
-  // most keys, so every head's costliest blocks start first
-  const int heads = a.B * a.Hq;
-  int qb = blockIdx.x / heads;
-  const int bh = blockIdx.x - qb * heads;
+  // which (batch, q head, query block): under a causal mask the last blocks
+  // see the most keys, so the costliest blocks start first.  With the remap,
+  // XCD x (workgroup i runs on XCD i % 8) takes a contiguous span of whole
+  // (batch, kv head) units, each unit's blocks query block major and its q
+  // heads innermost, so the q heads sharing a kv head stream its K and V
+  // tiles together through one L2; otherwise the grid is query block major
+  // over all (batch, head) pairs
+  int qb, b, h;
+  if (!VARLEN && a.dq_remap) {
+    const int lid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int per_unit = a.group * a.nqb;
+    const int unit = lid / per_unit, rem = lid - unit * per_unit;
+    qb = rem / a.group;
+    b = unit / a.Hkv;
+    h = (unit - b * a.Hkv) * a.group + (rem - qb * a.group);
+  } else {
+    const int heads = a.B * a.Hq;
+    qb = blockIdx.x / heads;
+    const int bh = blockIdx.x - qb * heads;
+    b = bh / a.Hq;
+    h = bh - b * a.Hq;
+  }
   if (MASK != 0) qb = a.nqb - 1 - qb;
-  const int b = bh / a.Hq;
-  const int h = bh - b * a.Hq;
   const int kvh = h / a.group;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -392,11 +407,21 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   static_assert((kKvW / 2) * 2 * DT * 16 * 64 * 4 <= L::ELEMS * 2, "partial sums fit in LDS");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[L::ELEMS];
 
-  // the key block runs slowest: under a causal mask the first blocks see the
-  // most queries, so every (batch, kv head)'s costliest blocks start first
-  const int units = a.B * a.Hkv;
-  const int kbk = blockIdx.x / units;
-  const int unit = blockIdx.x - kbk * units;
+  // which (batch, kv head, key block): under a causal mask the first blocks
+  // see the most queries, so the costliest blocks start first.  With the
+  // remap, XCD x (workgroup i runs on XCD i % 8) takes a contiguous span of
+  // whole units, so a unit's key blocks run together on one XCD; otherwise
+  // the grid is key block major over all units
+  int kbk, unit;
+  if (!VARLEN && a.dkv_remap) {
+    const int lid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    unit = lid / a.nkb;
+    kbk = lid - unit * a.nkb;
+  } else {
+    const int units = a.B * a.Hkv;
+    kbk = blockIdx.x / units;
+    unit = blockIdx.x - kbk * units;
+  }
   const int b = unit / a.Hkv;
   const int kvh = unit - b * a.Hkv;
 
@@ -483,9 +508,14 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   auto ld_row0 = [&](int h) __attribute__((always_inline)) {
     return a.ld + 2 * (VARLEN ? (int64_t)h * a.total_q + bq : ((int64_t)b * a.Hq + h) * a.Nq);
   };
+  // step it takes query tile ntq - 1 - it / group of q head it % group: the
+  // last tile first and the group's q heads innermost, so the key blocks of
+  // one (batch, kv head) running together read the same Q and dO tiles at
+  // the same time (every block's range ends at the last tile)
   auto dma_tile = [&](int it, int stage) __attribute__((always_inline)) {
-    const int hgi = it / nt;
-    const int t = tq0 + (it - hgi * nt);
+    const int tix = it / a.group;
+    const int hgi = it - tix * a.group;
+    const int t = ntq - 1 - tix;
     const int h = kvh * a.group + hgi;
     const int64_t qo = (int64_t)t * kBT * a.sqn, go = (int64_t)t * kBT * a.sdon;
     const i32x4 rq = rsrc_words(a.q + (VARLEN ? bq * a.sqn : (int64_t)b * a.sqb) + (int64_t)h * a.sqh + qo,
@@ -520,8 +550,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   const int kmin = k0 + 32 * kg;  // this wave's first key
 
   auto compute = [&](int stage, int it, bool masked) __attribute__((always_inline)) {
-    const int hgi = it / nt;
-    const int tq = (tq0 + (it - hgi * nt)) * kBT + 32 * qh;  // this wave's first query
+    const int tq = (ntq - 1 - it / a.group) * kBT + 32 * qh;  // this wave's first query
     // 32 queries that see none of this wave's keys
     if (masked && CAUSAL && kmin > tq + 31 + off) return;
     if (masked && BAND && (kmin > tq + 31 + off + WR || kmin + 31 < tq + off - WL)) return;
@@ -617,7 +646,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   for (int it = 0; it < total; ++it) {
     const int stage = it & 1;
     if (it + 1 < total) dma_tile(it + 1, stage ^ 1);
-    const int t = tq0 + it % nt;
+    const int t = ntq - 1 - it / a.group;
     compute(stage, it, (MASK != 0) && (t < full_lo || t >= full_hi));
     __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
     barrier_nofence();

@@ -122,6 +122,9 @@ struct BwdArgs {
   int B, Hq, Hkv, Nq, Nkv, group;
   int nqb, nkb;                // query blocks (dq), key blocks (dkdv) per (batch, head)
   unsigned dq_blocks, dkv_blocks;
+  // 1: XCD-aware block order (dense grids whose 8 XCD spans hold whole
+  // (batch, kv head) units), for the dQ and the dK/dV pass
+  int dq_remap, dkv_remap;
   // packed variable-length batches (null otherwise): sequence b owns query rows
   // [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]); B is then the
   // number of sequences, Nq / Nkv the max_seqlen bounds, and lse and the
