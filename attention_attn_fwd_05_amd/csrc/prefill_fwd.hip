@@ -75,10 +75,10 @@ struct PrefillLds {
 // ring depth: four stages (loads of tile t+3 issued before tile t); two for
 // D = 128 tiles in a 4-row-wave workgroup: with two key groups (two rings;
 // four stages would need 256 KiB of LDS), or with one, whose 64 KiB ring lets
-// two such workgroups share a CU
+// two such workgroups share a CU; and two for three key groups (three rings)
 template <int D, int KVS, int RW>
 constexpr int prefill_stages() {
-  return (D == 128 && RW == 4) ? 2 : 4;
+  return ((D == 128 && RW == 4) || KVS == 3) ? 2 : 4;
 }
 
 // MASK 0: every key below Nkv; 1: causal (j <= i + off); 2: a band of keys
@@ -91,12 +91,13 @@ constexpr int prefill_stages() {
 // SIMD.  The two groups' (m, l, O) meet in LDS at the end and are merged with
 // the rescale identity of the online softmax.
 template <int D, bool BF16, int MASK, bool VARLEN, int RW, int KVS>
-__global__ __launch_bounds__(64 * RW * KVS, 2) void prefill_fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(64 * RW * KVS) __attribute__((amdgpu_waves_per_eu(KVS == 3 ? 3 : 2)))
+void prefill_fwd_kernel(const FwdArgs a) {
   constexpr int kWaves = RW * KVS;    // waves per workgroup
   constexpr int kBM = 32 * RW;        // query rows per workgroup
   constexpr int kStages = prefill_stages<D, KVS, RW>();
   static_assert(kStages == 2 || kStages == 4, "the KV loop cycles two or four stages");
-  static_assert(KVS == 1 || KVS == 2, "one or two key groups");
+  static_assert(KVS >= 1 && KVS <= 3, "one to three key groups");
   constexpr bool CAUSAL = MASK == 1;
   constexpr bool BAND = MASK == 2;
   using L = PrefillLds<D, kStages>;
@@ -503,43 +504,51 @@ __global__ __launch_bounds__(64 * RW * KVS, 2) void prefill_fwd_kernel(const Fwd
   }
   for (; t < ntiles; t += KVS) masked_step(t);
 
-  if constexpr (KVS == 2) {
-    // the shorter group passes the barriers of the longer one's last step
+  if constexpr (KVS >= 2) {
+    // the groups with a tile fewer pass the barriers of the longest one's
+    // last step
     const int span = max(ntiles - t_begin, 0);
-    const int count = (max(span - grp, 0) + 1) / 2;  // this group's tiles
-    for (int j = count; j < (span + 1) / 2; ++j) barrier_nofence();
-    // ---- merge: group 1 leaves (m, l, O^T) in LDS (its ring is free: every
-    //      LDS read and load of both rings completed before the last
-    //      barrier), group 0 takes them up with the rescale identity
-    //      O = 2^(m0 - M) O0 + 2^(m1 - M) O1, l likewise, M = max(m0, m1)
+    const int count = (max(span - grp, 0) + KVS - 1) / KVS;  // this group's tiles
+    for (int j = count; j < (span + KVS - 1) / KVS; ++j) barrier_nofence();
+    // ---- merge: groups 1 .. KVS-1 leave (m, l, O^T) in LDS (the rings are
+    //      free: every LDS read and load of every ring completed before the
+    //      last barrier), group 0 takes them up with the rescale identity
+    //      O = sum_g 2^(m_g - M) O_g, l likewise, M = max_g m_g
     constexpr int NC = 1 + 4 * DT;  // 16-byte chunks per lane: (m, l), then O^T
+    static_assert((KVS - 1) * RW * NC * 64 * 16 <= KVS * L::ELEMS * 2, "the exchange fits in the rings");
     f32x4* const xch = reinterpret_cast<f32x4*>(smem) + (w * NC) * 64 + lane;
-    if (grp == 1) {
-      xch[0] = f32x4{m, l, lt, 0.f};
+    constexpr int XG = RW * NC * 64;  // f32x4 entries per group's exchange region
+    if (grp != 0) {
+      f32x4* const x = xch + (grp - 1) * XG;
+      x[0] = f32x4{m, l, lt, 0.f};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
-          xch[(1 + 4 * dt + c4) * 64] =
+          x[(1 + 4 * dt + c4) * 64] =
               f32x4{oacc[dt][4 * c4], oacc[dt][4 * c4 + 1], oacc[dt][4 * c4 + 2], oacc[dt][4 * c4 + 3]};
     }
     __syncthreads();
-    if (grp == 1) return;
-    const f32x4 ml = xch[0];
-    const float mx = fmaxf(m, ml[0]);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    const float a0 = fast_exp2(m - mu), a1 = fast_exp2(ml[0] - mu);
-    l = a0 * l + a1 * ml[1];
-    if constexpr (BF16) lt = a0 * lt + a1 * ml[2];
-    m = mx;
+    if (grp != 0) return;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int g = 1; g < KVS; ++g) {
+      const f32x4* const x = xch + (g - 1) * XG;
+      const f32x4 ml = x[0];
+      const float mx = fmaxf(m, ml[0]);
+      const float mu = (mx == -INFINITY) ? 0.f : mx;
+      const float a0 = fast_exp2(m - mu), a1 = fast_exp2(ml[0] - mu);
+      l = a0 * l + a1 * ml[1];
+      if constexpr (BF16) lt = a0 * lt + a1 * ml[2];
+      m = mx;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const f32x4 o1 = xch[(1 + 4 * dt + c4) * 64];
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[dt][4 * c4 + e] = a0 * oacc[dt][4 * c4 + e] + a1 * o1[e];
-      }
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f32x4 o1 = x[(1 + 4 * dt + c4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[dt][4 * c4 + e] = a0 * oacc[dt][4 * c4 + e] + a1 * o1[e];
+        }
+    }
   }
 
   // ---- epilogue: O = O^T / l, cast, store; lse = (m + log2 l) ln 2
@@ -575,6 +584,9 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   if (a.rows == 128) {
     if constexpr (VARLEN)
       hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4, 1>), dim3(a.nblocks), dim3(64 * 4), 0, stream,
+                         a);
+    else if constexpr (D == 64)
+      hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4, 3>), dim3(a.nblocks), dim3(64 * 12), 0, stream,
                          a);
     else
       hipLaunchKernelGGL((prefill_fwd_kernel<D, BF16, MASK, VARLEN, 4, 2>), dim3(a.nblocks), dim3(64 * 8), 0, stream,
