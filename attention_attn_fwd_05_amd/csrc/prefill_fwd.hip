@@ -10,7 +10,7 @@
 //   * one workgroup = 8 wave64s = 256 query rows of one q head; each wave owns
 //     32 rows for the whole KV loop (two waves per SIMD).  Dense grids that
 //     256-row blocks would leave at least half empty use 128-row blocks of two
-//     key groups (below).  Packed batches of short sequences use 128-row
+//     (D = 128) or three (D = 64) key groups (below).  Packed batches of short sequences use 128-row
 //     blocks of 4 waves and one key group, two workgroups per CU, with
 //     bitwise the same per-row arithmetic as 256-row blocks.
 //   * KV tiles of 64 rows go from HBM/L2 straight into LDS with buffer-to-LDS
@@ -84,12 +84,14 @@ constexpr int prefill_stages() {
 // MASK 0: every key below Nkv; 1: causal (j <= i + off); 2: a band of keys
 // i + off - win_left <= j <= i + off + win_right (either side may be open).
 // RW: row waves, 32 query rows each (RW = 8: 256-row blocks; RW = 4: 128).
-// KVS: key groups.  With KVS = 2 a workgroup of 8 waves owns 128 rows; waves
-// w and w + 4 share a SIMD and the same 32 rows, and each streams every
-// second key tile of the block's range through a ring of its own, so a grid
-// too small to fill the chip with 256-row blocks still runs two waves per
-// SIMD.  The two groups' (m, l, O) meet in LDS at the end and are merged with
-// the rescale identity of the online softmax.
+// KVS: key groups.  With KVS = 2 (3) a workgroup of 8 (12) waves owns 128
+// rows; waves w, w + 4 (and w + 8) share a SIMD and the same 32 rows, and each
+// streams every second (third) key tile of the block's range through a ring
+// of its own, so a grid too small to fill the chip with 256-row blocks still
+// runs two (three) waves per SIMD.  The groups' (m, l, O) meet in LDS at the
+// end and are merged with the rescale identity of the online softmax.  Three
+// groups are used at D = 64, whose kernel fits in the 168 VGPRs that three
+// waves per SIMD leave.
 template <int D, bool BF16, int MASK, bool VARLEN, int RW, int KVS>
 __global__ __launch_bounds__(64 * RW * KVS) __attribute__((amdgpu_waves_per_eu(KVS == 3 ? 3 : 2)))
 void prefill_fwd_kernel(const FwdArgs a) {
