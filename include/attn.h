@@ -152,7 +152,8 @@ attn_status attn_fwd_masked(const void* q, const void* k, const void* v, void* o
  *        offset, total], so malformed offsets give empty or shortened sequences
  *        but never an access outside the packed tensors.
  *   max_seqlen_q: host bound on the query rows of any sequence; sizes the grid
- *        (ceil(max_seqlen_q/256) query blocks per (sequence, head)).  Query
+ *        (ceil(max_seqlen_q/R) query blocks per (sequence, head), R = 128
+ *        rows when total_q <= 6144 * B, else 256).  Query
  *        rows at positions >= max_seqlen_q within a sequence are not computed
  *        and their o rows and lse entries are left untouched; the mask of the
  *        rows computed is still that of the whole sequence.
