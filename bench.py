@@ -707,8 +707,12 @@ def main():
         out["context"] = {"hbm_copy_gbs": round(copy_gbs, 1),
                           "note": "plain 256 MiB device copy (read+write bytes) on this box: an achievable HBM rate; "
                                   "decode.achieved / hbm_copy_gbs is the fraction of it"}
+        if do_d:
+            out["context"]["decode_frac_of_copy"] = round(res["decode"]["gbs"] / copy_gbs, 4)
         if gemm_tflops is not None:
             out["context"]["fp16_gemm_tflops"] = round(gemm_tflops, 1)
+            if do_p:
+                out["context"]["prefill_frac_of_gemm"] = round(res["prefill"]["tflops"] / gemm_tflops, 4)
             out["context"]["gemm_note"] = ("torch.mm of two 8192 x 8192 fp16 matrices (a library GEMM) on this box: an "
                                            "achievable dense-MFMA rate; roofline.achieved / fp16_gemm_tflops is the "
                                            "fraction of it")
