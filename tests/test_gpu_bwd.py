@@ -176,3 +176,29 @@ def test_bwd_serving_slices(causal):
         _check(f"dK[{b},{kvh}]", dk[b:b + 1, kvh:kvh + 1], rk, torch.float16,
                _floor(128, 4096, do, v.float(), sc, q.float()))
         _check(f"dV[{b},{kvh}]", dv[b:b + 1, kvh:kvh + 1], rv, torch.float16)
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_bwd_remapped_grid_matches_per_unit_calls(causal):
+    """The serving shape (B=2, Hq=32, Hkv=8, N=2048, D=128) runs both backward
+    passes in the XCD-aware block order (its grids split into whole (batch, kv
+    head) units per XCD); each unit run alone (B=1, Hkv=1: a grid too small for
+    that order) must give the same bits for every unit's dQ, dK and dV."""
+    case = W.serving(2048, causal)
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(case))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(W.BASE_SEED + 133)).half().to(DEV)
+    _say(f"{case.name} remapped grid vs per-unit calls")
+    sc = case.softmax_scale
+    o, lse = A.attn_fwd(q, k, v, causal=causal, scale=sc, return_lse=True)
+    dq, dk, dv = A.attn_bwd(q, k, v, o, do, lse, causal=causal, scale=sc)
+    G = case.Hq // case.Hkv
+    for b in range(case.B):
+        for kvh in range(case.Hkv):
+            hs = slice(kvh * G, (kvh + 1) * G)
+            qs, ks, vs = q[b:b + 1, hs].contiguous(), k[b:b + 1, kvh:kvh + 1].contiguous(), v[b:b + 1, kvh:kvh + 1].contiguous()
+            os_, dos, ls = o[b:b + 1, hs].contiguous(), do[b:b + 1, hs].contiguous(), lse[b:b + 1, hs].contiguous()
+            gq, gk, gv = A.attn_bwd(qs, ks, vs, os_, dos, ls, causal=causal, scale=sc)
+            torch.cuda.synchronize()
+            assert torch.equal(gq, dq[b:b + 1, hs]), (b, kvh, "dQ")
+            assert torch.equal(gk, dk[b:b + 1, kvh:kvh + 1]), (b, kvh, "dK")
+            assert torch.equal(gv, dv[b:b + 1, kvh:kvh + 1]), (b, kvh, "dV")
