@@ -31,10 +31,12 @@
 //     when the reference max moves (below); the row sum l is accumulated from
 //     the fp32 P, which then goes to 16 bits (round to nearest even) right
 //     before the P.V MFMA; m, l and O stay fp32.
-//   * the reference max used for exp2 moves -- rescaling O and l by alpha --
-//     only when a row's max exceeds it by more than 2^8.  O and l are always
+//   * P is formed against the current reference max first; the reference
+//     moves -- rescaling O and l by alpha, P formed again -- only when a
+//     row has none yet or a half row's P summed to more than 2^10 on the
+//     tile, so the common path forms no row max at all.  O and l are always
 //     relative to the same reference, so O / l is unchanged (the rescale of
-//     step 5f is an identity); P stays <= 256, well inside fp16/bf16 range.
+//     step 5f is an identity); P stays <= 2^10, well inside fp16/bf16 range.
 //   * causal: the KV loop stops at the block's diagonal; tiles below every
 //     row's diagonal take a path with no per-element compare, and on the last
 //     tiles each wave skips 32-key subtiles that lie wholly above its rows.
@@ -52,7 +54,7 @@ namespace attn {
 namespace {
 
 constexpr int kBN = 64;              // key rows per LDS tile
-constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
+constexpr float kSumBound = 1024.f;  // lazy rescale: bound on a half row's P sum per tile
 // instruction order hints of a tile's two MFMA phases
 constexpr int kKLead = 4;   // K fragment reads issued before the first score MFMA
 constexpr int kVLead = 2;   // V^T fragments (2 reads each) issued before the first P.V MFMA
@@ -352,26 +354,49 @@ void prefill_fwd_kernel(const FwdArgs a) {
         s1[e] = vis1 ? s1[e] : -INFINITY;
       }
     }
-    // this lane's half of its row: the 32 scores as a tree of 3-input maxima
-    // (v_maximum3_f32), 16 instructions
-    float t3[11];
+    // P = exp2(s*c - m) against the current reference, its fp32 row sum and
+    // the 16-bit B operand of P.V: pf[kk] holds keys 16*kk + 8u + 4*hh + t in
+    // k-slot 4u + t
+    u32x4 pf[4];
+    float rs0, rs1;
+    auto exps = [&](float mref) __attribute__((always_inline)) {
+      rs0 = 0.f;
+      rs1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {
-      const int j = 3 * i;
-      const float x0 = j < 16 ? s0[j] : s1[j - 16];
-      const float x1 = j + 1 < 16 ? s0[j + 1] : s1[j + 1 - 16];
-      const float x2 = j + 2 < 16 ? s0[j + 2] : s1[j + 2 - 16];
-      t3[i] = vmax(vmax(x0, x1), x2);
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s0[e], c, -mref));
+        const float p1 = fast_exp2(__builtin_fmaf(s0[e + 1], c, -mref));
+        const float p2 = fast_exp2(__builtin_fmaf(s1[e], c, -mref));
+        const float p3 = fast_exp2(__builtin_fmaf(s1[e + 1], c, -mref));
+        rs0 += p0 + p1;
+        rs1 += p2 + p3;
+        pf[e >> 3][(e & 7) >> 1] = pack2<BF16>(p0, p1);
+        pf[2 + (e >> 3)][(e & 7) >> 1] = pack2<BF16>(p2, p3);
+      }
+    };
+    // the reference moves only when some row has none yet (then P is not
+    // formed against it), or when this lane's half row summed to more than
+    // 2^10 on this tile (every P is then below 2^10 in the common path); the
+    // row's max is formed only then
+    bool move = __any(m == -INFINITY);
+    if (!move) {
+      exps(m);
+      move = __any(rs0 + rs1 > kSumBound);
     }
-    t3[10] = vmax(s1[14], s1[15]);
-    const float u0 = vmax(vmax(t3[0], t3[1]), t3[2]), u1 = vmax(vmax(t3[3], t3[4]), t3[5]);
-    const float u2 = vmax(vmax(t3[6], t3[7]), t3[8]), u3 = vmax(t3[9], t3[10]);
-    const float mx = vmax(vmax(u0, u1), vmax(u2, u3));
-
-    // move the reference max only when some row's max outgrew it by > 2^8.
-    // With c > 0 a row's max (times c) exceeds that bound iff one of its two
-    // halves does, so the common path needs no exchange between the halves
-    if (__any(mx * c > m + kRescaleLog2)) {
+    if (move) {
+      float t3[11];
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        const int j = 3 * i;
+        const float x0 = j < 16 ? s0[j] : s1[j - 16];
+        const float x1 = j + 1 < 16 ? s0[j + 1] : s1[j + 1 - 16];
+        const float x2 = j + 2 < 16 ? s0[j + 2] : s1[j + 2 - 16];
+        t3[i] = vmax(vmax(x0, x1), x2);
+      }
+      t3[10] = vmax(s1[14], s1[15]);
+      const float u0 = vmax(vmax(t3[0], t3[1]), t3[2]), u1 = vmax(vmax(t3[3], t3[4]), t3[5]);
+      const float u2 = vmax(vmax(t3[6], t3[7]), t3[8]), u3 = vmax(t3[9], t3[10]);
+      const float mx = vmax(vmax(u0, u1), vmax(u2, u3));
       const float m_new = fmaxf(m, max_xor32(mx) * c);  // the row's max in the log2 domain
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
 #pragma unroll
@@ -379,28 +404,12 @@ void prefill_fwd_kernel(const FwdArgs a) {
       l *= alpha;
       if constexpr (BF16) lt *= alpha;
       m = m_new;
-    }
-    const float m_use = (m == -INFINITY) ? 0.f : m;  // rows with nothing visible yet get P = 0
-
-    // P = exp2(s*c - m) in fp32, its fp32 row sum, then the 16-bit B operand of
-    // P.V: pf[kk] holds keys 16*kk + 8u + 4*hh + t in k-slot 4u + t
-    u32x4 pf[4];
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float p0 = fast_exp2(__builtin_fmaf(s0[e], c, -m_use));
-      const float p1 = fast_exp2(__builtin_fmaf(s0[e + 1], c, -m_use));
-      const float p2 = fast_exp2(__builtin_fmaf(s1[e], c, -m_use));
-      const float p3 = fast_exp2(__builtin_fmaf(s1[e + 1], c, -m_use));
-      rs0 += p0 + p1;
-      rs1 += p2 + p3;
-      pf[e >> 3][(e & 7) >> 1] = pack2<BF16>(p0, p1);
-      pf[2 + (e >> 3)][(e & 7) >> 1] = pack2<BF16>(p2, p3);
+      exps(m == -INFINITY ? 0.f : m);  // rows with nothing visible yet get P = 0
     }
     l += rs0 + rs1;
     if constexpr (BF16) {
       // a bf16 P carries 8 significant bits and, under the lazy rescale, can
-      // reach 2^8: normalising O by the sum of the rounded values makes O a
+      // reach 2^10: normalising O by the sum of the rounded values makes O a
       // convex combination of V rows, so the rounding of a dominant P cancels
       // between O and its normaliser instead of scaling O by up to 2^-9
 #pragma unroll

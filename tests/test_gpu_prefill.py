@@ -86,10 +86,11 @@ def test_reference_max_moves_every_tile(B, Hq, Hkv, dtype, causal, D):
     check_o(og.cpu(), Oref, case.torch_dtype)
     check_lse(lg.cpu(), Lref)
     # the inputs do what they are for: the last row's scores outgrow those of
-    # the first 64-key tile by far more than 2^8
+    # the first 64-key tile by far more than 2^10 (the kernel's rescale bound
+    # on a tile's P sum)
     _, l_first = oracle.attention_forward(_np(q[:, :, -1:]), _np(k[:, :, :64]), _np(v[:, :, :64]),
                                           case.softmax_scale, False)
-    assert float((Lref[..., -1] - l_first[..., 0]).min()) > 8 * math.log(2)
+    assert float((Lref[..., -1] - l_first[..., 0]).min()) > 10 * math.log(2)
 
 
 def test_cross_mqa_bf16():
