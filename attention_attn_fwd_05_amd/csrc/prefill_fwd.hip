@@ -111,6 +111,14 @@ void prefill_fwd_kernel(const FwdArgs a) {
   static_assert(NB >= 1, "every wave loads at least one block");
   constexpr int RPB = 64 / L::C;    // rows per 1 KiB block
   __shared__ __attribute__((aligned(1024))) uint16_t smem[KVS * L::ELEMS];
+  // masked grids with one key group and four stages keep the ring with
+  // counters in LDS instead of a barrier per tile (KV loop below)
+  constexpr bool kCounted = KVS == 1 && kStages == 4 && MASK != 0;
+  __shared__ uint32_t ring_cnt[9];
+  if constexpr (kCounted) {
+    if (threadIdx.x < 9) ring_cnt[threadIdx.x] = 0;
+    __syncthreads();
+  }
 
   // ---- which (batch, q head, query block) this workgroup owns
   const int bid = blockIdx.x;
@@ -297,14 +305,17 @@ void prefill_fwd_kernel(const FwdArgs a) {
     }
   };
 
-  auto compute = [&](auto stage_tag, int t, auto masked_tag) {
+  // mid() runs once per tile on every path, after the score MFMAs
+  auto compute = [&](auto stage_tag, int t, auto masked_tag, auto&& mid) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int STG = decltype(stage_tag)::value;
     const int kb = t * kBN;
     bool act1 = true;
     if constexpr (MASKED) {
-      if (kb >= Nkv || (CAUSAL && kb > wq_hi)) return;  // whole tile above this wave's rows
-      if (BAND && (kb > wq_hi + WR || kb + kBN - 1 < wq_lo - WL)) return;  // outside this wave's band
+      if (kb >= Nkv || (CAUSAL && kb > wq_hi) || (BAND && (kb > wq_hi + WR || kb + kBN - 1 < wq_lo - WL))) {
+        mid();
+        return;
+      }
       act1 = kb + 32 < Nkv && (!CAUSAL || kb + 32 <= wq_hi) && (!BAND || kb + 32 <= wq_hi + WR);
     }
     // S^T = K Q^T for the two 32-key subtiles; score register e of lane
@@ -328,6 +339,7 @@ void prefill_fwd_kernel(const FwdArgs a) {
         for (int ks = 0; ks < KS; ++ks) s0 = mfma_32x32x16<BF16>(lds_load16(ka[ks] + off0), qf[ks], s0);
       }
     }
+    mid();
 
     if constexpr (MASKED) {
       // mask before the row max.  Score register e of this lane holds key
@@ -451,9 +463,10 @@ void prefill_fwd_kernel(const FwdArgs a) {
   //      land.  After computing tile t a wave waits until only the loads of the
   //      group's tiles past its next one are outstanding (the next tile is in
   //      LDS), and the barrier publishes it to the workgroup; the stage
-  //      refilled next was last read before that barrier.  Full tiles go in
-  //      groups of kStages (stages 0 .. kStages-1); the rest (diagonal / key
-  //      tail / band edges) take the masked path.
+  //      refilled next was last read before that barrier (masked grids with
+  //      one key group replace the barrier by the counted ring below).  Full
+  //      tiles go in groups of kStages (stages 0 .. kStages-1); the rest
+  //      (diagonal / key tail / band edges) take the masked path.
   constexpr int NDMA = 2 * NB;  // DMA instructions per wave per tile
   static_assert(kStages == 2 || (kStages - 2) * NDMA < 64, "vmcnt field");
   // s_waitcnt immediate for vmcnt <= vm (gfx9 encoding: vmcnt bits 3:0 and
@@ -471,19 +484,77 @@ void prefill_fwd_kernel(const FwdArgs a) {
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);
   };
+  // ---- counted ring (masked grids): per stage, the number of waves that
+  //      have published their part of the stage's tile (`landed`) and the
+  //      number done reading it (`read`), both counting up over the stage's
+  //      reuses.  A wave starts its k-th tile once all waves have published
+  //      it, publishes its own part of tile k+1 (its loads of it waited for)
+  //      after tile k's scores, and after tile k refills the stage of tile
+  //      k-1 with tile k+3 once all waves have read k-1.  A wave can thus run
+  //      up to a tile ahead of the slowest: on diagonal and band-edge tiles
+  //      the waves of a block have unequal work (subtiles above a wave's
+  //      rows are skipped), and a barrier per tile made each of them cost
+  //      its slowest wave.  Every wait is bounded; one that runs out sets
+  //      the block's failure word, and the block's output is written as NaN.
+  const uint32_t landed = lds_addr(reinterpret_cast<const uint16_t*>(ring_cnt));
+  const uint32_t read = landed + 16;
+  const uint32_t failed = landed + 32;
+  auto wait_count = [&](uint32_t addr, uint32_t target) __attribute__((always_inline)) {
+    int i = 0;
+#pragma nounroll
+    for (; i < (1 << 18); ++i) {
+      uint32_t v;
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+      if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (i == (1 << 18) && lane == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(failed), "v"(1u) : "memory");
+    asm volatile("" ::: "memory");  // no LDS access moves above the wait
+  };
+  // a wave's LDS instructions are served in issue order, so its reads of a
+  // stage are done before its count of that stage goes up
+  auto count_up = [&](uint32_t addr) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
+  };
   auto step = [&](int tt, auto stage_tag, auto masked_tag) {
     constexpr int STG = decltype(stage_tag)::value;
-    if (tt + KVS * (kStages - 1) < ntiles) dma_tile(tt + KVS * (kStages - 1), (STG + kStages - 1) % kStages);
-    compute(stage_tag, tt, masked_tag);
-    wait_next(tt);
-    barrier_nofence();
+    if constexpr (kCounted) {
+      const int k = tt - first;  // the group's k-th tile, in stage k % 4
+      wait_count(landed + 4 * STG, kWaves * (k / 4 + 1));
+      compute(stage_tag, tt, masked_tag, [&]() __attribute__((always_inline)) {
+        if (tt + 1 < ntiles) {
+          // this wave's loads of tile k+1 have landed once at most those of
+          // tile k+2 are outstanding
+          if (tt + 2 < ntiles)
+            __builtin_amdgcn_s_waitcnt(kVm1);
+          else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+          count_up(landed + 4 * ((STG + 1) % 4));
+        }
+      });
+      count_up(read + 4 * STG);
+      if (tt + 3 < ntiles) {
+        if (k >= 1) wait_count(read + 4 * ((STG + 3) % 4), kWaves * ((k - 1) / 4 + 1));
+        dma_tile(tt + 3, (STG + 3) % 4);
+      }
+    } else {
+      if (tt + KVS * (kStages - 1) < ntiles) dma_tile(tt + KVS * (kStages - 1), (STG + kStages - 1) % kStages);
+      compute(stage_tag, tt, masked_tag, []() {});
+      wait_next(tt);
+      barrier_nofence();
+    }
   };
   // the group's k-th tile sits in ring stage k % kStages
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
     if (first + KVS * i < ntiles) dma_tile(first + KVS * i, i);
   wait_next(first - KVS);
-  barrier_nofence();
+  if constexpr (kCounted) {
+    if (first < ntiles) count_up(landed);
+  } else {
+    barrier_nofence();
+  }
   int t = first;
   auto masked_step = [&](int tt) __attribute__((always_inline)) {
     const int r = ((tt - first) / KVS) % kStages;
@@ -570,8 +641,15 @@ void prefill_fwd_kernel(const FwdArgs a) {
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int hh_e = lane_e >> 5;
   const int qrow_e = q0 + 32 * w + (lane_e & 31);
+  // a counted ring whose wait ran out: the block's output is not to be trusted
+  bool lost = false;
+  if constexpr (kCounted) {
+    uint32_t f;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f) : "v"(failed) : "memory");
+    lost = __builtin_amdgcn_readfirstlane(f) != 0;
+  }
   if (qrow_e < Nq) {
-    const float inv = (ln > 0.f) ? 1.f / ln : 0.f;
+    const float inv = lost ? __builtin_nanf("") : (ln > 0.f) ? 1.f / ln : 0.f;
     uint16_t* op = obase + (int64_t)qrow_e * a.son;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -583,7 +661,8 @@ void prefill_fwd_kernel(const FwdArgs a) {
         *reinterpret_cast<u32x2*>(op + d) = v2;
       }
     }
-    if (lbase != nullptr && hh_e == 0) lbase[qrow_e] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    if (lbase != nullptr && hh_e == 0)
+      lbase[qrow_e] = lost ? __builtin_nanf("") : (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
