@@ -11,6 +11,7 @@
 #include <initializer_list>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "launch.hpp"
 
@@ -33,6 +34,19 @@ constexpr int kDecodeTargetWorkgroups = 512;  // decode workgroups that fill MI3
 constexpr int kDecodeVarlenChunkTiles = 6;
 constexpr int kDecodePartPad = 4;       // floats ahead of o[D] in a per-head partial
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Polls a wait of the prefill's counted KV ring (masked grids) makes before
+// it gives up and the workgroup writes its rows as NaN.  A correct run never
+// comes near the default; the environment variable ATTN_RING_POLL_LIMIT
+// (read on every call, clamped to [1, 2^18]) lowers it, so that tests can
+// drive that path.
+inline int ring_poll_limit() {
+  constexpr int kDefault = 1 << 18;
+  const char* e = std::getenv("ATTN_RING_POLL_LIMIT");
+  if (e == nullptr || *e == 0) return kDefault;
+  const long v = std::strtol(e, nullptr, 10);
+  return (int)std::min<long>(std::max<long>(v, 1), kDefault);
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -178,6 +192,7 @@ static attn_status fwd_impl(const void* q, const void* k, const void* v, void* o
   if (nblocks > INT_MAX) return ATTN_ERR_SHAPE;
 
   attn::FwdArgs a{};
+  a.ring_polls = ring_poll_limit();
   a.rows = rows;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -263,6 +278,7 @@ static attn_status fwd_varlen_impl(const void* q, const void* k, const void* v, 
   if (nblocks > INT_MAX) return ATTN_ERR_SHAPE;
 
   attn::FwdArgs a{};
+  a.ring_polls = ring_poll_limit();
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);

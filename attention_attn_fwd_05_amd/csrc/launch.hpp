@@ -40,6 +40,7 @@ struct FwdArgs {
   // i + off + win_right; -1 leaves that side open
   int win_left, win_right;
   int rows;  // query rows per workgroup: 256; 128 for dense grids that 256-row blocks leave half empty and for packed batches of short sequences
+  int ring_polls;  // masked grids' counted KV ring: polls a wait makes before it gives up
 };
 
 // mask: 0 none, 1 causal, 2 band

@@ -494,21 +494,23 @@ void prefill_fwd_kernel(const FwdArgs a) {
   //      up to a tile ahead of the slowest: on diagonal and band-edge tiles
   //      the waves of a block have unequal work (subtiles above a wave's
   //      rows are skipped), and a barrier per tile made each of them cost
-  //      its slowest wave.  Every wait is bounded; one that runs out sets
-  //      the block's failure word, and the block's output is written as NaN.
+  //      its slowest wave.  Every wait is bounded (a.ring_polls polls); one that
+  //      runs out sets the block's failure word, and the block's output is
+  //      written as NaN.
   const uint32_t landed = lds_addr(reinterpret_cast<const uint16_t*>(ring_cnt));
   const uint32_t read = landed + 16;
   const uint32_t failed = landed + 32;
   auto wait_count = [&](uint32_t addr, uint32_t target) __attribute__((always_inline)) {
+    const int limit = a.ring_polls;
     int i = 0;
 #pragma nounroll
-    for (; i < (1 << 18); ++i) {
+    for (; i < limit; ++i) {
       uint32_t v;
       asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
       if (__builtin_amdgcn_readfirstlane(v) >= target) break;
       __builtin_amdgcn_s_sleep(1);
     }
-    if (i == (1 << 18) && lane == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(failed), "v"(1u) : "memory");
+    if (i == limit && lane == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(failed), "v"(1u) : "memory");
     asm volatile("" ::: "memory");  // no LDS access moves above the wait
   };
   // a wave's LDS instructions are served in issue order, so its reads of a

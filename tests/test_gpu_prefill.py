@@ -308,3 +308,40 @@ def test_small_grid_key_split_matches_large_grid(causal, align, window, D, dtype
     assert d <= O_TOL[dt], d
     rel = float(((l1[0] - l8[0]).abs() / l8[0].abs().clamp(min=1.0)).max())
     assert rel <= 1e-5, rel
+
+
+@pytest.mark.parametrize("window", [None, (300, -1)], ids=["causal", "window300"])
+def test_counted_ring_poll_limit(monkeypatch, window):
+    """Masked grids keep their KV ring with counters in LDS, and every wait on
+    them is bounded.  With the bound cut to one poll (ATTN_RING_POLL_LIMIT=1,
+    forced from the host) waits run out: the kernel still finishes, and each
+    256-row block either writes NaN for all its rows (O and lse), or, when
+    none of its waits ran out, exactly the result of a normal call.  No block
+    returns finite numbers computed from a tile that had not landed."""
+    case = W.PrefillCase("ring_poll1", 2, 16, 4, 2048, 2048, 128, "fp16", True, seed=W.BASE_SEED + 180)
+    q, k, v = (t.to(DEV) for t in W.prefill_inputs(case))
+    _say(f"{case.name} window={window} (256-row blocks, counted ring)")
+    kw = dict(causal=True, scale=case.softmax_scale, return_lse=True, window=window)
+    o_ref, l_ref = A.attn_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("ATTN_RING_POLL_LIMIT", "1")
+    o, l = A.attn_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("ATTN_RING_POLL_LIMIT")
+    nan_blocks = 0
+    for b in range(case.B):
+        for h in range(case.Hq):
+            for r0 in range(0, case.Nq, 256):
+                ob, lb = o[b, h, r0:r0 + 256], l[b, h, r0:r0 + 256]
+                if torch.isnan(lb).any():
+                    assert torch.isnan(lb).all() and torch.isnan(ob).all(), (b, h, r0)
+                    nan_blocks += 1
+                else:
+                    assert torch.equal(ob, o_ref[b, h, r0:r0 + 256]), (b, h, r0)
+                    assert torch.equal(lb, l_ref[b, h, r0:r0 + 256]), (b, h, r0)
+    print(f"    {nan_blocks} of {case.B * case.Hq * case.Nq // 256} blocks ran out of polls", flush=True)
+    assert nan_blocks > 0  # one poll is far too few for the waves of a block to meet
+    # the same call without the limit is back to the normal result
+    o2, l2 = A.attn_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_ref) and torch.equal(l2, l_ref)
