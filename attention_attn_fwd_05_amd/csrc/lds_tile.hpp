@@ -55,6 +55,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
 // 16 bytes from LDS byte address `addr`
 __device__ __forceinline__ u32x4 lds_load16(uint32_t addr) { return *(lds_u32x4*)addr; }
 
+// 8 bytes to LDS byte address `addr`
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+__device__ __forceinline__ void lds_store8(uint32_t addr, u32x2 v) { *(lds_u32x2*)(uintptr_t)addr = v; }
+
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t*)p;
 }

@@ -650,22 +650,40 @@ void prefill_fwd_kernel(const FwdArgs a) {
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f) : "v"(failed) : "memory");
     lost = __builtin_amdgcn_readfirstlane(f) != 0;
   }
-  if (qrow_e < Nq) {
-    const float inv = lost ? __builtin_nanf("") : (ln > 0.f) ? 1.f / ln : 0.f;
-    uint16_t* op = obase + (int64_t)qrow_e * a.son;
+  // O goes through LDS so that the stores cover whole rows: a lane holds
+  // half of its row's columns in 8-byte pieces, which stored directly would
+  // touch 32 rows per instruction.  Each wave stages its 32 rows (2D bytes
+  // each, 16-byte chunk c of row r at slot c ^ (r mod CPR), which keeps the
+  // writes and the row reads free of bank conflicts beyond two-way) in LDS
+  // of its own: a slice of the ring once every wave is done with it (one
+  // key group), or its merge slot (several).
+  const float inv = lost ? __builtin_nanf("") : (ln > 0.f) ? 1.f / ln : 0.f;
+  constexpr int RB = 2 * D;     // bytes per row
+  constexpr int CPR = RB / 16;  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR; // rows per 64-lane read
+  if constexpr (kCounted) barrier_nofence();  // the ring: every wave past its last tile
+  const uint32_t stg = lds_addr(smem) + (KVS == 1 ? w * 32 * RB : w * (1 + 4 * DT) * 1024);
+  {
+    const int n_e = lane_e & 31;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hh_e;
+        const int c = 4 * dt + g;
         const u32x2 v2{pack2<BF16>(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
                        pack2<BF16>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d) = v2;
+        lds_store8(stg + n_e * RB + 16 * (c ^ (n_e % CPR)) + 8 * hh_e, v2);
       }
-    }
-    if (lbase != nullptr && hh_e == 0)
-      lbase[qrow_e] = lost ? __builtin_nanf("") : (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
   }
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane_e / CPR, c = lane_e % CPR;
+    const u32x4 v4 = lds_load16(stg + r * RB + 16 * (c ^ (r % CPR)));
+    const int row = q0 + 32 * w + r;
+    if (row < Nq) store16(obase + (int64_t)row * a.son + 8 * c, v4);
+  }
+  if (qrow_e < Nq && lbase != nullptr && hh_e == 0)
+    lbase[qrow_e] = lost ? __builtin_nanf("") : (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 // 128-row blocks: dense grids too small for 256-row blocks take two key groups
