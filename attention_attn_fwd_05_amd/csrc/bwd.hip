@@ -372,19 +372,11 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
     barrier_nofence();
   }
 
-  // ---- dQ = scale (dQ^T)^T, cast, store
-  if (qrow < Nq) {
-    uint16_t* op = a.dq + (VARLEN ? bq * a.sdqn : (int64_t)b * a.sdqb) + (int64_t)h * a.sdqh + (int64_t)qrow * a.sdqn;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hh;
-        *reinterpret_cast<u32x2*>(op + d) =
-            u32x2{pack2<BF16>(acc[dt][4 * g] * a.scale, acc[dt][4 * g + 1] * a.scale),
-                  pack2<BF16>(acc[dt][4 * g + 2] * a.scale, acc[dt][4 * g + 3] * a.scale)};
-      }
-  }
+  // ---- dQ = scale (dQ^T)^T, cast, stored as whole rows through the wave's
+  //      slice of the ring (every wave is past the last barrier)
+  uint16_t* const dqb = a.dq + (VARLEN ? bq * a.sdqn : (int64_t)b * a.sdqb) + (int64_t)h * a.sdqh;
+  static_assert(kDqW * 32 * 2 * D <= L::ELEMS * 2, "every wave's rows fit in the ring");
+  store_tile_rows<D, BF16>(lds_addr(smem) + w * 32 * 2 * D, acc, a.scale, dqb, a.sdqn, q0 + 32 * w, Nq);
 }
 
 // ---- dK, dV: one workgroup per (batch, kv head, 128 keys).  Wave w owns keys

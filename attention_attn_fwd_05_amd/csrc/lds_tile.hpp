@@ -1,7 +1,7 @@
 // LDS tile helpers shared by the prefill and backward kernels (gfx950 only):
 // the XOR swizzle of row-major K/V (or Q/dO) tiles, transposing and plain LDS
-// reads, buffer-to-LDS loads issued as inline assembly, and a fence-free
-// workgroup barrier.
+// reads, buffer-to-LDS loads issued as inline assembly, whole-row stores of an
+// accumulator tile through LDS, and a fence-free workgroup barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -91,6 +91,48 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, int32_t bytes) {
 // fenced barrier.  The ring's explicit vmcnt waits and barriers order it.
 __device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds_base, int32_t voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds_base));
+}
+
+// Stores a wave's 32 x D tile of 16-bit values as whole rows.  The tile is a
+// transposed-MFMA accumulator: lane (n, hh) = (l % 32, l / 32) holds row n,
+// columns 32 dt + 8 g + 4 hh + j in acc[dt][4 g + j]; each value is
+// multiplied by `mul` (the lane's own factor) and rounded to 16 bits.
+// Stored directly, every instruction would touch 32 rows in 8-byte pieces;
+// instead the tile goes through `stg`, 32 * 2D bytes of LDS that no other
+// wave uses meanwhile, and back as 16-byte chunks of whole rows, 4 (D = 128)
+// or 8 (D = 64) rows per instruction.  Rows r with row0 + r < nrows go to
+// base + (row0 + r) * stride.  The 8-byte piece s of row r sits at slot
+// s ^ X(r), X(r) = r mod 32 (D = 128, a row per 256 bytes of banks) or
+// r/2 mod 16 (D = 64, two rows per 256 bytes): the 32 rows' pieces of one
+// write fill all 64 banks, and a 16-byte chunk c then sits at c ^ X(r)/2,
+// its halves swapped when X(r) is odd, so the row reads are conflict free.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_tile_rows(uint32_t stg, const f32x16 (&acc)[D / 32], float mul, uint16_t* base,
+                                                int64_t stride, int row0, int nrows) {
+  constexpr int RB = 2 * D;      // bytes per row
+  constexpr int CPR = RB / 16;   // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per 64-lane read
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  auto xs = [](int r) { return D == 128 ? (r & 31) : ((r >> 1) & 15); };
+  {
+    const int n = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 4 * dt + g;
+        const u32x2 v2{pack2<BF16>(acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul),
+                       pack2<BF16>(acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul)};
+        lds_store8(stg + n * RB + 8 * ((2 * c + hh) ^ xs(n)), v2);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / CPR, c = lane % CPR;
+    u32x4 v4 = lds_load16(stg + r * RB + 16 * (c ^ (xs(r) >> 1)));
+    if (xs(r) & 1) v4 = u32x4{v4[2], v4[3], v4[0], v4[1]};
+    if (row0 + r < nrows) store16(base + (int64_t)(row0 + r) * stride + 8 * c, v4);
+  }
 }
 
 // workgroup barrier without a memory fence: a tile's loads are waited for

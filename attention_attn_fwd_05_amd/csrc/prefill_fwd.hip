@@ -650,43 +650,15 @@ void prefill_fwd_kernel(const FwdArgs a) {
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(f) : "v"(failed) : "memory");
     lost = __builtin_amdgcn_readfirstlane(f) != 0;
   }
-  // O goes through LDS so that the stores cover whole rows: a lane holds
-  // half of its row's columns in 8-byte pieces, which stored directly would
-  // touch 32 rows per instruction.  Each wave stages its 32 rows (2D bytes
-  // each) in LDS of its own: a slice of the ring once every wave is done
-  // with it (one key group), or its merge slot (several).  The 8-byte piece
-  // s of row r sits at slot s ^ X(r), X(r) = r mod 32 (D = 128, a row per
-  // 256 bytes of banks) or r/2 mod 16 (D = 64, two rows per 256 bytes), so
-  // the 32 rows' pieces of one write fill all 64 banks; a 16-byte chunk c
-  // then sits at c ^ X(r)/2 with its halves swapped when X(r) is odd, and
-  // the row reads are conflict free too.
+  // O goes through LDS so that the stores cover whole rows: the wave's own
+  // slice of the ring once every wave is done with it (one key group), or
+  // its merge slot (several)
   const float inv = lost ? __builtin_nanf("") : (ln > 0.f) ? 1.f / ln : 0.f;
-  constexpr int RB = 2 * D;     // bytes per row
-  constexpr int CPR = RB / 16;  // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR; // rows per 64-lane read
   if constexpr (kCounted) barrier_nofence();  // the ring: every wave past its last tile
-  const uint32_t stg = lds_addr(smem) + (KVS == 1 ? w * 32 * RB : w * (1 + 4 * DT) * 1024);
-  auto xs = [](int r) { return D == 128 ? (r & 31) : ((r >> 1) & 15); };
-  {
-    const int n_e = lane_e & 31;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = 4 * dt + g;
-        const u32x2 v2{pack2<BF16>(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
-                       pack2<BF16>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
-        lds_store8(stg + n_e * RB + 8 * ((2 * c + hh_e) ^ xs(n_e)), v2);
-      }
-  }
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = RPI * i + lane_e / CPR, c = lane_e % CPR;
-    u32x4 v4 = lds_load16(stg + r * RB + 16 * (c ^ (xs(r) >> 1)));
-    if (xs(r) & 1) v4 = u32x4{v4[2], v4[3], v4[0], v4[1]};
-    const int row = q0 + 32 * w + r;
-    if (row < Nq) store16(obase + (int64_t)row * a.son + 8 * c, v4);
-  }
+  const uint32_t stg = lds_addr(smem) + (KVS == 1 ? w * 32 * 2 * D : w * (1 + 4 * DT) * 1024);
+  static_assert(KVS > 1 || kWaves * 32 * 2 * D <= L::ELEMS * 2, "every wave's rows fit in the ring");
+  static_assert(KVS == 1 || (1 + 4 * DT) * 1024 >= 32 * 2 * D, "a wave's rows fit in its merge slot");
+  store_tile_rows<D, BF16>(stg, oacc, inv, obase, a.son, q0 + 32 * w, Nq);
   if (qrow_e < Nq && lbase != nullptr && hh_e == 0)
     lbase[qrow_e] = lost ? __builtin_nanf("") : (l > 0.f) ? (m + __log2f(l)) * kLn2 : -INFINITY;
 }
