@@ -10,15 +10,19 @@
 //   * one workgroup = 8 wave64s = 256 query rows of one q head; each wave owns
 //     32 rows for the whole KV loop (two waves per SIMD).  Dense grids that
 //     256-row blocks would leave at least half empty use 128-row blocks of two
-//     (D = 128) or three (D = 64) key groups (below).  Packed batches of short sequences use 128-row
-//     blocks of 4 waves and one key group, two workgroups per CU, with
-//     bitwise the same per-row arithmetic as 256-row blocks.
+//     (D = 128) or three (D = 64) key groups (below).  Packed batches of
+//     short sequences use 128-row blocks of 4 waves and one key group, two
+//     workgroups per CU, with bitwise the same per-row arithmetic as 256-row
+//     blocks.
 //   * KV tiles of 64 rows go from HBM/L2 straight into LDS with buffer-to-LDS
 //     loads (no register staging), through a 4-stage ring, row-major with an
 //     XOR swizzle of 16-byte slots that keeps every access pattern free of bank
 //     conflicts.  The loads of tile t+3 are issued before tile t is computed;
 //     the buffer range check writes zeros past the last key, so ragged tails
-//     need no branches.
+//     need no branches.  Unmasked grids keep the ring with a barrier per
+//     tile; masked ones with counters in LDS, so that the waves of a block,
+//     whose work differs on diagonal and band-edge tiles, need not wait for
+//     each other on every tile.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //     Q is the register-resident B operand and each lane ends up owning one
 //     query row's scores.  The P.V MFMA takes V^T as its A operand, assembled
@@ -37,6 +41,8 @@
 //     tile, so the common path forms no row max at all.  O and l are always
 //     relative to the same reference, so O / l is unchanged (the rescale of
 //     step 5f is an identity); P stays <= 2^10, well inside fp16/bf16 range.
+//   * the epilogue stores O as whole rows, through LDS: a lane holds half of
+//     its row's columns, which stored directly would touch 32 rows per store.
 //   * causal: the KV loop stops at the block's diagonal; tiles below every
 //     row's diagonal take a path with no per-element compare, and on the last
 //     tiles each wave skips 32-key subtiles that lie wholly above its rows.
