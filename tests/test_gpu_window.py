@@ -58,6 +58,13 @@ BANDS = [
     ("br_left_int_max_q_longer", 1, 4, 2, 700, 300, 128, "fp16", "bottom_right", True, (2 ** 31 - 1, -1)),
     ("both_sides_int_max", 1, 4, 4, 257, 513, 64, "bf16", "bottom_right", False, (2 ** 31 - 1, 2 ** 31 - 1)),
     ("left_int_max_right_5", 1, 4, 2, 500, 500, 128, "fp16", "top_left", False, (2 ** 31 - 1, 5)),
+    # grids of more than 128 blocks of 256 rows, so masked ones keep their KV
+    # ring with counters instead of barriers: a block whose rows see no key
+    # runs no tile at all; one key per row; a 4-key window; a two-sided band
+    ("grid_br_q_longer", 4, 16, 4, 700, 300, 128, "fp16", "bottom_right", True, (-1, -1)),
+    ("grid_diagonal_only", 4, 16, 4, 600, 600, 64, "bf16", "top_left", False, (0, 0)),
+    ("grid_br_window3", 4, 16, 4, 600, 900, 128, "fp16", "bottom_right", True, (3, -1)),
+    ("grid_two_sided", 4, 16, 2, 777, 777, 64, "fp16", "top_left", False, (100, 37)),
 ]
 
 
