@@ -32,6 +32,13 @@
  *     any error nothing is launched and no memory is touched ([P3] GQA phase:
  *     unsupported cases must refuse rather than run silently).  Errors are
  *     returned, never thrown.
+ *   - Causal and band prefill calls (attn_fwd, attn_fwd_masked and their
+ *     packed forms) whose blocks run 256 rows coordinate the waves of a block
+ *     through counters in LDS, with bounded waits.  A correct run never
+ *     reaches the bound; if a wait ever ran out, that block writes NaN to all
+ *     of its o rows and lse entries instead of values it could not trust.  The
+ *     environment variable ATTN_RING_POLL_LIMIT (read on every call, clamped
+ *     to [1, 2^18], default 2^18) lowers the bound, for tests of that path.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
