@@ -20,9 +20,9 @@
 //     conflicts.  The loads of tile t+3 are issued before tile t is computed;
 //     the buffer range check writes zeros past the last key, so ragged tails
 //     need no branches.  Unmasked grids keep the ring with a barrier per
-//     tile; masked ones with counters in LDS, so that the waves of a block,
-//     whose work differs on diagonal and band-edge tiles, need not wait for
-//     each other on every tile.
+//     tile; band grids with counters in LDS, and causal ones with counters on
+//     their diagonal tiles: there the waves of a block have unequal work and
+//     need not wait for each other on every tile.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //     Q is the register-resident B operand and each lane ends up owning one
 //     query row's scores.  The P.V MFMA takes V^T as its A operand, assembled
@@ -500,9 +500,14 @@ void prefill_fwd_kernel(const FwdArgs a) {
   //      up to a tile ahead of the slowest: on diagonal and band-edge tiles
   //      the waves of a block have unequal work (subtiles above a wave's
   //      rows are skipped), and a barrier per tile made each of them cost
-  //      its slowest wave.  Every wait is bounded (a.ring_polls polls); one that
-  //      runs out sets the block's failure word, and the block's output is
-  //      written as NaN.
+  //      its slowest wave.  Causal blocks keep the barrier protocol for their
+  //      full tiles (where no wave has less work, and a barrier costs less
+  //      than the counters) and count only on the diagonal ones; band blocks
+  //      count on every tile.  Each wave tallies what all waves have added
+  //      (exp_landed, exp_read); a tile right after a barrier needs no wait,
+  //      and a full tile after counted ones takes a barrier first.  Every
+  //      wait is bounded (a.ring_polls polls); one that runs out sets the
+  //      block's failure word, and the block's output is written as NaN.
   const uint32_t landed = lds_addr(reinterpret_cast<const uint16_t*>(ring_cnt));
   const uint32_t read = landed + 16;
   const uint32_t failed = landed + 32;
@@ -525,27 +530,45 @@ void prefill_fwd_kernel(const FwdArgs a) {
     asm volatile("" ::: "memory");
     if (lane == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(1u) : "memory");
   };
+  // each wave's tally of what all waves have added to the counters, whether
+  // the last step ended on a barrier, and whether it was counted
+  uint32_t exp_landed[4] = {0, 0, 0, 0}, exp_read[4] = {0, 0, 0, 0};
+  bool synced = true, prev_counted = false;
   auto step = [&](int tt, auto stage_tag, auto masked_tag) {
     constexpr int STG = decltype(stage_tag)::value;
-    if constexpr (kCounted) {
-      const int k = tt - first;  // the group's k-th tile, in stage k % 4
-      wait_count(landed + 4 * STG, kWaves * (k / 4 + 1));
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (kCounted && (MASKED || !CAUSAL)) {
+      // a tile right after a barrier is in LDS for every wave already
+      if (!synced) wait_count(landed + 4 * STG, exp_landed[STG]);
       compute(stage_tag, tt, masked_tag, [&]() __attribute__((always_inline)) {
         if (tt + 1 < ntiles) {
-          // this wave's loads of tile k+1 have landed once at most those of
-          // tile k+2 are outstanding
           if (tt + 2 < ntiles)
             __builtin_amdgcn_s_waitcnt(kVm1);
           else
             __builtin_amdgcn_s_waitcnt(0x0F70);
           count_up(landed + 4 * ((STG + 1) % 4));
+          exp_landed[(STG + 1) % 4] += kWaves;
         }
       });
       count_up(read + 4 * STG);
+      exp_read[STG] += kWaves;
       if (tt + 3 < ntiles) {
-        if (k >= 1) wait_count(read + 4 * ((STG + 3) % 4), kWaves * ((k - 1) / 4 + 1));
+        // the stage of the previous tile: after a barrier every wave is done with it
+        if (prev_counted) wait_count(read + 4 * ((STG + 3) % 4), exp_read[(STG + 3) % 4]);
         dma_tile(tt + 3, (STG + 3) % 4);
       }
+      synced = false;
+      prev_counted = true;
+    } else if constexpr (kCounted) {
+      // a full tile of a causal block: the barrier protocol, after a barrier
+      // if the last step was counted
+      if (!synced) barrier_nofence();
+      if (tt + 3 < ntiles) dma_tile(tt + 3, (STG + 3) % 4);
+      compute(stage_tag, tt, masked_tag, []() {});
+      wait_next(tt);
+      barrier_nofence();
+      synced = true;
+      prev_counted = false;
     } else {
       if (tt + KVS * (kStages - 1) < ntiles) dma_tile(tt + KVS * (kStages - 1), (STG + kStages - 1) % kStages);
       compute(stage_tag, tt, masked_tag, []() {});
@@ -558,11 +581,7 @@ void prefill_fwd_kernel(const FwdArgs a) {
   for (int i = 0; i < kStages - 1; ++i)
     if (first + KVS * i < ntiles) dma_tile(first + KVS * i, i);
   wait_next(first - KVS);
-  if constexpr (kCounted) {
-    if (first < ntiles) count_up(landed);
-  } else {
-    barrier_nofence();
-  }
+  barrier_nofence();
   int t = first;
   auto masked_step = [&](int tt) __attribute__((always_inline)) {
     const int r = ((tt - first) / KVS) % kStages;
