@@ -48,12 +48,12 @@ typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 // lanes: lane i of a group receives element i % 4 of the 8-byte pieces
 // addressed by lanes 4r + i/4 (r = 0..3) of its group.
 __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
   return __builtin_bit_cast(u32x2, v);
 }
 
 // 16 bytes from LDS byte address `addr`
-__device__ __forceinline__ u32x4 lds_load16(uint32_t addr) { return *(lds_u32x4*)addr; }
+__device__ __forceinline__ u32x4 lds_load16(uint32_t addr) { return *(lds_u32x4*)(uintptr_t)addr; }
 
 // 8 bytes to LDS byte address `addr`
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
