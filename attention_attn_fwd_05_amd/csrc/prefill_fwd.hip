@@ -157,7 +157,11 @@ void prefill_fwd_kernel(const FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave 0..kWaves-1 (uniform)
-  const int w = KVS == 1 ? wv : wv % RW;   // row wave: rows 32 w .. 32 w + 31 of the block
+  // row wave: rows 32 w .. 32 w + 31 of the block.  Waves wv and wv + 4 share
+  // a SIMD; in 256-row blocks they take row slices wv and 7 - wv, so that on
+  // diagonal and band-edge tiles, where a slice's work grows (or shrinks) with
+  // its rank, every SIMD holds the same total
+  const int w = KVS == 1 ? (RW == 8 ? (wv < 4 ? wv : 11 - wv) : wv) : wv % RW;
   const int grp = KVS == 1 ? 0 : wv / RW;  // key group
   const int n = lane & 31;   // this lane's query column within the wave
   const int hh = lane >> 5;  // which half of the wave
