@@ -65,6 +65,9 @@ BANDS = [
     ("grid_diagonal_only", 4, 16, 4, 600, 600, 64, "bf16", "top_left", False, (0, 0)),
     ("grid_br_window3", 4, 16, 4, 600, 900, 128, "fp16", "bottom_right", True, (3, -1)),
     ("grid_two_sided", 4, 16, 2, 777, 777, 64, "fp16", "top_left", False, (100, 37)),
+    # the same grids with no band: ragged 256-row blocks, every row compared
+    ("grid_causal_ragged", 4, 16, 4, 777, 777, 128, "fp16", "top_left", True, (-1, -1)),
+    ("grid_full_ragged", 4, 16, 4, 777, 777, 64, "bf16", "top_left", False, (-1, -1)),
 ]
 
 
