@@ -94,8 +94,12 @@ def _fwd_cases(n=48, seed=7001):
 
 @pytest.mark.parametrize("cs", _fwd_cases(), ids=lambda c: f"fwd{c['i']}")
 def test_sweep_forward(cs):
+    _run_forward(cs, 9000)
+
+
+def _run_forward(cs, seed_base):
     _say(cs)
-    g = torch.Generator().manual_seed(9000 + cs["i"])
+    g = torch.Generator().manual_seed(seed_base + cs["i"])
     B, Hq, Hkv, Nq, Nkv, D, dt = cs["B"], cs["Hq"], cs["Hkv"], cs["Nq"], cs["Nkv"], cs["D"], cs["dtype"]
     q, k, v = _rand((B, Hq, Nq, D), dt, g), _rand((B, Hkv, Nkv, D), dt, g), _rand((B, Hkv, Nkv, D), dt, g)
     scale = (-1.0 if cs["neg"] else 1.0) * D ** -0.5
@@ -110,6 +114,31 @@ def test_sweep_forward(cs):
     Oref, Lref = oracle.attention_forward(_np(q), _np(k), _np(v), scale, cs["causal"],
                                           causal_offset=off if masked else 0, window=cs["window"] or (-1, -1))
     _compare_rows(o, l, Oref, Lref, _DT[dt], "dense")
+
+
+
+def _fwd_large_cases(n=24, seed=7005):
+    """Grids of more than 128 blocks of 256 rows (the one-key-group kernels,
+    the counted ring on masked ones) with ragged lengths."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([2, 4, 8]))
+        Hq = Hkv * int(rng.choice([2, 4]))
+        Nq, Nkv = int(rng.integers(257, 1100)), int(rng.integers(257, 1100))
+        B = 1
+        while B * Hq * ((Nq + 255) // 256) <= 128:
+            B += 1
+        causal, align, window = _mask_choice(rng, Nq, Nkv)
+        out.append(dict(i=i, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, D=int(rng.choice([64, 128])),
+                        dtype=str(rng.choice(["fp16", "bf16"])), causal=causal, align=align, window=window,
+                        neg=bool(rng.integers(0, 4) == 0), bnhd=bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("cs", _fwd_large_cases(), ids=lambda c: f"fwdL{c['i']}")
+def test_sweep_forward_large_grid(cs):
+    _run_forward(cs, 9500)
 
 
 # ---- forward, packed
