@@ -285,7 +285,11 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   const int wq_hi = q0 + 32 * w + 31 + off;
   const int wq_lo = q0 + 32 * w + off;
 
-  auto compute = [&](int stage, int t, bool masked) __attribute__((always_inline)) {
+  // the stage and whether the tile needs masks are compile-time, so the
+  // stage offsets fold into the LDS reads' immediate offsets and full tiles
+  // carry no mask arithmetic
+  auto compute = [&](auto stage_tag, int t, bool masked) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_tag)::value;
     const int kb = t * kBT;
     bool act1 = true;
     if (masked) {
@@ -322,16 +326,24 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // the mask test sits outside the element loop: inside it the compiler
+      // branched on it once per element
+      auto soft = [&](auto mask_tag) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float pv = fast_exp2(__builtin_fmaf(sx[e], c, -lse2));
-        if (masked) {
-          const int key = kb + 32 * u + 8 * (e >> 2) + 4 * hh + (e & 3);
-          pv = (key < Nkv && (!CAUSAL || key <= qrow + off) &&
-                (!BAND || (key >= qrow + off - WL && key <= qrow + off + WR))) ? pv : 0.f;
+        for (int e = 0; e < 16; ++e) {
+          float pv = fast_exp2(__builtin_fmaf(sx[e], c, -lse2));
+          if constexpr (decltype(mask_tag)::value) {
+            const int key = kb + 32 * u + 8 * (e >> 2) + 4 * hh + (e & 3);
+            pv = (key < Nkv && (!CAUSAL || key <= qrow + off) &&
+                  (!BAND || (key >= qrow + off - WL && key <= qrow + off + WR))) ? pv : 0.f;
+          }
+          sx[e] = pv * (px[e] - delta);
         }
-        sx[e] = pv * (px[e] - delta);
-      }
+      };
+      if (masked)
+        soft(std::true_type{});
+      else
+        soft(std::false_type{});
       pack_pt<BF16>(sx, pf + 2 * u);
     }
     const uint32_t so = 2 * stage * L::TILE;
@@ -360,17 +372,27 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   else
     __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
   barrier_nofence();
-  for (int t = t_begin; t < ntiles; ++t) {
-    const int stage = (t - t_begin) % 3;
+  // tile t sits in stage (t - t_begin) % 3: the loop steps through the three
+  // stages with the stage a compile-time constant
+  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_tag)::value;
     const bool pre = t + 2 < ntiles;
     if (pre) dma_tile(t + 2, (stage + 2) % 3);
-    compute(stage, t, t >= n_full || t < full_lo);
+    compute(stage_tag, t, t >= n_full || t < full_lo);
     if (pre)
       __builtin_amdgcn_s_waitcnt(kWaitCnt(NDMA));
     else
       __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
     barrier_nofence();
+  };
+  int t = t_begin;
+  for (; t + 2 < ntiles; t += 3) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+    step(t + 2, std::integral_constant<int, 2>{});
   }
+  if (t < ntiles) step(t, std::integral_constant<int, 0>{});
+  if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
 
   // ---- dQ = scale (dQ^T)^T, cast, stored as whole rows through the wave's
   //      slice of the ring (every wave is past the last barrier)
@@ -541,12 +563,15 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   const float c = a.c;
   const int kmin = k0 + 32 * kg;  // this wave's first key
 
-  auto compute = [&](int stage, int it, bool masked) __attribute__((always_inline)) {
+  // the stage and whether the tile needs masks are compile-time (as in the
+  // dQ pass)
+  auto compute = [&](auto stage_tag, int it, bool masked) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_tag)::value;
     const int tq = (ntq - 1 - it / a.group) * kBT + 32 * qh;  // this wave's first query
     // 32 queries that see none of this wave's keys
     if (masked && CAUSAL && kmin > tq + 31 + off) return;
     if (masked && BAND && (kmin > tq + 31 + off + WR || kmin + 31 < tq + off - WL)) return;
-    const uint32_t sq = stage * 2 * L::TILE * 2, sg = sq + 2 * L::TILE;
+    constexpr uint32_t sq = stage * 2 * L::TILE * 2, sg = sq + 2 * L::TILE;
     f32x16 sx = f32x16{}, px = f32x16{};
     // software pipeline: the four operand reads of k-step ks + PF go out before
     // k-step ks's two MFMAs (a loaded LDS read takes some 250 cycles); the
@@ -580,24 +605,32 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
       __builtin_amdgcn_sched_barrier(0);
     }
     // element e of lane (n, hh) is query tq + 8(e/4) + 4hh + e%4, key `key`
+    // the mask test sits outside the element loop (as in the dQ pass)
+    auto soft = [&](auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 a0 = ldp[2 * g], a1 = ldp[2 * g + 1];
-      const float l2[4] = {a0[0], a0[2], a1[0], a1[2]};
-      const float dl[4] = {a0[1], a0[3], a1[1], a1[3]};
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 a0 = ldp[2 * g], a1 = ldp[2 * g + 1];
+        const float l2[4] = {a0[0], a0[2], a1[0], a1[2]};
+        const float dl[4] = {a0[1], a0[3], a1[1], a1[3]};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 4 * g + j;
-        float pv = fast_exp2(__builtin_fmaf(sx[e], c, -l2[j]));
-        if (masked && CAUSAL) pv = (key <= tq + 8 * g + 4 * hh + j + off) ? pv : 0.f;
-        if (masked && BAND) {
-          const int p = tq + 8 * g + 4 * hh + j + off;
-          pv = (key >= p - WL && key <= p + WR) ? pv : 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * g + j;
+          float pv = fast_exp2(__builtin_fmaf(sx[e], c, -l2[j]));
+          if constexpr (MK && CAUSAL) pv = (key <= tq + 8 * g + 4 * hh + j + off) ? pv : 0.f;
+          if constexpr (MK && BAND) {
+            const int p = tq + 8 * g + 4 * hh + j + off;
+            pv = (key >= p - WL && key <= p + WR) ? pv : 0.f;
+          }
+          sx[e] = pv;
+          px[e] = pv * (px[e] - dl[j]);
         }
-        sx[e] = pv;
-        px[e] = pv * (px[e] - dl[j]);
       }
-    }
+    };
+    if (masked)
+      soft(std::true_type{});
+    else
+      soft(std::false_type{});
     u32x4 pp[2], dp[2];
     pack_pt<BF16>(sx, pp);
     pack_pt<BF16>(px, dp);
@@ -635,14 +668,20 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   if (total > 0) dma_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
   barrier_nofence();
-  for (int it = 0; it < total; ++it) {
-    const int stage = it & 1;
+  auto step = [&](int it, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_tag)::value;
     if (it + 1 < total) dma_tile(it + 1, stage ^ 1);
     const int t = ntq - 1 - it / a.group;
-    compute(stage, it, (MASK != 0) && (t < full_lo || t >= full_hi));
+    compute(stage_tag, it, (MASK != 0) && (t < full_lo || t >= full_hi));
     __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
     barrier_nofence();
+  };
+  int it = 0;
+  for (; it + 1 < total; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    step(it + 1, std::integral_constant<int, 1>{});
   }
+  if (it < total) step(it, std::integral_constant<int, 0>{});
 
   // ---- add the two query halves' partial sums (through LDS), then
   //      dV = (dV^T)^T, dK = scale (dK^T)^T, cast, store
