@@ -530,16 +530,10 @@ def main():
                           device=dev)
         run_bwd = lambda: A.attn_bwd(bq, bk, bv, bo, bdo, blse, causal=True, scale=bc.softmax_scale, dq=bdq,
                                      dk=bdk, dv=bdv, workspace=bws)
-        for _ in range(2):
-            run_bwd()
-        torch.cuda.synchronize()
-        torch.cuda._sleep(5_000_000)
-        e0.record(stream)
+        # 5 warm-up and 20 back-to-back calls (~80 ms), as in its kernel trace
         for _ in range(5):
             run_bwd()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bt = e0.elapsed_time(e1) / 5
+        bt = _back_to_back_ms(lambda i: run_bwd(), 20, stream, sleep_cycles=5_000_000)
         bflops = int(2.5 * bc.flops())  # 5 GEMMs against the forward's 2
         widened["backward"] = {
             "workload": bc.name + "_backward", "B": bc.B, "Hq": bc.Hq, "Hkv": bc.Hkv, "N": bc.Nq, "D": bc.D,
@@ -557,16 +551,9 @@ def main():
         vdq, vdk, vdv = torch.empty_like(vq), torch.empty_like(vk), torch.empty_like(vv)
         run_vbwd = lambda: A.attn_bwd_varlen(vq, vk, vv, vo, vdo, vl, vcq, vcq, vb.max_q, vb.max_q, causal=True,
                                              scale=vb.softmax_scale, dq=vdq, dk=vdk, dv=vdv)
-        for _ in range(2):
-            run_vbwd()
-        torch.cuda.synchronize()
-        torch.cuda._sleep(5_000_000)
-        e0.record(stream)
         for _ in range(5):
             run_vbwd()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        vbt = e0.elapsed_time(e1) / 5
+        vbt = _back_to_back_ms(lambda i: run_vbwd(), 20, stream, sleep_cycles=5_000_000)
         vbflops = int(2.5 * vb.flops())
         widened["backward_varlen"] = {
             "workload": vb.name + "_backward", "sequences": vb.B, "Hq": vb.Hq, "Hkv": vb.Hkv, "D": vb.D,
