@@ -237,6 +237,11 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
     lse2 = ld.x;
     delta = ld.y;
   }
+  // wait for these loads here, before the ring's buffer-to-LDS loads go out:
+  // the compiler does not see those loads, and a wait it placed at the first
+  // use of Q or dO inside the KV loop would also wait, on every tile, for the
+  // loads of the tile two ahead
+  __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
 
   const uint16_t* kbase = a.k + (VARLEN ? bk * a.skn : (int64_t)b * a.skb) + (int64_t)kvh * a.skh;
   const uint16_t* vbase = a.v + (VARLEN ? bk * a.svn : (int64_t)b * a.svb) + (int64_t)kvh * a.svh;
