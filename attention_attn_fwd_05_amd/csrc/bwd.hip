@@ -10,10 +10,11 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P (dP - delta),  delta = rowsum(dO * O)
 //   dQ = scale dS K,  dK = scale dS^T Q    (dK, dV summed over a kv head's group)
 //
-// gfx950 design, three kernels, no atomics:
-//   * bwd_prep: per query row, lse * log2(e) and delta, as (float, float) pairs.
+// gfx950 design, two kernels, no atomics:
 //   * bwd_dq: the forward's shape.  A workgroup of 8 waves owns 256 query rows
-//     of one q head; Q and dO are register-resident B operands, K and V tiles
+//     of one q head; it first forms lse * log2(e) and delta for its rows from
+//     O and dO and stores them, as (float, float) pairs, for bwd_dkdv.
+//     Q and dO are register-resident B operands, K and V tiles
 //     of 64 keys stream through a 3-stage LDS ring (buffer-to-LDS loads).
 //     S^T = K Q^T and dP^T = V dO^T come out one query per lane, so lse and
 //     delta are one value per lane; dQ^T += K^T dS^T reads K^T with the
@@ -50,35 +51,6 @@ constexpr int kBStages = 3;      // LDS ring depth
 constexpr int kDqReadAhead = 1;    // dQ pass: K/V reads ahead of its S, dP MFMAs
 constexpr int kKvReadAhead = 1;    // dK/dV pass: operand reads ahead of its S, dP MFMAs
 constexpr int kKvTrReadAhead = 1;  // dK/dV pass: transposing reads ahead of its dV, dK MFMAs
-
-// ---- lse * log2(e) and delta = rowsum(dO * O) per query row, fp32 pairs
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a) {
-  constexpr int C = D / 8;  // 16-byte chunks per row = lanes per row
-  const int64_t total = (int64_t)a.B * a.Hq * a.Nq;
-  const int64_t r = (int64_t)blockIdx.x * (256 / C) + threadIdx.x / C;
-  const int c = threadIdx.x % C;
-  float s = 0.f;
-  if (r < total) {
-    const int i = (int)(r % a.Nq);
-    const int64_t bh = r / a.Nq;
-    const int h = (int)(bh % a.Hq);
-    const int64_t b = bh / a.Hq;
-    const u32x4 o = load16(a.o + b * a.sob + h * a.soh + (int64_t)i * a.son + 8 * c);
-    const u32x4 g = load16(a.dout + b * a.sdob + h * a.sdoh + (int64_t)i * a.sdon + 8 * c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s += to_f32<BF16>(o[j] & 0xffff) * to_f32<BF16>(g[j] & 0xffff);
-      s += to_f32<BF16>(o[j] >> 16) * to_f32<BF16>(g[j] >> 16);
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < C; m <<= 1) s += __shfl_xor(s, m);
-  if (r < total && c == 0) {
-    float2* out = reinterpret_cast<float2*>(a.ld) + r;
-    *out = make_float2(a.lse[r] * kLog2e, s);
-  }
-}
 
 // LDS ring of the dq kernel: V tiles of all stages, then K tiles
 template <int D>
@@ -214,34 +186,65 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   const int64_t bq = VARLEN ? t0 : 0, bk = VARLEN ? s0 : 0;  // packed: first row of the sequence
   const uint16_t* qbase = a.q + (VARLEN ? bq * a.sqn : (int64_t)b * a.sqb) + (int64_t)h * a.sqh;
   const uint16_t* gbase = a.dout + (VARLEN ? bq * a.sdon : (int64_t)b * a.sdob) + (int64_t)h * a.sdoh;
-  const float2* ldrow = reinterpret_cast<const float2*>(a.ld) +
-                        (VARLEN ? (int64_t)h * a.total_q + bq : ((int64_t)b * a.Hq + h) * a.Nq);
+  const uint16_t* obase = a.o + (VARLEN ? bq * a.son : (int64_t)b * a.sob) + (int64_t)h * a.soh;
+  // (lse, delta) rows of this (sequence, q head): (b, h) of (B, Hq, Nq), packed (h, bq) of (Hq, total_q)
+  const int64_t row0 = VARLEN ? (int64_t)h * a.total_q + bq : ((int64_t)b * a.Hq + h) * a.Nq;
 
-  // stationary B operands: Q and dO rows (zeros past Nq); lse2 and delta
-  u32x4 qf[KS], gf[KS];
+  // stationary B operands: Q and dO rows (zeros past Nq); the O rows for delta
+  u32x4 qf[KS], gf[KS], of[KS];
   {
-    const int64_t qo = (int64_t)q0 * a.sqn, go = (int64_t)q0 * a.sdon;
+    const int64_t qo = (int64_t)q0 * a.sqn, go = (int64_t)q0 * a.sdon, oo = (int64_t)q0 * a.son;
+    const int64_t o_bytes = ((int64_t)(Nq - 1) * a.son + D) * 2;
     const auto rq = make_rsrc(qbase + qo, clamp_bytes(q_bytes - 2 * qo));
     const auto rg = make_rsrc(gbase + go, clamp_bytes(do_bytes - 2 * go));
+    const auto ro = make_rsrc(obase + oo, clamp_bytes(o_bytes - 2 * oo));
     const int32_t oq = (32 * w + n) * (int32_t)a.sqn * 2 + 16 * hh;
     const int32_t og = (32 * w + n) * (int32_t)a.sdon * 2 + 16 * hh;
+    const int32_t ob = (32 * w + n) * (int32_t)a.son * 2 + 16 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = bload16(rq, oq + 32 * ks);
       gf[ks] = bload16(rg, og + 32 * ks);
+      of[ks] = bload16(ro, ob + 32 * ks);
     }
   }
-  float lse2 = 0.f, delta = 0.f;
-  if (qrow < Nq) {
-    const float2 ld = ldrow[qrow];
-    lse2 = ld.x;
-    delta = ld.y;
-  }
+  float lse2 = 0.f;
+  if (qrow < Nq) lse2 = a.lse[row0 + qrow] * kLog2e;
   // wait for these loads here, before the ring's buffer-to-LDS loads go out:
   // the compiler does not see those loads, and a wait it placed at the first
   // use of Q or dO inside the KV loop would also wait, on every tile, for the
   // loads of the tile two ahead
   __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
+
+  // delta = rowsum(dO * O) in fp32: one partial sum per 16-byte chunk (this
+  // lane holds chunks 2 ks + hh of row n), chunk pairs added across the two
+  // lane halves, then a pairwise tree over the pairs
+  float delta;
+  {
+    float ps[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s += to_f32<BF16>(of[ks][j] & 0xffff) * to_f32<BF16>(gf[ks][j] & 0xffff);
+        s += to_f32<BF16>(of[ks][j] >> 16) * to_f32<BF16>(gf[ks][j] >> 16);
+      }
+      ps[ks] = s + __shfl_xor(s, 32);
+    }
+#pragma unroll
+    for (int m = 1; m < KS; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < KS; i += 2 * m) ps[i] += ps[i + m];
+    delta = ps[0];
+  }
+  // every query row of the sequence belongs to one dq workgroup, which hands
+  // its (lse2, delta) pair to the dK/dV pass (launched after this one)
+  if (qrow < Nq) {
+    if (hh == 0) reinterpret_cast<float2*>(a.ld)[row0 + qrow] = make_float2(lse2, delta);
+  } else {
+    delta = 0.f;
+  }
 
   const uint16_t* kbase = a.k + (VARLEN ? bk * a.skn : (int64_t)b * a.skb) + (int64_t)kvh * a.skh;
   const uint16_t* vbase = a.v + (VARLEN ? bk * a.svn : (int64_t)b * a.svb) + (int64_t)kvh * a.svh;
@@ -726,16 +729,6 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
 
 template <int D, bool BF16, int MASK, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  // the row pass sees a packed batch as one sequence of total_q rows
-  BwdArgs p = a;
-  if (VARLEN) {
-    p.B = 1;
-    p.Nq = a.total_q;
-    p.sob = p.sdob = 0;
-  }
-  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-  const int64_t prep_blocks = (rows + 256 / (D / 8) - 1) / (256 / (D / 8));
-  hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, MASK, VARLEN>), dim3(a.dq_blocks), dim3(64 * kDqW), 0, stream, a);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, MASK, VARLEN>), dim3(a.dkv_blocks), dim3(64 * kKvW), 0, stream, a);
   return hipGetLastError();

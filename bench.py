@@ -284,7 +284,7 @@ def main():
             res.append({"workload": vp.name, "us_per_launch": round(ms * 1e3, 2),
                         "tflops": round(vp.flops() / (ms * 1e-3) / 1e12, 1)})
         else:
-            # backward of the headline prefill (as widened.backward): prep, dQ and dK/dV kernels
+            # backward of the headline prefill (as widened.backward): the dQ and dK/dV kernels
             bc = W.serving(8192, True)
             q, k, v = (t.to(dev) for t in W.prefill_inputs(bc))
             do = torch.randn(q.shape, generator=torch.Generator().manual_seed(W.BASE_SEED + 60)).to(q.dtype).to(dev)

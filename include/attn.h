@@ -213,9 +213,10 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *   lse: contiguous fp32 (B, Hq, Nq), as attn_fwd returns it for the same
  *   inputs, causal argument and scale.  causal: as attn_fwd (attn_bwd_masked
  *   takes a band mask).  workspace: attn_bwd_workspace_bytes(B, Hq, Nq)
- *   bytes, 16-byte aligned, contents irrelevant.  Three kernels run in order on
- *   `stream` (row statistics, dQ, dK/dV); no atomics, so the result does not
- *   depend on scheduling.
+ *   bytes, 16-byte aligned, contents irrelevant.  Two kernels run in order on
+ *   `stream`: dQ (which also leaves each query row's statistics in the
+ *   workspace), then dK/dV; no atomics, so the result does not depend on
+ *   scheduling.
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                      void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nkv, int D,
