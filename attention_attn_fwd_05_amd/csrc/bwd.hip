@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   int Nq = a.Nq, Nkv = a.Nkv;
   int off = MASK != 0 ? a.causal_off : 0;
   int64_t t0 = 0, s0 = 0;
-  int64_t q_bytes = a.q_bytes, do_bytes = a.do_bytes, k_bytes = a.k_bytes, v_bytes = a.v_bytes;
+  int64_t q_bytes = a.q_bytes, do_bytes = a.do_bytes;
   if constexpr (VARLEN) {
     t0 = min(max(a.cu_q[b], 0), a.total_q);
     const int t1 = min(max(a.cu_q[b + 1], (int)t0), a.total_q);
@@ -180,8 +180,6 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
     if (q0 >= Nq) return;  // whole workgroup
     q_bytes = ((int64_t)(Nq - 1) * a.sqn + D) * 2;
     do_bytes = ((int64_t)(Nq - 1) * a.sdon + D) * 2;
-    k_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.skn + D) * 2 : 0;
-    v_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.svn + D) * 2 : 0;
   }
   const int64_t bq = VARLEN ? t0 : 0, bk = VARLEN ? s0 : 0;  // packed: first row of the sequence
   const uint16_t* qbase = a.q + (VARLEN ? bq * a.sqn : (int64_t)b * a.sqb) + (int64_t)h * a.sqh;
@@ -273,8 +271,10 @@ __global__ __launch_bounds__(64 * kDqW, 2) void bwd_dq_kernel(const BwdArgs a) {
   const uint32_t lds_v = lds_addr(smem + L::V0) + 1024 * NB * w;
   auto dma_tile = [&](int t, int stage) __attribute__((always_inline)) {
     const int64_t ko = (int64_t)t * kBT * a.skn, vo = (int64_t)t * kBT * a.svn;
-    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(k_bytes - 2 * ko));
-    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(v_bytes - 2 * vo));
+    // each load's range ends with the tile's last key row (none past Nkv)
+    const int rows = min(Nkv - t * kBT, kBT);
+    const i32x4 rk = rsrc_words(kbase + ko, rows > 0 ? ((rows - 1) * (int32_t)a.skn + D) * 2 : 0);
+    const i32x4 rv = rsrc_words(vbase + vo, rows > 0 ? ((rows - 1) * (int32_t)a.svn + D) * 2 : 0);
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma16(rk, lds_k + 2 * stage * L::TILE + 1024 * i, dk[i]);
 #pragma unroll
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   int Nq = a.Nq, Nkv = a.Nkv;
   int off = MASK != 0 ? a.causal_off : 0;
   int64_t bq = 0, bk = 0;
-  int64_t q_bytes = a.q_bytes, do_bytes = a.do_bytes, k_bytes = a.k_bytes, v_bytes = a.v_bytes;
+  int64_t k_bytes = a.k_bytes, v_bytes = a.v_bytes;
   if constexpr (VARLEN) {
     bq = min(max(a.cu_q[b], 0), a.total_q);
     const int t1 = min(max(a.cu_q[b + 1], (int)bq), a.total_q);
@@ -470,8 +470,6 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
     if (MASK != 0) off = a.causal_br ? Nkv - Nq : 0;
     Nq = min(Nq, a.Nq);
     if (k0 >= Nkv) return;  // whole workgroup: block past this sequence's keys
-    q_bytes = Nq > 0 ? ((int64_t)(Nq - 1) * a.sqn + D) * 2 : 0;
-    do_bytes = Nq > 0 ? ((int64_t)(Nq - 1) * a.sdon + D) * 2 : 0;
     k_bytes = ((int64_t)(Nkv - 1) * a.skn + D) * 2;
     v_bytes = ((int64_t)(Nkv - 1) * a.svn + D) * 2;
   }
@@ -534,17 +532,20 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   // last tile first and the group's q heads innermost, so the key blocks of
   // one (batch, kv head) running together read the same Q and dO tiles at
   // the same time (every block's range ends at the last tile)
-  auto dma_tile = [&](int it, int stage) __attribute__((always_inline)) {
-    const int tix = it / a.group;
-    const int hgi = it - tix * a.group;
-    const int t = ntq - 1 - tix;
-    const int h = kvh * a.group + hgi;
-    const int64_t qo = (int64_t)t * kBT * a.sqn, go = (int64_t)t * kBT * a.sdon;
-    const i32x4 rq = rsrc_words(a.q + (VARLEN ? bq * a.sqn : (int64_t)b * a.sqb) + (int64_t)h * a.sqh + qo,
-                                clamp_bytes(q_bytes - 2 * qo));
-    const i32x4 rg = rsrc_words(a.dout + (VARLEN ? bq * a.sdon : (int64_t)b * a.sdob) + (int64_t)h * a.sdoh + go,
-                                clamp_bytes(do_bytes - 2 * go));
-    const i32x4 rl = rsrc_words(ld_row0(h) + (int64_t)t * kBT * 2, clamp_bytes(((int64_t)Nq - (int64_t)t * kBT) * 8));
+  // byte addresses of the first Q, dO and (lse2, delta) row of query tile t
+  // of q head kvh * group + hg, and the steps from one tile of the walk to the
+  // next: the next q head, or from the group's last q head back to its first
+  // one tile lower.  Each load's range ends with the tile's last row.
+  const int64_t lstride = 8 * (VARLEN ? (int64_t)a.total_q : (int64_t)a.Nq);  // between q heads
+  const int64_t gm1 = a.group - 1;
+  const int64_t sq_h = 2 * a.sqh, sq_w = -gm1 * 2 * a.sqh - 2 * kBT * a.sqn;
+  const int64_t sg_h = 2 * a.sdoh, sg_w = -gm1 * 2 * a.sdoh - 2 * kBT * a.sdon;
+  const int64_t sl_h = lstride, sl_w = -gm1 * lstride - 8 * kBT;
+  auto dma_tile = [&](int t, uint64_t aq, uint64_t ag, uint64_t al, int stage) __attribute__((always_inline)) {
+    const int rows = min(Nq - t * kBT, kBT);  // >= 1: t < ntq
+    const i32x4 rq = rsrc_words((const void*)aq, ((rows - 1) * (int32_t)a.sqn + D) * 2);
+    const i32x4 rg = rsrc_words((const void*)ag, ((rows - 1) * (int32_t)a.sdon + D) * 2);
+    const i32x4 rl = rsrc_words((const void*)al, rows * 8);
     const uint32_t sq = lds_q + stage * 2 * L::TILE * 2;
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma16(rq, sq + 1024 * i, dq_[i]);
@@ -573,9 +574,9 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
 
   // the stage and whether the tile needs masks are compile-time (as in the
   // dQ pass)
-  auto compute = [&](auto stage_tag, int it, bool masked) __attribute__((always_inline)) {
+  auto compute = [&](auto stage_tag, int t, bool masked) __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_tag)::value;
-    const int tq = (ntq - 1 - it / a.group) * kBT + 32 * qh;  // this wave's first query
+    const int tq = t * kBT + 32 * qh;  // this wave's first query
     // 32 queries that see none of this wave's keys
     if (masked && CAUSAL && kmin > tq + 31 + off) return;
     if (masked && BAND && (kmin > tq + 31 + off + WR || kmin + 31 < tq + off - WL)) return;
@@ -673,16 +674,34 @@ __global__ __launch_bounds__(64 * kKvW, 2) void bwd_dkdv_kernel(const BwdArgs a)
   };
 
   // 2-stage ring: the loads of tile it + 1 go out before tile it is computed
-  if (total > 0) dma_tile(0, 0);
+  // (t, hg) and the addresses of step it, counted along the walk
+  int t = ntq - 1, hg = 0;
+  const int64_t h0 = (int64_t)kvh * a.group, r0 = (int64_t)(ntq - 1) * kBT;
+  uint64_t aq = (uint64_t)a.q + 2 * ((VARLEN ? bq * a.sqn : (int64_t)b * a.sqb) + h0 * a.sqh + r0 * a.sqn);
+  uint64_t ag = (uint64_t)a.dout + 2 * ((VARLEN ? bq * a.sdon : (int64_t)b * a.sdob) + h0 * a.sdoh + r0 * a.sdon);
+  uint64_t al = (uint64_t)ld_row0((int)h0) + 8 * r0;
+  if (total > 0) dma_tile(t, aq, ag, al, 0);
   __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
   barrier_nofence();
   auto step = [&](int it, auto stage_tag) __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_tag)::value;
-    if (it + 1 < total) dma_tile(it + 1, stage ^ 1);
-    const int t = ntq - 1 - it / a.group;
-    compute(stage_tag, it, (MASK != 0) && (t < full_lo || t >= full_hi));
+    int tn = t, hn = hg + 1;
+    const bool wrap = hn == a.group;
+    if (wrap) {
+      hn = 0;
+      --tn;
+    }
+    const uint64_t aqn = aq + (uint64_t)(wrap ? sq_w : sq_h), agn = ag + (uint64_t)(wrap ? sg_w : sg_h),
+                   aln = al + (uint64_t)(wrap ? sl_w : sl_h);
+    if (it + 1 < total) dma_tile(tn, aqn, agn, aln, stage ^ 1);
+    compute(stage_tag, t, (MASK != 0) && (t < full_lo || t >= full_hi));
     __builtin_amdgcn_s_waitcnt(kWaitCnt(0));
     barrier_nofence();
+    t = tn;
+    hg = hn;
+    aq = aqn;
+    ag = agn;
+    al = aln;
   };
   int it = 0;
   for (; it + 1 < total; it += 2) {

@@ -176,7 +176,7 @@ void prefill_fwd_kernel(const FwdArgs a) {
   const uint16_t *qbase, *kbase, *vbase;
   uint16_t* obase;
   float* lbase;
-  int64_t q_bytes = a.q_bytes, k_bytes = a.k_bytes, v_bytes = a.v_bytes;
+  int64_t q_bytes = a.q_bytes;
   if constexpr (VARLEN) {
     const int t0 = min(max(a.cu_q[b], 0), a.total_q);
     const int t1 = min(max(a.cu_q[b + 1], t0), a.total_q);
@@ -193,8 +193,6 @@ void prefill_fwd_kernel(const FwdArgs a) {
     obase = a.o + (int64_t)t0 * a.son + (int64_t)h * a.soh;
     lbase = a.lse ? a.lse + (int64_t)h * a.total_q + t0 : nullptr;
     q_bytes = ((int64_t)(Nq - 1) * a.sqn + D) * 2;
-    k_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.skn + D) * 2 : 0;
-    v_bytes = Nkv > 0 ? ((int64_t)(Nkv - 1) * a.svn + D) * 2 : 0;
   } else {
     qbase = a.q + (int64_t)b * a.sqb + (int64_t)h * a.sqh;
     kbase = a.k + (int64_t)b * a.skb + (int64_t)kvh * a.skh;
@@ -249,8 +247,10 @@ void prefill_fwd_kernel(const FwdArgs a) {
   const uint32_t lds_v = lds_addr(ring + L::V0) + 1024 * NB * w;
   auto dma_tile = [&](int t, int stage) {
     const int64_t ko = (int64_t)t * kBN * a.skn, vo = (int64_t)t * kBN * a.svn;
-    const i32x4 rk = rsrc_words(kbase + ko, clamp_bytes(k_bytes - 2 * ko));
-    const i32x4 rv = rsrc_words(vbase + vo, clamp_bytes(v_bytes - 2 * vo));
+    // each load's range ends with the tile's last key row (none past Nkv)
+    const int rows = min(Nkv - t * kBN, kBN);
+    const i32x4 rk = rsrc_words(kbase + ko, rows > 0 ? ((rows - 1) * (int32_t)a.skn + D) * 2 : 0);
+    const i32x4 rv = rsrc_words(vbase + vo, rows > 0 ? ((rows - 1) * (int32_t)a.svn + D) * 2 : 0);
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma16(rk, lds_k + 2 * stage * L::TILE + 1024 * i, dk[i]);
 #pragma unroll
