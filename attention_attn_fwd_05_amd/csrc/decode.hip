@@ -47,10 +47,6 @@ constexpr int kDecodeWgsPerCu = 2;  // workgroups per CU the register budget is 
 constexpr int kMaxSplits = 64;  // partials merged by one combine (the host keeps nsplit <= this)
 constexpr int kPartPad = 4;     // per-head partial: m, l, 2 pad, o[D] -> 16-byte aligned o
 
-__device__ __forceinline__ int32_t clamp_bytes(int64_t x) {
-  return (int32_t)(x < 0 ? 0 : (x > 0x7fffffff ? 0x7fffffff : x));
-}
-
 // MODE 0: one length for every sequence; 1: per-sequence lengths; 2: per-sequence
 // lengths over a paged cache.  WINDOW: a sliding window hides the slots before
 // len - 1 - window_left (without it none of that code is compiled in)
@@ -191,9 +187,11 @@ __global__ __launch_bounds__(256, kDecodeWgsPerCu) void decode_kernel(const Deco
       return;
     }
     const int64_t ko = (int64_t)kb * a.skn, vo = (int64_t)kb * a.svn;
-    const int64_t rows = k1 - kb;  // keys of this split from kb on
-    const auto rk = make_rsrc(kbase + ko, clamp_bytes(((rows - 1) * a.skn + D) * 2));
-    const auto rv = make_rsrc(vbase + vo, clamp_bytes(((rows - 1) * a.svn + D) * 2));
+    // keys of this split in the tile: each load's range ends with the last
+    // one (the tile's loads read its rows 0 .. kDT - 1 only)
+    const int rows = min(k1 - kb, kDT);
+    const auto rk = make_rsrc(kbase + ko, rows > 0 ? ((rows - 1) * (int32_t)a.skn + D) * 2 : 0);
+    const auto rv = make_rsrc(vbase + vo, rows > 0 ? ((rows - 1) * (int32_t)a.svn + D) * 2 : 0);
     if (WINDOW && kb < kvis) {
       // the window's lead-in tile: rows before kvis re-read row kvis (their
       // scores are masked, their P is 0), so hidden slots are never read
